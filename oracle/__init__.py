@@ -1,0 +1,312 @@
+"""Python face of the plain CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only users.  The product path
+(``sparse_mixture_experts_50_amd``) never imports this package, and this
+package never imports the product.  The arithmetic lives in the C file;
+this module only marshals numpy arrays (float64 results) and chains the
+steps in the order the pages give:
+router -> softmax -> top-k + renormalise -> count / capacity / dispatch
+-> expert FFNs -> weighted combine, with the load-balance statistics and
+the balancing-bias update beside them.
+
+Inputs may be torch CPU tensors or numpy arrays; bfloat16 tensors are passed
+as their raw 16-bit patterns and widened exactly inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+__all__ = ["capacity", "router", "topk", "renorm_selection", "dispatch",
+           "stats", "layer_rows", "bias_update", "forward", "lib"]
+
+_LIB = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load (building once if absent) the oracle shared library."""
+    global _LIB
+    if _LIB is None:
+        path = _build.library_path()
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_capacity.restype = ctypes.c_int
+        L.oracle_capacity.argtypes = [ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double]
+        L.oracle_router.restype = None
+        L.oracle_router.argtypes = [ctypes.c_int] * 4 + [_vp, _vp, _f32p,
+                                                         _f32p, _f64p, _f64p]
+        L.oracle_topk.restype = None
+        L.oracle_topk.argtypes = [ctypes.c_int] * 3 + [_f64p, _i32p, _f64p,
+                                                       _f64p]
+        L.oracle_renorm_selection.restype = None
+        L.oracle_renorm_selection.argtypes = [ctypes.c_int] * 3 + [
+            _f64p, _i32p, _f64p]
+        L.oracle_dispatch.restype = ctypes.c_int
+        L.oracle_dispatch.argtypes = [ctypes.c_int] * 4 + [_i32p] * 6
+        L.oracle_stats.restype = None
+        L.oracle_stats.argtypes = [ctypes.c_int] * 3 + [
+            _f64p, _i32p, ctypes.c_double, _f64p, _f64p, _f64p]
+        L.oracle_layer_rows.restype = ctypes.c_int
+        L.oracle_layer_rows.argtypes = [ctypes.c_int, _i32p] + \
+            [ctypes.c_int] * 4 + [_vp, _i32p, _f64p, _i32p] + \
+            [ctypes.POINTER(_vp)] * 4 + [_vp] * 4 + [_f64p]
+        L.oracle_bias_update.restype = None
+        L.oracle_bias_update.argtypes = [ctypes.c_int, _i32p, ctypes.c_float,
+                                         ctypes.c_float, _f32p]
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------- marshal
+def _raw(a):
+    """(contiguous numpy array, dtype code) of a float32 / bfloat16 input.
+    dtype code 0 = float32 words, 1 = bfloat16 bit patterns."""
+    if a is None:
+        return None, None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().contiguous()
+            if a.device.type != "cpu":
+                a = a.cpu()
+            if a.dtype == torch.bfloat16:
+                return np.ascontiguousarray(a.view(torch.int16).numpy()
+                                            .view(np.uint16)), 1
+            if a.dtype == torch.float32:
+                return np.ascontiguousarray(a.numpy()), 0
+            raise TypeError(f"unsupported tensor dtype {a.dtype}")
+    except ImportError:
+        pass
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return np.ascontiguousarray(a), 1
+    if a.dtype == np.float32:
+        return np.ascontiguousarray(a), 0
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def _f32(a):
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().to(torch.float32).numpy()
+    except ImportError:
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _p(a, typ):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+# ------------------------------------------------------------------ steps
+def capacity(T: int, E: int, capacity_factor: Optional[float]) -> int:
+    """floor(T / E * cf), or -1 for no limit."""
+    if capacity_factor is None:
+        return -1
+    return int(lib().oracle_capacity(T, E, float(capacity_factor)))
+
+
+def router(x, wr, add_bias=None, sub_bias=None):
+    """(logits, probs), both float64 [T, E]."""
+    xa, dt = _raw(x)
+    wa, dt2 = _raw(wr)
+    assert dt == dt2, "x and Wr must share a dtype"
+    T, d = xa.shape
+    E = wa.shape[0]
+    add = _f32(add_bias)
+    sub = _f32(sub_bias)
+    logits = np.empty((T, E), np.float64)
+    probs = np.empty((T, E), np.float64)
+    lib().oracle_router(T, d, E, dt, xa.ctypes.data, wa.ctypes.data,
+                        _p(add, _f32p), _p(sub, _f32p), _p(logits, _f64p),
+                        _p(probs, _f64p))
+    return logits, probs
+
+
+def topk(probs: np.ndarray, k: int):
+    """(idx int32 [T,k], w float64 [T,k], margin float64 [T])."""
+    probs = np.ascontiguousarray(probs, dtype=np.float64)
+    T, E = probs.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    margin = np.empty((T,), np.float64)
+    lib().oracle_topk(T, E, k, _p(probs, _f64p), _p(idx, _i32p),
+                      _p(w, _f64p), _p(margin, _f64p))
+    return idx, w, margin
+
+
+def renorm_selection(probs: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    probs = np.ascontiguousarray(probs, dtype=np.float64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, E = probs.shape
+    k = idx.shape[1]
+    w = np.empty((T, k), np.float64)
+    lib().oracle_renorm_selection(T, E, k, _p(probs, _f64p), _p(idx, _i32p),
+                                  _p(w, _f64p))
+    return w
+
+
+def dispatch(idx: np.ndarray, E: int, cap: int) -> dict:
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    out = dict(counts=np.empty(E, np.int32), kept=np.empty(E, np.int32),
+               offsets=np.empty(E + 1, np.int32),
+               slot_token=np.empty(T * k, np.int32),
+               slot_of=np.empty((T, k), np.int32))
+    rc = lib().oracle_dispatch(
+        T, E, k, cap, _p(idx, _i32p), _p(out["counts"], _i32p),
+        _p(out["kept"], _i32p), _p(out["offsets"], _i32p),
+        _p(out["slot_token"], _i32p), _p(out["slot_of"], _i32p))
+    if rc != 0:
+        raise ValueError("expert index out of range")
+    return out
+
+
+def stats(probs: np.ndarray, counts: np.ndarray, k: int, alpha: float):
+    """(f [E], p [E], L_aux) in float64."""
+    probs = np.ascontiguousarray(probs, dtype=np.float64)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    T, E = probs.shape
+    f = np.empty(E, np.float64)
+    p = np.empty(E, np.float64)
+    l = np.empty(1, np.float64)
+    lib().oracle_stats(T, E, k, _p(probs, _f64p), _p(counts, _i32p),
+                       float(alpha), _p(f, _f64p), _p(p, _f64p),
+                       _p(l, _f64p))
+    return f, p, float(l[0])
+
+
+class Experts:
+    """Per-expert weights for :func:`layer_rows`.
+
+    ``get(e)`` returns ``(W1[d_ff,d], b1|None, W2[d,d_ff], b2|None)`` as
+    torch CPU tensors or numpy arrays; it is only called for experts that a
+    listed token actually uses, so large layers can be fetched lazily."""
+
+    def __init__(self, E: int, get):
+        self.E = E
+        self.get = get
+
+    @staticmethod
+    def stacked(w1, b1, w2, b2):
+        E = w1.shape[0]
+        return Experts(E, lambda e: (w1[e], None if b1 is None else b1[e],
+                                     w2[e], None if b2 is None else b2[e]))
+
+
+def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
+               shared=None) -> np.ndarray:
+    """Layer output rows y[tokens] (float64 [n, d]) for the given routing.
+    ``slot_of`` None means every assignment is kept.  ``shared`` is
+    ``(Ws1, bs1, Ws2, bs2)`` or None."""
+    tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    xa, dt = _raw(x)
+    T, d = xa.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    k = idx.shape[1]
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    so = None if slot_of is None else np.ascontiguousarray(slot_of,
+                                                          dtype=np.int32)
+    E = experts.E
+    need = set()
+    for t in tokens.tolist():
+        for j in range(k):
+            if so is None or so[t, j] >= 0:
+                need.add(int(idx[t, j]))
+    keep = []           # keeps converted arrays alive during the call
+    tabs = [(_vp * E)() for _ in range(4)]
+    d_ff = None
+    for e in sorted(need):
+        parts = experts.get(e)
+        for i, a in enumerate(parts):
+            ra, rdt = _raw(a)
+            if ra is None:
+                continue
+            assert rdt == dt, "weights and x must share a dtype"
+            keep.append(ra)
+            tabs[i][e] = ra.ctypes.data
+        d_ff = parts[0].shape[0]
+    sh = [None] * 4
+    if shared is not None:
+        for i, a in enumerate(shared):
+            ra, rdt = _raw(a)
+            if ra is not None:
+                assert rdt == dt
+                keep.append(ra)
+                sh[i] = ra.ctypes.data
+        d_ff = shared[0].shape[0]
+    if d_ff is None:
+        d_ff = 1
+    y = np.zeros((len(tokens), d), np.float64)
+    has_b1 = any(tabs[1][e] for e in range(E))
+    has_b2 = any(tabs[3][e] for e in range(E))
+    rc = lib().oracle_layer_rows(
+        len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, xa.ctypes.data,
+        _p(idx, _i32p), _p(w, _f64p), _p(so, _i32p), tabs[0],
+        tabs[1] if has_b1 else None, tabs[2], tabs[3] if has_b2 else None,
+        sh[0], sh[1], sh[2], sh[3], _p(y, _f64p))
+    if rc != 0:
+        raise RuntimeError(f"oracle_layer_rows failed ({rc})")
+    return y
+
+
+def bias_update(counts, target: float, gamma: float, bias) -> np.ndarray:
+    """One float32 balancing step; returns the new bias (input untouched)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    b = np.array(_f32(bias), dtype=np.float32, copy=True)
+    lib().oracle_bias_update(len(counts), _p(counts, _i32p),
+                             ctypes.c_float(target), ctypes.c_float(gamma),
+                             _p(b, _f32p))
+    return b
+
+
+def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
+            alpha: float = 0.01, tokens: Optional[Sequence[int]] = None,
+            selection: Optional[np.ndarray] = None) -> dict:
+    """The whole layer, step by step, as the pages define it.
+
+    ``inp`` holds x, wr, br, ebias, w1, b1, w2, b2, ws1, bs1, ws2, bs2 (the
+    dict the workload generator returns).  ``tokens`` restricts the costly
+    expert evaluation to some rows (routing, counts and statistics always
+    cover every token).  ``selection`` replaces the oracle's own top-k
+    choice (a checker adopting equally valid picks at near-ties); the
+    weights are then renormalised from the oracle's probabilities."""
+    x = inp["x"]
+    T = x.shape[0]
+    E = inp["wr"].shape[0]
+    _, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
+    idx, w, margin = topk(probs, k)
+    if selection is not None:
+        idx = np.ascontiguousarray(selection, dtype=np.int32)
+        w = renorm_selection(probs, idx)
+    cap = capacity(T, E, capacity_factor)
+    disp = dispatch(idx, E, cap)
+    f, p, l_aux = stats(probs, disp["counts"], k, alpha)
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    experts = Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
+                              inp.get("b2"))
+    shared = None
+    if inp.get("ws1") is not None:
+        shared = (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+    y = layer_rows(tokens, x, idx, w, disp["slot_of"], experts, shared)
+    out = dict(probs=probs, topk_idx=idx, topk_w=w, margin=margin,
+               capacity=cap, f=f, p=p, l_aux=l_aux, y=y,
+               tokens=np.asarray(tokens, dtype=np.int32))
+    out.update(disp)
+    return out

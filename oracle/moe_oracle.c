@@ -1,0 +1,322 @@
+/*
+ * Plain CPU oracle of the sparse Mixture-of-Experts FFN layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg use it.  It shares no code with the HIP
+ * library and is written to be read against the pages, not to be fast.
+ *
+ * Sources (page title, then section):
+ *   [SKILL]  "AI-Research-SKILLs MoE training guide" (discosf.com):
+ *            sec. 3.1 basic MoE layer, sec. 4.1 data-flow figure,
+ *            sec. 4.2 routing mechanisms, sec. 4.3 auxiliary loss and
+ *            router z-loss, sec. 6.1 Mixtral block, sec. 7.1 DeepSeekMoE,
+ *            sec. 8.2 capacity factor, sec. 10.1 monitoring metrics.
+ *   [DIVE]   "MoE architecture deep dive: from routing to production
+ *            inference" (juejin.cn): sec. 1.1 dense FFN to sparse MoE,
+ *            sec. 1.2 gating network, sec. 1.3 top-K routing,
+ *            sec. 2.2 auxiliary load-balancing loss, sec. 2.3 expert
+ *            capacity, sec. 2.4 auxiliary-loss-free balancing,
+ *            sec. 3 DeepSeek-V3 shared expert.
+ *   [GROUP]  "The expert group activated per token" (wmrh.cn):
+ *            sec. 3.1 anatomy of an MoE layer (FFN formula, router).
+ *
+ * Precision: every floating-point step is IEEE double, except the
+ * balancing-bias update, which the layer defines on float32 state.
+ * Inputs arrive as float32 words (dtype 0) or bfloat16 bit patterns
+ * (dtype 1) and are widened exactly to double.
+ *
+ * Tie rule (the pages give none): among equal probabilities the lower
+ * expert index ranks first.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_ERR_ARG -1
+#define OR_ERR_MISSING_EXPERT -2
+
+/* Exact widening of one stored element to double. */
+static double ld(const void *p, size_t i, int dtype)
+{
+    if (dtype == 0)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Expert capacity: floor((tokens / experts) * capacity_factor).
+ * [DIVE] sec. 2.3; [SKILL] sec. 8.2 (integer truncation of the same
+ * quotient).  A negative factor means "no limit" and returns -1. */
+int oracle_capacity(int T, int E, double cf)
+{
+    if (cf < 0.0 || E <= 0)
+        return -1;
+    return (int)floor(((double)T / (double)E) * cf);
+}
+
+/* Router logits and softmax probabilities for every token.
+ *   logit[t,e] = sum_c x[t,c] * Wr[e,c] + add[e] - sub[e]
+ *   prob[t,:]  = softmax(logit[t,:])
+ * [DIVE] sec. 1.2 (gate_weights = Softmax(x . W_g)); [SKILL] sec. 3.1
+ * (router nn.Linear, which carries an additive bias); [DIVE] sec. 2.4
+ * (adjusted_logits_i = logits_i - b_i).  add and sub may be NULL. */
+void oracle_router(int T, int d, int E, int dtype, const void *x,
+                   const void *wr, const float *add, const float *sub,
+                   double *logits, double *probs)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        double *lg = logits + (size_t)t * E;
+        double *pr = probs + (size_t)t * E;
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc += ld(x, (size_t)t * d + c, dtype) *
+                       ld(wr, (size_t)e * d + c, dtype);
+            if (add)
+                acc += (double)add[e];
+            if (sub)
+                acc -= (double)sub[e];
+            lg[e] = acc;
+        }
+        double m = lg[0];
+        for (int e = 1; e < E; ++e)
+            if (lg[e] > m)
+                m = lg[e];
+        double s = 0.0;
+        for (int e = 0; e < E; ++e)
+            s += exp(lg[e] - m);
+        for (int e = 0; e < E; ++e)
+            pr[e] = exp(lg[e] - m) / s;
+    }
+}
+
+/* Top-k selection and renormalisation.
+ * The k largest probabilities in descending order (ties: lower index),
+ * then w_j = p_j / sum of the k selected, so the weights sum to one.
+ * [DIVE] sec. 1.3 steps 2-3; [SKILL] sec. 3.1 and sec. 4.2 (top-2 with
+ * renormalisation).  margin[t] = p_(k) - p_(k+1), +inf when k == E. */
+void oracle_topk(int T, int E, int k, const double *probs, int32_t *idx,
+                 double *w, double *margin)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const double *pr = probs + (size_t)t * E;
+        char *taken = (char *)calloc((size_t)E, 1);
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || pr[e] > pr[best]))
+                    best = e;
+            taken[best] = 1;
+            idx[(size_t)t * k + j] = best;
+            sum += pr[best];
+        }
+        for (int j = 0; j < k; ++j)
+            w[(size_t)t * k + j] = pr[idx[(size_t)t * k + j]] / sum;
+        if (margin) {
+            if (k >= E) {
+                margin[t] = INFINITY;
+            } else {
+                int next = -1;
+                for (int e = 0; e < E; ++e)
+                    if (!taken[e] && (next < 0 || pr[e] > pr[next]))
+                        next = e;
+                margin[t] = pr[idx[(size_t)t * k + k - 1]] - pr[next];
+            }
+        }
+        free(taken);
+    }
+}
+
+/* Renormalised weights of a given selection (used when a checker adopts a
+ * different but equally valid choice at a near-tie): w_j = p[sel_j] / sum. */
+void oracle_renorm_selection(int T, int E, int k, const double *probs,
+                             const int32_t *idx, double *w)
+{
+    for (int t = 0; t < T; ++t) {
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j)
+            sum += probs[(size_t)t * E + idx[(size_t)t * k + j]];
+        for (int j = 0; j < k; ++j)
+            w[(size_t)t * k + j] =
+                probs[(size_t)t * E + idx[(size_t)t * k + j]] / sum;
+    }
+}
+
+/* Counting, capacity and dispatch.
+ *   count[e]  = number of (t, j) with idx[t,j] == e        ([SKILL] 4.3,
+ *               the bincount of the selected indices)
+ *   kept[e]   = min(count[e], C), C = capacity or unlimited ([DIVE] 2.3)
+ *   offset[e] = sum of kept[e'] over e' < e; offset[E] = total kept
+ * Assignments are visited in token order, then slot order.  The r-th
+ * assignment to expert e (r counted from 0) is kept when r < C and is
+ * given slot offset[e] + r; otherwise it overflows: slot_of = -1, and the
+ * token skips that expert (its residual passes through, [DIVE] 2.3).
+ * slot_token[s] is the token of slot s; unused slots hold -1. */
+int oracle_dispatch(int T, int E, int k, int capacity, const int32_t *idx,
+                    int32_t *counts, int32_t *kept, int32_t *offsets,
+                    int32_t *slot_token, int32_t *slot_of)
+{
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (size_t a = 0; a < (size_t)T * k; ++a) {
+        int e = idx[a];
+        if (e < 0 || e >= E)
+            return OR_ERR_ARG;
+        counts[e] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        kept[e] = (capacity >= 0 && counts[e] > capacity) ? capacity
+                                                          : counts[e];
+        offsets[e + 1] = offsets[e] + kept[e];
+    }
+    for (size_t s = 0; s < (size_t)T * k; ++s)
+        slot_token[s] = -1;
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int e = idx[(size_t)t * k + j];
+            int r = seen[e]++;
+            if (capacity < 0 || r < capacity) {
+                int s = offsets[e] + r;
+                slot_token[s] = t;
+                slot_of[(size_t)t * k + j] = s;
+            } else {
+                slot_of[(size_t)t * k + j] = -1;
+            }
+        }
+    }
+    free(seen);
+    return OR_OK;
+}
+
+/* Load-balance statistics.
+ *   p_i   = mean over tokens of prob[t,i]         ([DIVE] 2.2; [SKILL] 4.3)
+ *   f_i   = count_i / (T * k), before capacity     ([SKILL] 4.3: bincount
+ *           divided by the number of selected indices)
+ *   L_aux = alpha * E * sum_i f_i * p_i            ([DIVE] 2.2)
+ * With T == 0 everything is 0. */
+void oracle_stats(int T, int E, int k, const double *probs,
+                  const int32_t *counts, double alpha, double *f, double *p,
+                  double *l_aux)
+{
+    double acc = 0.0;
+    for (int e = 0; e < E; ++e) {
+        double s = 0.0;
+        for (int t = 0; t < T; ++t)
+            s += probs[(size_t)t * E + e];
+        p[e] = T > 0 ? s / (double)T : 0.0;
+        f[e] = T > 0 ? (double)counts[e] / ((double)T * (double)k) : 0.0;
+        acc += f[e] * p[e];
+    }
+    *l_aux = alpha * (double)E * acc;
+}
+
+/* One expert applied to one token:
+ *   h = GELU(W1 x + b1),  out = W2 h + b2,  GELU(z) = z/2 (1 + erf(z/sqrt 2))
+ * [GROUP] sec. 3.1 (FFN(x) = W2 GELU(W1 x + b1) + b2); [SKILL] sec. 3.1
+ * (Linear(h, 4h), GELU, Linear(4h, h)).  W1 is [d_ff][d] and W2 is
+ * [d][d_ff], the nn.Linear weight layout.  b1 and b2 may be NULL. */
+static void expert_apply(int d, int d_ff, int dtype, const double *xrow,
+                         const void *w1, const void *b1, const void *w2,
+                         const void *b2, double *h, double *out)
+{
+    for (int f = 0; f < d_ff; ++f) {
+        double z = 0.0;
+        for (int c = 0; c < d; ++c)
+            z += ld(w1, (size_t)f * d + c, dtype) * xrow[c];
+        if (b1)
+            z += ld(b1, (size_t)f, dtype);
+        h[f] = 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+    }
+    for (int c = 0; c < d; ++c) {
+        double o = 0.0;
+        for (int f = 0; f < d_ff; ++f)
+            o += ld(w2, (size_t)c * d_ff + f, dtype) * h[f];
+        if (b2)
+            o += ld(b2, (size_t)c, dtype);
+        out[c] = o;
+    }
+}
+
+/* The layer output for a list of tokens, given their routing:
+ *   y_t = sum over kept j of w[t,j] * Expert_{idx[t,j]}(x_t)  + Shared(x_t)
+ * in slot order j = 0..k-1.  A dropped assignment (slot_of < 0) adds
+ * nothing and the remaining weights are not renormalised.
+ * [DIVE] sec. 1.1 (Output = sum of normalized_weight_i * Expert_i(x));
+ * [DIVE] sec. 3 (Output = Shared_Expert(x) + sum of routed terms);
+ * [SKILL] sec. 3.1 (weighted merge); [DIVE] sec. 2.3 (overflow skips the
+ * experts).
+ * Expert weights come as per-expert pointer tables; an entry may be NULL
+ * for an expert that no listed token uses.  slot_of may be NULL (no
+ * capacity limit: every assignment is kept).  ws1 == NULL means no shared
+ * expert.  y is [n][d] double. */
+int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
+                      int dtype, const void *x, const int32_t *idx,
+                      const double *w, const int32_t *slot_of,
+                      const void *const *w1, const void *const *b1,
+                      const void *const *w2, const void *const *b2,
+                      const void *ws1, const void *bs1, const void *ws2,
+                      const void *bs2, double *y)
+{
+    int status = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n; ++r) {
+        int t = tokens[r];
+        double *xrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        double *yr = y + (size_t)r * d;
+        for (int c = 0; c < d; ++c) {
+            xrow[c] = ld(x, (size_t)t * d + c, dtype);
+            yr[c] = 0.0;
+        }
+        for (int j = 0; j < k; ++j) {
+            size_t a = (size_t)t * k + j;
+            if (slot_of && slot_of[a] < 0)
+                continue;
+            int e = idx[a];
+            if (!w1[e] || !w2[e]) {
+#pragma omp atomic write
+                status = OR_ERR_MISSING_EXPERT;
+                continue;
+            }
+            expert_apply(d, d_ff, dtype, xrow, w1[e], b1 ? b1[e] : NULL,
+                         w2[e], b2 ? b2[e] : NULL, h, o);
+            for (int c = 0; c < d; ++c)
+                yr[c] += w[a] * o[c];
+        }
+        if (ws1) {
+            expert_apply(d, d_ff, dtype, xrow, ws1, bs1, ws2, bs2, h, o);
+            for (int c = 0; c < d; ++c)
+                yr[c] += o[c];
+        }
+        free(xrow);
+        free(h);
+        free(o);
+    }
+    return status;
+}
+
+/* Auxiliary-loss-free balancing, one step on float32 state:
+ *   b_i <- b_i + gamma * sign(count_i - target),  sign(0) = 0
+ * An overloaded expert's bias grows, which lowers its adjusted logit
+ * (logit - b_i) on the next call.  [DIVE] sec. 2.4; [SKILL] sec. 4.3. */
+void oracle_bias_update(int E, const int32_t *counts, float target,
+                        float gamma, float *bias)
+{
+    for (int e = 0; e < E; ++e) {
+        float c = (float)counts[e];
+        float sgn = c > target ? 1.0f : (c < target ? -1.0f : 0.0f);
+        volatile float step = gamma * sgn; /* exactly +-gamma or 0 */
+        bias[e] = bias[e] + step;
+    }
+}

@@ -1,0 +1,419 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle step to a value the pages print, a closed form, an
+invariant, brute force on a tiny input, or a special case that reduces to a
+library routine (torch's float64 Linear / GELU / softmax, numpy's stable
+sort and bincount).  Every test is chosen so that a plausible slip in the
+oracle (a dropped bias term, a flipped sign, a transposed weight, a wrong
+tie rule, an off-by-one in the capacity rank) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden",
+                      "page_examples.json")
+
+
+def golden(name):
+    with open(GOLDEN) as fh:
+        return json.load(fh)[name]
+
+
+def dense_ffn_torch(x, w1, b1, w2, b2):
+    """Textbook two-layer MLP with exact GELU via torch float64 library
+    calls (the dense FFN the layer reduces to)."""
+    f = lambda a: None if a is None else torch.as_tensor(a).double()
+    h = torch.nn.functional.linear(f(x), f(w1), f(b1))
+    h = torch.nn.functional.gelu(h, approximate="none")
+    return torch.nn.functional.linear(h, f(w2), f(b2)).numpy()
+
+
+def tiny_inputs(T=16, d=8, E=4, d_ff=12, seed=3, biases=True):
+    w = workloads.Workload(name="t", T=T, d=d, E=E, k=1, d_ff=d_ff,
+                           dtype="f32", router_bias="linear" if biases
+                           else "none", linear_biases=biases, seed=seed)
+    return w, workloads.make_inputs(w)
+
+
+# ----------------------------------------------------------------- router
+def test_router_closed_form_permutation_weights():
+    # Wr is a permutation matrix: logit_e = x[pi(e)] exactly, so softmax is
+    # q / sum(q) for x = log q.  A transposed Wr gives x[pi^-1(e)] instead.
+    E = 5
+    pi = [2, 0, 4, 1, 3]                    # not an involution
+    wr = np.zeros((E, E), np.float32)
+    for e, c in enumerate(pi):
+        wr[e, c] = 1.0
+    q = np.array([1, 2, 3, 4, 6], np.float64)
+    x = np.log(q).astype(np.float32)[None, :]
+    logits, probs = oracle.router(x, wr)
+    xq = np.exp(x.astype(np.float64)[0])
+    expect = xq[pi] / xq.sum()
+    assert np.allclose(probs[0], expect, rtol=1e-15, atol=0)
+    assert np.allclose(logits[0], x.astype(np.float64)[0][pi], rtol=0,
+                       atol=0)
+
+
+def test_router_bias_signs():
+    # Additive router bias shifts logits up, the balancing bias shifts them
+    # down: with add == sub the probabilities are unchanged, and a
+    # subtracted log r divides each probability by r (then renormalises).
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((6, 8)).astype(np.float32)
+    wr = rng.standard_normal((4, 8)).astype(np.float32)
+    r = np.array([1.0, 2.0, 4.0, 0.5], np.float32)
+    add = rng.standard_normal(4).astype(np.float32)
+    _, p0 = oracle.router(x, wr)
+    la, pa = oracle.router(x, wr, add_bias=add)
+    logr = np.log(r).astype(np.float32)
+    ls, ps = oracle.router(x, wr, sub_bias=logr)
+    _, pboth = oracle.router(x, wr, add_bias=add, sub_bias=add)
+    l0, _ = oracle.router(x, wr)
+    assert np.allclose(la - l0, add.astype(np.float64)[None, :], atol=1e-12)
+    assert np.allclose(pboth, p0, rtol=1e-13, atol=1e-16)
+    expect = p0 / np.exp(logr.astype(np.float64))[None, :]
+    expect /= expect.sum(1, keepdims=True)
+    assert np.allclose(ps, expect, rtol=1e-12, atol=1e-16)
+    assert not np.allclose(pa, p0)
+
+
+def test_router_softmax_shift_invariance_and_uniform():
+    x = np.ones((3, 4), np.float32)
+    wr = np.zeros((8, 4), np.float32)
+    _, p = oracle.router(x, wr, add_bias=np.full(8, 7.5, np.float32))
+    assert np.all(p == 1.0 / 8)             # exp(0)/8 is exact
+    # huge logits must not overflow: max subtraction
+    wr2 = np.zeros((3, 4), np.float32)
+    wr2[1, 0] = 1.0
+    _, p2 = oracle.router(np.full((1, 4), 1000.0, np.float32), wr2)
+    assert p2[0, 1] == 1.0 and p2[0, 0] == 0.0
+
+
+# ------------------------------------------------------------------ top-k
+def brute_topk(p, k):
+    """Every k-subset; the best has the largest sum, ties to the
+    lexicographically smallest sorted index set; order by (-p, index)."""
+    best = None
+    for sub in itertools.combinations(range(len(p)), k):
+        s = sum(p[i] for i in sub)
+        if best is None or s > best[0]:
+            best = (s, sub)
+    sel = sorted(best[1], key=lambda i: (-p[i], i))
+    return sel
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 9).flatmap(lambda E: st.tuples(
+    st.just(E), st.integers(1, E),
+    st.lists(st.integers(1, 6), min_size=E, max_size=E))))
+def test_topk_brute_force_with_ties(args):
+    E, k, ints = args
+    # small-integer probabilities make exact ties common
+    p = np.array(ints, np.float64) / 64.0
+    idx, w, margin = oracle.topk(p[None, :], k)
+    assert list(idx[0]) == brute_topk(list(p), k)
+    sel = p[idx[0]]
+    assert np.allclose(w[0], sel / sel.sum(), rtol=1e-15)
+    assert abs(w[0].sum() - 1.0) < 1e-12
+    if k < E:
+        rest = np.delete(p, idx[0])
+        assert margin[0] == sel[-1] - rest.max()
+    else:
+        assert math.isinf(margin[0])
+
+
+def test_topk_golden_renorm_figure():
+    g = golden("renorm_figure")
+    p = np.array(g["probs"], np.float64)
+    assert abs(p.sum() - 1.0) < 1e-15
+    idx, w, _ = oracle.topk(p[None, :], g["k"])
+    assert list(idx[0]) == g["topk_idx"]
+    assert np.allclose(w[0], g["topk_w"], rtol=1e-15, atol=1e-15)
+
+
+def test_topk_golden_router_vector():
+    g = golden("router_vector")
+    E = g["E"]
+    p = np.full(E, g["tail"])
+    p[:3] = g["head"]
+    p /= p.sum()
+    idx, w, _ = oracle.topk(p[None, :], g["k"])
+    assert idx[0, 0] == g["top1_idx"] and w[0, 0] == g["top1_w"]
+
+
+def test_activation_ratio_golden():
+    g = golden("activation_ratio")
+    rng = np.random.default_rng(1)
+    p = rng.random((100, g["E"]))
+    idx, _, _ = oracle.topk(p, g["k"])
+    d = oracle.dispatch(idx, g["E"], -1)
+    assert d["counts"].sum() == 100 * g["k"]
+    # every token activates exactly k distinct experts
+    assert all(len(set(r)) == g["k"] for r in idx.tolist())
+    assert g["k"] / g["E"] == g["ratio"]
+
+
+def test_renorm_single_expert_is_one():
+    rng = np.random.default_rng(2)
+    p = rng.random((50, 16))
+    p /= p.sum(1, keepdims=True)
+    idx, w, _ = oracle.topk(p, 1)
+    assert np.all(w == 1.0)
+    assert np.array_equal(idx[:, 0], np.argmax(p, axis=1))   # argmax routing
+
+
+# --------------------------------------------------------------- dispatch
+def test_capacity_golden():
+    g = golden("capacity")
+    for c in g["cases"]:
+        assert oracle.capacity(c["T"], c["E"], c["cf"]) == c["C"], c
+    assert oracle.capacity(10, 2, None) == -1
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 6), st.integers(1, 3),
+       st.integers(-1, 12), st.integers(0, 10_000))
+def test_dispatch_against_stable_sort(T, E, k, cap, seed):
+    k = min(k, E)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(
+        np.int32)
+    d = oracle.dispatch(idx, E, cap)
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(d["counts"], counts)
+    kept = counts if cap < 0 else np.minimum(counts, cap)
+    assert np.array_equal(d["kept"], kept)
+    assert np.array_equal(d["offsets"], np.concatenate([[0],
+                                                        np.cumsum(kept)]))
+    # token-major order of assignments, grouped stably by expert
+    order = np.argsort(flat, kind="stable")
+    rank = np.empty_like(flat)
+    for e in range(E):
+        members = order[flat[order] == e]
+        rank[members] = np.arange(len(members))
+    keep = (rank < cap) if cap >= 0 else np.ones_like(flat, bool)
+    slot_of = np.where(keep, d["offsets"][flat] + rank, -1)
+    assert np.array_equal(d["slot_of"].reshape(-1), slot_of)
+    st_ = np.full(T * k, -1, np.int32)
+    st_[slot_of[keep]] = (np.arange(T * k) // k)[keep]
+    assert np.array_equal(d["slot_token"], st_)
+    # structure: increasing tokens within each segment
+    for e in range(E):
+        seg = d["slot_token"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_dispatch_zero_capacity_and_empty():
+    idx = np.array([[0], [1], [0]], np.int32)
+    d = oracle.dispatch(idx, 2, 0)
+    assert np.all(d["slot_of"] == -1) and d["offsets"][-1] == 0
+    d0 = oracle.dispatch(np.zeros((0, 2), np.int32), 3, -1)
+    assert np.all(d0["counts"] == 0) and d0["offsets"][-1] == 0
+
+
+# ------------------------------------------------------------------ stats
+def test_aux_loss_uniform_golden():
+    g = golden("aux_loss_uniform")
+    # zero router weights: every probability is exactly 1/E
+    T, d, E, k = 64, 8, 8, 2
+    x = np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)
+    _, probs = oracle.router(x, np.zeros((E, d), np.float32))
+    idx, _, _ = oracle.topk(probs, k)
+    disp = oracle.dispatch(idx, E, -1)
+    f, p, l_aux = oracle.stats(probs, disp["counts"], k, g["alpha"])
+    assert abs(l_aux - g["l_aux"]) < 1e-15
+    assert abs(f.sum() - 1) < 1e-15 and abs(p.sum() - 1) < 1e-15
+
+
+def test_aux_loss_collapse_and_sums():
+    # all tokens on expert 2 with probability 1: L = alpha * E
+    T, E = 10, 4
+    probs = np.zeros((T, E))
+    probs[:, 2] = 1.0
+    counts = np.array([0, 0, T, 0], np.int32)
+    f, p, l = oracle.stats(probs, counts, 1, 0.01)
+    assert abs(l - 0.01 * E) < 1e-15
+    # f is before capacity and normalised by T*k
+    rng = np.random.default_rng(5)
+    pr = rng.random((30, 6))
+    pr /= pr.sum(1, keepdims=True)
+    idx, _, _ = oracle.topk(pr, 3)
+    c = oracle.dispatch(idx, 6, 2)["counts"]
+    f, p, l = oracle.stats(pr, c, 3, 0.5)
+    assert np.allclose(f, np.bincount(idx.reshape(-1), minlength=6) / 90)
+    assert np.allclose(p, pr.mean(0))
+    assert abs(l - 0.5 * 6 * float(np.dot(f, p))) < 1e-14
+
+
+# -------------------------------------------------------------- expert FFN
+def test_single_expert_is_dense_ffn():
+    # E = 1, k = 1: p = w = 1 and the layer is the dense FFN
+    w, inp = tiny_inputs(E=1)
+    out = oracle.forward(inp, k=1)
+    ref = dense_ffn_torch(inp["x"], inp["w1"][0], inp["b1"][0],
+                          inp["w2"][0], inp["b2"][0])
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_gelu_textbook_values():
+    # one hidden unit, identity read-out: y = GELU(z) for chosen z
+    zs = np.array([-3.0, -1.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    x = zs[:, None]
+    w1 = np.ones((1, 1), np.float32)
+    w2 = np.ones((1, 1), np.float32)
+    ex = oracle.Experts(1, lambda e: (w1, None, w2, None))
+    y = oracle.layer_rows(range(len(zs)), x, np.zeros((6, 1), np.int32),
+                          np.ones((6, 1)), None, ex)
+    phi = np.array([0.0013498980316301, 0.15865525393145707, 0.5,
+                    0.6914624612740131, 0.8413447460685429,
+                    0.9772498680518208])            # standard normal CDF
+    assert np.allclose(y[:, 0], zs * phi, rtol=1e-13, atol=1e-15)
+
+
+def test_identical_experts_independent_of_routing():
+    w, inp = tiny_inputs(E=6, T=40)
+    for key in ("w1", "b1", "w2", "b2"):
+        inp[key] = inp[key][:1].repeat(6, *([1] * (inp[key].dim() - 1)))
+    out = oracle.forward(inp, k=3)
+    ref = dense_ffn_torch(inp["x"], inp["w1"][0], inp["b1"][0],
+                          inp["w2"][0], inp["b2"][0])
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_soft_mixture_k_equals_E():
+    w, inp = tiny_inputs(E=4, T=20)
+    out = oracle.forward(inp, k=4)
+    logits = torch.nn.functional.linear(inp["x"].double(),
+                                        inp["wr"].double(),
+                                        inp["br"].double())
+    p = torch.softmax(logits, -1).numpy()
+    ref = sum(p[:, e:e + 1] * dense_ffn_torch(
+        inp["x"], inp["w1"][e], inp["b1"][e], inp["w2"][e], inp["b2"][e])
+        for e in range(4))
+    assert np.allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+    assert np.allclose(out["probs"], p, rtol=1e-12)
+
+
+def test_shared_expert_alone():
+    w, inp = tiny_inputs(E=4, T=20)
+    sh = workloads.make_expert(w, 0, shared=True)
+    inp.update(ws1=sh[0], bs1=sh[1], ws2=sh[2], bs2=sh[3])
+    inp["w2"].zero_()
+    inp["b2"].zero_()
+    out = oracle.forward(inp, k=2)
+    ref = dense_ffn_torch(inp["x"], *sh)
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+    # and shared + routed is the sum of both parts
+    w_, inp2 = tiny_inputs(E=4, T=20)
+    routed = oracle.forward(inp2, k=2)["y"]
+    inp2.update(ws1=sh[0], bs1=sh[1], ws2=sh[2], bs2=sh[3])
+    both = oracle.forward(inp2, k=2)["y"]
+    assert np.allclose(both, routed + ref, rtol=1e-12, atol=1e-13)
+
+
+def test_top2_combine_by_definition_of_pages():
+    # y_t = w0 * FFN_{i0}(x) + w1 * FFN_{i1}(x) with the renormalised
+    # top-2 weights: each term from the torch dense reduction.
+    w, inp = tiny_inputs(E=5, T=12)
+    out = oracle.forward(inp, k=2)
+    for t in range(12):
+        ref = 0
+        for j in range(2):
+            e = out["topk_idx"][t, j]
+            ref = ref + out["topk_w"][t, j] * dense_ffn_torch(
+                inp["x"][t:t + 1], inp["w1"][e], inp["b1"][e], inp["w2"][e],
+                inp["b2"][e])[0]
+        assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_capacity_drops_give_exact_zero():
+    w, inp = tiny_inputs(E=4, T=64, biases=False)
+    out = oracle.forward(inp, k=1, capacity_factor=0.5)   # C = 8
+    assert out["capacity"] == 8
+    dropped = out["slot_of"][:, 0] < 0
+    assert dropped.any() and (~dropped).any()
+    assert np.all(out["y"][dropped] == 0.0)
+    kept_rows = ~dropped
+    e0 = out["topk_idx"][kept_rows, 0]
+    xs = inp["x"][kept_rows]
+    for i, e in enumerate(e0):
+        ref = dense_ffn_torch(xs[i:i + 1], inp["w1"][e], None, inp["w2"][e],
+                              None)
+        assert np.allclose(out["y"][kept_rows][i], ref[0], rtol=1e-12,
+                           atol=1e-13)
+    # the first C tokens in token order are the kept ones, per expert
+    for e in range(4):
+        toks = np.nonzero(out["topk_idx"][:, 0] == e)[0]
+        assert np.array_equal(out["slot_of"][toks[:8], 0] >= 0,
+                              np.ones(min(8, len(toks)), bool))
+        assert np.all(out["slot_of"][toks[8:], 0] == -1)
+    zero = oracle.forward(inp, k=1, capacity_factor=0.01)  # C = 0
+    assert zero["capacity"] == 0 and np.all(zero["y"] == 0.0)
+
+
+def test_scaling_second_layer_by_two_is_exact():
+    w, inp = tiny_inputs(E=4, T=16)
+    y1 = oracle.forward(inp, k=2)["y"]
+    inp["w2"] = inp["w2"] * 2
+    inp["b2"] = inp["b2"] * 2
+    y2 = oracle.forward(inp, k=2)["y"]
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_bf16_inputs_widen_exactly():
+    # bf16 bit patterns are widened exactly: same result as the float32
+    # copy of the same values
+    w, inp = tiny_inputs(E=4, T=16)
+    bf = {k: (v.to(torch.bfloat16) if isinstance(v, torch.Tensor) and
+              k not in ("br", "ebias") else v) for k, v in inp.items()}
+    f32 = {k: (v.float() if isinstance(v, torch.Tensor) else v)
+           for k, v in bf.items()}
+    a = oracle.forward(bf, k=2)
+    b = oracle.forward(f32, k=2)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["probs"], b["probs"])
+
+
+# -------------------------------------------------------------- bias step
+def test_bias_update_golden():
+    g = golden("bias_update")
+    b = np.array(g["bias_in"], np.float32)
+    nb = oracle.bias_update(np.array(g["counts"], np.int32), g["target"],
+                            g["gamma"], b)
+    expect = b + np.float32(g["gamma"]) * np.array(g["sign"], np.float32)
+    assert np.array_equal(nb, expect.astype(np.float32))
+    assert nb[1] == b[1]                     # exactly on target: unchanged
+    # the higher bias lowers the adjusted logit of an overloaded expert
+    x = np.ones((1, 2), np.float32)
+    wr = np.ones((4, 2), np.float32)
+    _, p_before = oracle.router(x, wr, sub_bias=np.zeros(4, np.float32))
+    _, p_after = oracle.router(x, wr, sub_bias=nb - b)
+    assert p_after[0, 0] < p_before[0, 0] and p_after[0, 2] > p_before[0, 2]
+
+
+def test_capacity_top2_keeps_pre_drop_weight():
+    # A dropped assignment adds nothing and the surviving weight is not
+    # renormalised: y_t = w_kept * FFN_kept(x_t).
+    w, inp = tiny_inputs(E=3, T=48, biases=False)
+    out = oracle.forward(inp, k=2, capacity_factor=1.0)     # C = 16
+    so = out["slot_of"]
+    part = (so[:, 0] >= 0) ^ (so[:, 1] >= 0)
+    assert part.any()
+    for t in np.nonzero(part)[0]:
+        j = 0 if so[t, 0] >= 0 else 1
+        e = out["topk_idx"][t, j]
+        ref = out["topk_w"][t, j] * dense_ffn_torch(
+            inp["x"][t:t + 1], inp["w1"][e], None, inp["w2"][e], None)[0]
+        assert out["topk_w"][t, j] < 1.0
+        assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
