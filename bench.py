@@ -1,0 +1,207 @@
+"""Benchmark of the sparse MoE FFN layer forward on one MI355X.
+
+A step is one whole layer forward (router + top-k, permute, grouped expert
+FFNs, combine) over one batch of seeded synthetic tokens already resident in
+HBM.  Prints ONE JSON line with tokens/s, the roofline position of the
+dominant kernel (the grouped up-projection GEMM) measured with HIP events
+on the stream it runs on, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector/matrix
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU-oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def algorithmic(wl, counts, kept):
+    """FLOPs and bytes of one forward (kept rows only, touched experts)."""
+    import numpy as np
+    es = wl.elem_bytes
+    rows = int(np.sum(kept)) + wl.n_shared * wl.T
+    touched = int(np.sum(kept > 0)) + wl.n_shared
+    flops = 2.0 * wl.T * wl.d * wl.E + 4.0 * rows * wl.d * wl.d_ff
+    expert_bytes = (2 * wl.d * wl.d_ff + (wl.d + wl.d_ff if wl.linear_biases
+                                          else 0)) * es
+    bytes_ = (wl.E * wl.d * es + touched * expert_bytes +
+              2 * wl.T * wl.d * es)
+    up_flops = 2.0 * rows * wl.d * wl.d_ff
+    up_bytes = touched * wl.d * wl.d_ff * es + rows * (wl.d + wl.d_ff) * es
+    return dict(flops=flops, bytes=bytes_, rows=rows, touched=touched,
+                up_flops=up_flops, up_bytes=up_bytes)
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The oracle, as it stands, on the first n tokens of the same inputs
+    (n sized to the time budget), through the whole layer."""
+    import numpy as np
+    import torch
+    import oracle
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v)
+            for k, v in inp.items()}
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp:
+        cores = min(cores, int(omp))
+
+    def run(n):
+        sub = dict(host)
+        sub["x"] = host["x"][:n]
+        t0 = time.perf_counter()
+        oracle.forward(sub, wl.k, wl.capacity_factor, wl.alpha)
+        return time.perf_counter() - t0
+
+    n = min(wl.T, max(1, cores))
+    dt = run(n)
+    while dt < budget_s / 4 and n < wl.T:
+        n = min(wl.T, max(n + 1, int(n * min(8.0, budget_s / max(dt, 1e-3)
+                                              / 2))))
+        dt = run(n)
+    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"first {n} of {wl.T} tokens of {wl.name}, whole "
+                       f"layer (router to combine) in fp64, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus "
+              f"{args.gpus}); the layer is not sharded across GPUs",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_50_amd as moe
+    import workloads
+
+    wl = workloads.get(args.workload)
+    steps = args.steps if args.steps is not None else (
+        wl.calls if wl.calls > 1 else 20)
+    warmup = args.warmup
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.name}: generating inputs on {dev}")
+    inp = workloads.make_inputs(wl, dev)
+    n_x = wl.calls
+    xs = [inp["x"]] + [workloads.make_x(wl, dev, c) for c in range(1, n_x)]
+    weights = moe.Weights.from_dict(inp)
+    layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha)
+    desc, r, ws, y = layer.buffers(wl.T)
+    stream = torch.cuda.current_stream(dev)
+
+    up_ev = []
+
+    def step(i, timed):
+        x = xs[i % n_x]
+        moe.moe_router_topk(desc, x, weights, r, ws)
+        moe.moe_permute(desc, r, ws)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        moe.moe_ffn_up(desc, x, weights, r, ws)
+        if timed:
+            e1.record(stream)
+            up_ev.append((e0, e1))
+        moe.moe_ffn_down(desc, weights, r, ws)
+        moe.moe_combine(desc, r, y, ws)
+
+    log(f"[bench] warmup {warmup}")
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    up_ms = [a.elapsed_time(b) for a, b in up_ev]
+    up_avg_ms = float(np.mean(up_ms))
+    ms_per_step = total_ms / steps
+
+    # algorithmic work of the last call (counts of each call are similar;
+    # decode calls differ, so average their touched/row counts)
+    counts = r.counts.cpu().numpy()
+    kept = r.kept.cpu().numpy()
+    alg = algorithmic(wl, counts, kept)
+    assert int(counts.sum()) == wl.T * wl.k
+    tokens_per_s = wl.T * steps / (total_ms / 1e3)
+    if wl.T * wl.k / wl.E <= 48:
+        roof = dict(bound="hbm", achieved=alg["up_bytes"] / (up_avg_ms * 1e6),
+                    peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" \
+            else MFMA_F32_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=alg["up_flops"] /
+                    (up_avg_ms * 1e9), peak=peak, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped GEMM up (moe_ffn_up)"
+    roof["kernel_ms"] = up_avg_ms
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer fwd tokens/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E,
+                   "k": wl.k, "d_ff": wl.d_ff, "n_shared": wl.n_shared,
+                   "capacity_factor": wl.capacity_factor,
+                   "parallelism": "single-gpu"},
+        "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
+        "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),
+        "wall_s": wall,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

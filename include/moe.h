@@ -1,0 +1,201 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer
+ * forward.
+ *
+ * The layer (sources are the pages' titles and sections):
+ *   1. router logits  l[t,e] = x[t,:] . Wr[e,:] + add[e] - b[e], softmax
+ *      ("MoE architecture deep dive", sec. 1.2 gating network; sec. 2.4
+ *      aux-loss-free balancing subtracts b);
+ *   2. top-k with renormalised weights (same page, sec. 1.3 steps 2-3;
+ *      "AI-Research-SKILLs MoE training guide", sec. 3.1 and 4.2);
+ *   3. per-expert counts, optional capacity C = floor(T/E * cf), stable
+ *      token-order dispatch; overflow assignments skip the expert
+ *      ("MoE architecture deep dive", sec. 2.3);
+ *   4. each expert: W2 GELU(W1 x + b1) + b2 with exact erf GELU
+ *      ("The expert group activated per token", sec. 3.1 FFN formula);
+ *      optional always-on shared expert ("MoE architecture deep dive",
+ *      sec. 3, DeepSeek-V3 shared expert);
+ *   5. y[t] = sum_j w[t,j] Expert_{idx[t,j]}(x[t]) (+ Shared(x[t]))
+ *      ("MoE architecture deep dive", sec. 1.1);
+ *   6. f_i = count_i / (T k), p_i = mean_t p[t,i],
+ *      L_aux = alpha * E * sum f_i p_i (same page, sec. 2.2; "AI-Research-
+ *      SKILLs MoE training guide", sec. 4.3);
+ *   7. balancing-bias step b_i += gamma * sign(count_i - target)
+ *      ("MoE architecture deep dive", sec. 2.4).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in the structs and arguments are DEVICE pointers unless
+ *     stated otherwise; arrays are row-major and contiguous.
+ *   - The caller owns every buffer, including the workspace sized by
+ *     moe_workspace_size().  The library allocates nothing, keeps no state
+ *     between calls, and only enqueues work on `stream` (a hipStream_t;
+ *     NULL is the default stream).  No call synchronises the device or
+ *     reads device data back to the host.
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check returns a negative moe_status and enqueues nothing.  A failed
+ *     kernel launch returns MOE_ERR_HIP.  T == 0 is valid: once the
+ *     descriptor passes its checks the call returns MOE_OK, enqueues
+ *     nothing and does not look at the pointers.  Non-finite inputs are not
+ *     checked.
+ *   - Calls on distinct streams with distinct workspaces may run
+ *     concurrently.
+ *   - The residual is not applied: a token whose every assignment
+ *     overflowed capacity gets y = 0 exactly, so the caller's x + y passes
+ *     it through unchanged.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k out of range */
+    MOE_ERR_UNSUPPORTED = -2, /* shape or dtype this library cannot run */
+    MOE_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape, host struct passed by pointer.
+ *   T         tokens (>= 0)
+ *   d         model width; multiple of 64
+ *   E         routed experts, 1 <= E <= 256
+ *   k         experts per token, 1 <= k <= E
+ *   d_ff      expert hidden width; multiple of 64
+ *   n_shared  0 or 1 always-on shared expert (weight 1)
+ *   dtype     MOE_F32 or MOE_BF16 for x, all weight matrices, the expert
+ *             Linear biases and y (arithmetic accumulates in fp32)
+ *   capacity  -1 = no limit, else C >= 0 assignments kept per expert
+ *             (see moe_capacity)
+ *   aux_alpha coefficient of L_aux (0.01 is the pages' usual value) */
+typedef struct moe_desc {
+    int32_t T, d, E, k, d_ff;
+    int32_t n_shared;
+    int32_t dtype;
+    int32_t capacity;
+    float aux_alpha;
+} moe_desc;
+
+/* Weights: caller-owned, read-only device buffers; NULL = absent.
+ *   w_router    [E][d]        dtype                 (required)
+ *   b_router    [E]           fp32, ADDED to logits (nn.Linear bias, or a
+ *                             fixed per-expert skew)
+ *   expert_bias [E]           fp32, SUBTRACTED from logits (aux-loss-free
+ *                             balancing); enters softmax, selection and
+ *                             weights
+ *   w1, b1      [E][d_ff][d], [E][d_ff]   dtype (w1 required)
+ *   w2, b2      [E][d][d_ff], [E][d]      dtype (w2 required)
+ *   ws1..bs2    shared expert, same shapes without the E axis; ws1/ws2
+ *               required iff n_shared == 1 */
+typedef struct moe_weights {
+    const void *w_router;
+    const float *b_router;
+    const float *expert_bias;
+    const void *w1, *b1;
+    const void *w2, *b2;
+    const void *ws1, *bs1, *ws2, *bs2;
+} moe_weights;
+
+/* Routing results and statistics: caller-owned device buffers.
+ *   topk_idx   [T][k] int32  selected experts, descending probability,
+ *                            ties to the lower index
+ *   topk_w     [T][k] fp32   renormalised weights (sum 1 per token)
+ *   counts     [E]    int32  assignments per expert, before capacity
+ *   kept       [E]    int32  min(counts, C)
+ *   offsets    [E+1]  int32  exclusive prefix sum of kept
+ *   slot_token [T*k]  int32  token of each expert-sorted slot; slots at
+ *                            and beyond offsets[E] hold -1
+ *   slot_of    [T][k] int32  slot of each assignment, -1 if it overflowed
+ *   f, p       [E]    fp32   f_i = counts_i/(T k), p_i = mean_t p[t,i]
+ *   l_aux      [1]    fp32   alpha * E * sum_i f_i p_i */
+typedef struct moe_routing {
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *counts, *kept, *offsets;
+    int32_t *slot_token, *slot_of;
+    float *f, *p, *l_aux;
+} moe_routing;
+
+/* Host.  floor((double)T / E * cf): the capacity formula of "MoE
+ * architecture deep dive", sec. 2.3.  Returns -1 if cf < 0 (no limit) and
+ * MOE_ERR_INVALID_ARG if T < 0 or E < 1. */
+int32_t moe_capacity(int32_t T, int32_t E, double cf);
+
+/* Host, pure.  Bytes of workspace the calls below need for this shape, or 0
+ * if the descriptor is invalid.  One workspace serves every entry point;
+ * moe_router_topk writes router partial sums into it that moe_permute reads,
+ * and moe_grouped_ffn writes the expert outputs that moe_combine reads, so
+ * run a sequence of calls with one workspace. */
+size_t moe_workspace_size(const moe_desc *desc);
+
+/* Router GEMM fused with bias, softmax, top-k and renormalisation
+ * (layer steps 1-2).  Reads x [T][d] and the router weights; writes
+ * r->topk_idx, r->topk_w and per-token-tile probability column sums into
+ * the workspace (consumed by moe_permute for p_i). */
+int moe_router_topk(const moe_desc *desc, const void *x,
+                    const moe_weights *w, moe_routing *r, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* Counts, capacity, stable dispatch and statistics (layer steps 3 and 6).
+ * Reads r->topk_idx and the router partial sums in the workspace; writes
+ * counts, kept, offsets, slot_token, slot_of, f, p and l_aux. */
+int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* Grouped expert FFNs (layer step 4): for every kept slot s of expert e,
+ *   Yp[s] = W2_e GELU(W1_e x[slot_token[s]] + b1_e) + b2_e,
+ * and, with a shared expert, Yp[T*k + t] = Shared(x[t]) for every token.
+ * Yp is written into the workspace (dtype, [T*k + n_shared*T][d]); the
+ * hidden activations are rounded to dtype between the two GEMMs.
+ * Equivalent to moe_ffn_up followed by moe_ffn_down. */
+int moe_grouped_ffn(const moe_desc *desc, const void *x,
+                    const moe_weights *w, const moe_routing *r, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* First half of moe_grouped_ffn: H[s] = GELU(W1_e x[token(s)] + b1_e)
+ * into the workspace (one kernel launch). */
+int moe_ffn_up(const moe_desc *desc, const void *x, const moe_weights *w,
+               const moe_routing *r, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* Second half of moe_grouped_ffn: Yp[s] = W2_e H[s] + b2_e (one launch). */
+int moe_ffn_down(const moe_desc *desc, const moe_weights *w,
+                 const moe_routing *r, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Weighted combine (layer step 5): y[t] = sum over kept j, in j order, of
+ * topk_w[t,j] * Yp[slot_of[t,j]], plus Yp[T*k + t] with a shared expert;
+ * fp32 accumulation, one rounding to dtype.  y is [T][d], dtype. */
+int moe_combine(const moe_desc *desc, const moe_routing *r, void *y,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* The whole forward: moe_router_topk, moe_permute, moe_grouped_ffn and
+ * moe_combine on one stream. */
+int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
+                moe_routing *r, void *y, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* Balancing-bias step (layer step 7), in place on fp32 state:
+ * bias[e] = bias[e] + gamma * sign(counts[e] - target), sign(0) = 0, one
+ * fp32 add.  Apply after a forward; it affects the next call. */
+int moe_bias_update(int32_t E, const int32_t *counts, float target,
+                    float gamma, float *expert_bias, void *stream);
+
+/* Host.  Static English text of a moe_status value. */
+const char *moe_status_string(int status);
+
+/* Host.  Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -277,7 +277,8 @@ def bias_update(counts, target: float, gamma: float, bias) -> np.ndarray:
 
 def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
             alpha: float = 0.01, tokens: Optional[Sequence[int]] = None,
-            selection: Optional[np.ndarray] = None) -> dict:
+            selection: Optional[np.ndarray] = None,
+            probs: Optional[np.ndarray] = None) -> dict:
     """The whole layer, step by step, as the pages define it.
 
     ``inp`` holds x, wr, br, ebias, w1, b1, w2, b2, ws1, bs1, ws2, bs2 (the
@@ -285,11 +286,14 @@ def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
     expert evaluation to some rows (routing, counts and statistics always
     cover every token).  ``selection`` replaces the oracle's own top-k
     choice (a checker adopting equally valid picks at near-ties); the
-    weights are then renormalised from the oracle's probabilities."""
+    weights are then renormalised from the oracle's probabilities.
+    ``probs`` passes in this oracle's own router output from an earlier
+    call on the same inputs, to skip recomputing it."""
     x = inp["x"]
     T = x.shape[0]
     E = inp["wr"].shape[0]
-    _, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
+    if probs is None:
+        _, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
     idx, w, margin = topk(probs, k)
     if selection is not None:
         idx = np.ascontiguousarray(selection, dtype=np.int32)

@@ -1,0 +1,140 @@
+// Device-side helpers shared by the HIP kernels of the MoE layer (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_E 256
+#define MOE_MAX_GROUPS (MOE_MAX_E + 1)   // routed experts + one shared
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (promotes to registers, unlike the struct uint4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ bfloat16
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+    return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+    return __uint_as_float(w & 0xFFFF0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+// Round-to-nearest-even float -> bfloat16 (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Exact-erf GELU: z/2 * (1 + erf(z / sqrt 2)), with the device erff.
+__device__ __forceinline__ float gelu_erf(float z) {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+// ------------------------------------------------------------- wave ops
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ---------------------------------------------------------- tile table
+// Groups g = 0..E-1 are the routed experts (rows offsets[g]..offsets[g+1]),
+// group E (when n_shared) is the shared expert with rows
+// shared_base..shared_base+T.  Tiles of a group are enumerated n-tile major,
+// m-tile minor, so consecutive tiles share one weight panel.
+struct TileTable {
+    int base[MOE_MAX_GROUPS + 1];   // first tile of each group
+    int start[MOE_MAX_GROUPS];      // first slot row of each group
+    int rows[MOE_MAX_GROUPS];
+    int mt[MOE_MAX_GROUPS];         // m-tiles of each group
+};
+
+// Build the table in LDS with the whole block; ends with __syncthreads().
+__device__ __forceinline__ void build_tile_table(
+    TileTable &tt, const int32_t *__restrict__ offsets, int E, int n_shared,
+    int shared_base, int T, int BM, int n_tiles_n) {
+    const int G = E + n_shared;
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        int st, rw;
+        if (g < E) {
+            st = offsets[g];
+            rw = offsets[g + 1] - st;
+        } else {
+            st = shared_base;
+            rw = T;
+        }
+        int mt = (rw + BM - 1) / BM;
+        tt.start[g] = st;
+        tt.rows[g] = rw;
+        tt.mt[g] = mt;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = (G + 63) / 64;
+        const int g0 = lane * per;
+        int local = 0;
+        for (int i = 0; i < per; ++i)
+            if (g0 + i < G) local += tt.mt[g0 + i] * n_tiles_n;
+        int incl = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        int run = incl - local;
+        for (int i = 0; i < per; ++i) {
+            if (g0 + i < G) {
+                tt.base[g0 + i] = run;
+                run += tt.mt[g0 + i] * n_tiles_n;
+            }
+        }
+        if (lane == 63) tt.base[G] = incl;
+    }
+    __syncthreads();
+}
+
+// Largest g with base[g] <= L (base[G] > L assumed).
+__device__ __forceinline__ int find_group(const TileTable &tt, int G, int L) {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (tt.base[mid] <= L) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// Arguments of one grouped GEMM pass (up: gathered x -> H with GELU;
+// down: H -> Yp).  Weight panels are row-major [N][K] per group.
+struct GemmParams {
+    const void *A;            // up: x [T][K]; down: H [slots][K]
+    const int32_t *slot_token;
+    const int32_t *offsets;   // [E+1]
+    const void *W;            // [E][N][K]
+    const void *bias;         // [E][N] or null
+    const void *Ws;           // shared [N][K] or null
+    const void *bias_s;       // shared [N] or null
+    void *out;                // [slots][N]
+    int E, n_shared, T, shared_base;
+    int N, K;
+};

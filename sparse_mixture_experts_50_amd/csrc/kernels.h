@@ -1,0 +1,65 @@
+// Launch interfaces of the MoE layer kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+// Tokens per router block.
+#define MOE_ROUTER_TOKENS 32
+// Assignments per permute chunk.
+#define MOE_PERMUTE_CHUNK 256
+
+struct RouterParams {
+    const void *x;        // [T][d]
+    const void *wr;       // [E][d]
+    const float *add;     // [E] or null
+    const float *sub;     // [E] or null
+    int32_t *topk_idx;    // [T][k]
+    float *topk_w;        // [T][k]
+    float *p_part;        // [ceil(T/32)][E]
+    int T, d, E, k;
+};
+
+struct PermuteParams {
+    const int32_t *topk_idx;  // [T*k]
+    const float *p_part;      // [n_rtiles][E]
+    int32_t *blk;             // [n_chunks][E] scratch
+    int32_t *counts, *kept, *offsets, *slot_token, *slot_of;
+    float *f, *p, *l_aux;
+    int T, E, k, capacity, n_rtiles, n_chunks;
+    float alpha;
+};
+
+struct CombineParams {
+    const void *yp;           // [slots][d]
+    const int32_t *slot_of;   // [T][k]
+    const float *topk_w;      // [T][k]
+    void *y;                  // [T][d]
+    int T, d, k, n_shared, shared_base;
+};
+
+// GEMM kernel variants.
+enum GemmVariant {
+    GEMM_BF16_256x256 = 0,
+    GEMM_BF16_128x256 = 1,
+    GEMM_BF16_32x256 = 2,
+    GEMM_BF16_64x64 = 3,
+    GEMM_F32_64x64 = 4,
+};
+
+struct GemmVariantInfo {
+    int bm, bn, threads, lds_bytes;
+};
+
+GemmVariantInfo gemm_variant_info(int variant);
+
+hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s);
+hipError_t launch_permute(const PermuteParams &p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
+                       hipStream_t s);
+hipError_t launch_combine(const CombineParams &p, int dtype, hipStream_t s);
+hipError_t launch_bias_update(int E, const int32_t *counts, float target,
+                              float gamma, float *bias, hipStream_t s);

@@ -1,0 +1,351 @@
+// Host side of the C ABI declared in include/moe.h: argument checks,
+// workspace layout, kernel-variant choice and launches.  Every check runs
+// before the first HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+    size_t p_part, blk, h, yp, total;
+    int n_rtiles, n_chunks;
+    size_t rows;
+};
+
+int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+int check_desc(const moe_desc *d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->d < 1 ||
+        d->d_ff < 1 || d->capacity < -1 ||
+        (d->n_shared != 0 && d->n_shared != 1))
+        return MOE_ERR_INVALID_ARG;
+    if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->E > MOE_MAX_E || d->k > 64) return MOE_ERR_UNSUPPORTED;
+    if (d->d % 64 != 0 || d->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    // 32-bit element offsets inside the kernels
+    const double rows = (double)d->T * d->k + (double)d->n_shared * d->T;
+    if (rows * d->d_ff >= 2147483647.0 || rows * d->d >= 2147483647.0 ||
+        (double)d->d * d->d_ff >= 2147483647.0)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+WsLayout layout(const moe_desc *d) {
+    WsLayout L;
+    const size_t es = elem_bytes(d->dtype);
+    L.n_rtiles = (d->T + MOE_ROUTER_TOKENS - 1) / MOE_ROUTER_TOKENS;
+    L.n_chunks = (int)(((size_t)d->T * d->k + MOE_PERMUTE_CHUNK - 1) /
+                       MOE_PERMUTE_CHUNK);
+    L.rows = (size_t)d->T * d->k + (size_t)d->n_shared * d->T;
+    size_t off = 0;
+    L.p_part = off;
+    off += align_up((size_t)L.n_rtiles * d->E * sizeof(float));
+    L.blk = off;
+    off += align_up((size_t)L.n_chunks * d->E * sizeof(int32_t));
+    L.h = off;
+    off += align_up(L.rows * d->d_ff * es);
+    L.yp = off;
+    off += align_up(L.rows * d->d * es);
+    L.total = off > 0 ? off : kAlign;
+    return L;
+}
+
+int check_ws(const moe_desc *d, void *ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < layout(d).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+char *at(void *ws, size_t off) { return (char *)ws + off; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Compute units of the current device (host query, cached per device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                                  dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int pick_variant(const moe_desc *d, int N) {
+    if (d->dtype == MOE_F32) return GEMM_F32_64x64;
+    if (N % 256 != 0) return GEMM_BF16_64x64;
+    const double avg = (double)d->T * d->k / d->E;
+    if (avg <= 48.0) return GEMM_BF16_32x256;
+    if (avg <= 192.0) return GEMM_BF16_128x256;
+    return GEMM_BF16_256x256;
+}
+
+int gemm_grid(const moe_desc *d, int variant, int N) {
+    const GemmVariantInfo vi = gemm_variant_info(variant);
+    const long long mtiles = ((long long)d->T * d->k + vi.bm - 1) / vi.bm +
+                             d->E +
+                             (long long)d->n_shared * ((d->T + vi.bm - 1) / vi.bm);
+    const long long ub = mtiles * (N / vi.bn);
+    int per_cu = 1;
+    if (vi.lds_bytes == 0) per_cu = 4;
+    else if (vi.lds_bytes <= 80 * 1024) per_cu = 2;
+    long long g = (long long)device_cus() * per_cu;
+    if (ub < g) g = ub;
+    g = (g + 7) / 8 * 8;
+    return (int)(g < 8 ? 8 : g);
+}
+
+int check_weights_router(const moe_weights *w) {
+    if (!w || !w->w_router) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_weights_ffn(const moe_desc *d, const moe_weights *w) {
+    if (!w || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+    if (d->n_shared && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_routing_router(const moe_routing *r) {
+    if (!r || !r->topk_idx || !r->topk_w) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_routing_permute(const moe_routing *r) {
+    if (!r || !r->topk_idx || !r->counts || !r->kept || !r->offsets ||
+        !r->slot_token || !r->slot_of || !r->f || !r->p || !r->l_aux)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_routing_ffn(const moe_routing *r) {
+    if (!r || !r->offsets || !r->slot_token) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_routing_combine(const moe_routing *r) {
+    if (!r || !r->slot_of || !r->topk_w) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
+                       const moe_routing *r, bool up, const void *x, void *ws) {
+    const WsLayout L = layout(d);
+    GemmParams p;
+    p.slot_token = r->slot_token;
+    p.offsets = r->offsets;
+    p.E = d->E;
+    p.n_shared = d->n_shared;
+    p.T = d->T;
+    p.shared_base = d->T * d->k;
+    if (up) {
+        p.A = x;
+        p.W = w->w1;
+        p.bias = w->b1;
+        p.Ws = w->ws1;
+        p.bias_s = w->bs1;
+        p.out = at(ws, L.h);
+        p.N = d->d_ff;
+        p.K = d->d;
+    } else {
+        p.A = at(ws, L.h);
+        p.W = w->w2;
+        p.bias = w->b2;
+        p.Ws = w->ws2;
+        p.bias_s = w->bs2;
+        p.out = at(ws, L.yp);
+        p.N = d->d;
+        p.K = d->d_ff;
+    }
+    return p;
+}
+
+int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
+             bool up, const void *x, void *ws, hipStream_t s) {
+    const GemmParams p = gemm_params(d, w, r, up, x, ws);
+    const int variant = pick_variant(d, p.N);
+    const int grid = gemm_grid(d, variant, p.N);
+    return to_status(launch_gemm(p, variant, up, grid, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int32_t T, int32_t E, double cf) {
+    if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+    if (cf < 0.0) return -1;
+    const double c = floor(((double)T / (double)E) * cf);
+    if (c > 2147483647.0) return 2147483647;
+    return (int32_t)c;
+}
+
+size_t moe_workspace_size(const moe_desc *desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    return layout(desc).total;
+}
+
+int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
+                    moe_routing *r, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if (!x) return MOE_ERR_INVALID_ARG;
+    if ((st = check_weights_router(w)) != MOE_OK) return st;
+    if ((st = check_routing_router(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    const WsLayout L = layout(desc);
+    RouterParams p;
+    p.x = x;
+    p.wr = w->w_router;
+    p.add = w->b_router;
+    p.sub = w->expert_bias;
+    p.topk_idx = r->topk_idx;
+    p.topk_w = r->topk_w;
+    p.p_part = (float *)at(ws, L.p_part);
+    p.T = desc->T;
+    p.d = desc->d;
+    p.E = desc->E;
+    p.k = desc->k;
+    return to_status(launch_router(p, desc->dtype, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
+                size_t ws_bytes, void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if ((st = check_routing_permute(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    const WsLayout L = layout(desc);
+    PermuteParams p;
+    p.topk_idx = r->topk_idx;
+    p.p_part = (const float *)at(ws, L.p_part);
+    p.blk = (int32_t *)at(ws, L.blk);
+    p.counts = r->counts;
+    p.kept = r->kept;
+    p.offsets = r->offsets;
+    p.slot_token = r->slot_token;
+    p.slot_of = r->slot_of;
+    p.f = r->f;
+    p.p = r->p;
+    p.l_aux = r->l_aux;
+    p.T = desc->T;
+    p.E = desc->E;
+    p.k = desc->k;
+    p.capacity = desc->capacity;
+    p.n_rtiles = L.n_rtiles;
+    p.n_chunks = L.n_chunks;
+    p.alpha = desc->aux_alpha;
+    return to_status(launch_permute(p, (hipStream_t)stream));
+}
+
+int moe_ffn_up(const moe_desc *desc, const void *x, const moe_weights *w,
+               const moe_routing *r, void *ws, size_t ws_bytes,
+               void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if (!x) return MOE_ERR_INVALID_ARG;
+    if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
+    if ((st = check_routing_ffn(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    return run_gemm(desc, w, r, true, x, ws, (hipStream_t)stream);
+}
+
+int moe_ffn_down(const moe_desc *desc, const moe_weights *w,
+                 const moe_routing *r, void *ws, size_t ws_bytes,
+                 void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
+    if ((st = check_routing_ffn(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    return run_gemm(desc, w, r, false, nullptr, ws, (hipStream_t)stream);
+}
+
+int moe_grouped_ffn(const moe_desc *desc, const void *x, const moe_weights *w,
+                    const moe_routing *r, void *ws, size_t ws_bytes,
+                    void *stream) {
+    int st = moe_ffn_up(desc, x, w, r, ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_ffn_down(desc, w, r, ws, ws_bytes, stream);
+}
+
+int moe_combine(const moe_desc *desc, const moe_routing *r, void *y, void *ws,
+                size_t ws_bytes, void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if (!y) return MOE_ERR_INVALID_ARG;
+    if ((st = check_routing_combine(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    const WsLayout L = layout(desc);
+    CombineParams p;
+    p.yp = at(ws, L.yp);
+    p.slot_of = r->slot_of;
+    p.topk_w = r->topk_w;
+    p.y = y;
+    p.T = desc->T;
+    p.d = desc->d;
+    p.k = desc->k;
+    p.n_shared = desc->n_shared;
+    p.shared_base = desc->T * desc->k;
+    return to_status(launch_combine(p, desc->dtype, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
+                moe_routing *r, void *y, void *ws, size_t ws_bytes,
+                void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if (!x || !y) return MOE_ERR_INVALID_ARG;
+    if ((st = check_weights_router(w)) != MOE_OK) return st;
+    if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
+    if ((st = check_routing_router(r)) != MOE_OK) return st;
+    if ((st = check_routing_permute(r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    if ((st = moe_router_topk(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
+        return st;
+    if ((st = moe_permute(desc, r, ws, ws_bytes, stream)) != MOE_OK) return st;
+    if ((st = moe_grouped_ffn(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
+        return st;
+    return moe_combine(desc, r, y, ws, ws_bytes, stream);
+}
+
+int moe_bias_update(int32_t E, const int32_t *counts, float target,
+                    float gamma, float *expert_bias, void *stream) {
+    if (E < 1 || E > MOE_MAX_E || !counts || !expert_bias)
+        return MOE_ERR_INVALID_ARG;
+    return to_status(launch_bias_update(E, counts, target, gamma, expert_bias,
+                                        (hipStream_t)stream));
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *moe_version(void) { return "moe-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+"""torch-facing wrappers of the C ABI, with the C entry points' names.
+
+Only argument checking and marshalling happens here; each call enqueues the
+HIP kernels on torch's current stream for the tensors' device.  Shapes and
+layouts are those of include/moe.h:
+  x [T][d]; w_router [E][d]; w1 [E][d_ff][d]; w2 [E][d][d_ff];
+  b1 [E][d_ff]; b2 [E][d]; shared expert ws1 [d_ff][d], ws2 [d][d_ff];
+  b_router / expert_bias float32 [E].
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MoeDesc, MoeRouting, MoeWeights, check
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _opt(t, name, shape, dtype, device):
+    if t is not None:
+        _need(t, name, shape, dtype, device)
+
+
+def make_desc(T: int, d: int, E: int, k: int, d_ff: int, dtype: torch.dtype,
+              n_shared: int = 0, capacity: int = -1,
+              aux_alpha: float = 0.01) -> MoeDesc:
+    if dtype not in _DT:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return MoeDesc(T, d, E, k, d_ff, n_shared, _DT[dtype], capacity,
+                   aux_alpha)
+
+
+def moe_capacity(T: int, E: int, capacity_factor: Optional[float]) -> int:
+    """floor(T / E * cf); -1 (no limit) when cf is None."""
+    if capacity_factor is None:
+        return -1
+    c = _lib.lib().moe_capacity(T, E, float(capacity_factor))
+    if c < -1:
+        check("moe_capacity", c)
+    return c
+
+
+def moe_workspace_size(desc: MoeDesc) -> int:
+    n = _lib.lib().moe_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise _lib.MoeError("moe_workspace_size", _lib.MOE_ERR_INVALID_ARG)
+    return n
+
+
+class Weights:
+    """Device weight tensors of one layer (see module docstring)."""
+
+    def __init__(self, w_router, w1, w2, b_router=None, expert_bias=None,
+                 b1=None, b2=None, ws1=None, bs1=None, ws2=None, bs2=None):
+        self.w_router, self.w1, self.w2 = w_router, w1, w2
+        self.b_router, self.expert_bias = b_router, expert_bias
+        self.b1, self.b2 = b1, b2
+        self.ws1, self.bs1, self.ws2, self.bs2 = ws1, bs1, ws2, bs2
+        E, d_ff, d = w1.shape
+        self.E, self.d, self.d_ff = E, d, d_ff
+        self.dtype = w1.dtype
+        self.device = w1.device
+        self.n_shared = 0 if ws1 is None else 1
+        dt, dev = self.dtype, self.device
+        _need(w_router, "w_router", (E, d), dt, dev)
+        _need(w1, "w1", (E, d_ff, d), dt, dev)
+        _need(w2, "w2", (E, d, d_ff), dt, dev)
+        _opt(b_router, "b_router", (E,), torch.float32, dev)
+        _opt(expert_bias, "expert_bias", (E,), torch.float32, dev)
+        _opt(b1, "b1", (E, d_ff), dt, dev)
+        _opt(b2, "b2", (E, d), dt, dev)
+        if self.n_shared:
+            _need(ws1, "ws1", (d_ff, d), dt, dev)
+            _need(ws2, "ws2", (d, d_ff), dt, dev)
+            _opt(bs1, "bs1", (d_ff,), dt, dev)
+            _opt(bs2, "bs2", (d,), dt, dev)
+
+    @staticmethod
+    def from_dict(inp: dict, device=None) -> "Weights":
+        def g(key):
+            t = inp.get(key)
+            if t is None:
+                return None
+            return t.to(device).contiguous() if device is not None else t
+        return Weights(g("wr"), g("w1"), g("w2"), b_router=g("br"),
+                       expert_bias=g("ebias"), b1=g("b1"), b2=g("b2"),
+                       ws1=g("ws1"), bs1=g("bs1"), ws2=g("ws2"),
+                       bs2=g("bs2"))
+
+    def struct(self) -> MoeWeights:
+        return MoeWeights(*[_ptr(t) for t in (
+            self.w_router, self.b_router, self.expert_bias, self.w1, self.b1,
+            self.w2, self.b2, self.ws1, self.bs1, self.ws2, self.bs2)])
+
+
+class Routing:
+    """Device buffers of the routing results and statistics."""
+
+    def __init__(self, T: int, E: int, k: int, device):
+        i32, f32 = torch.int32, torch.float32
+        z = lambda *s, dt: torch.empty(s, dtype=dt, device=device)
+        self.topk_idx = z(T, k, dt=i32)
+        self.topk_w = z(T, k, dt=f32)
+        self.counts = z(E, dt=i32)
+        self.kept = z(E, dt=i32)
+        self.offsets = z(E + 1, dt=i32)
+        self.slot_token = z(T * k, dt=i32)
+        self.slot_of = z(T, k, dt=i32)
+        self.f = z(E, dt=f32)
+        self.p = z(E, dt=f32)
+        self.l_aux = z(1, dt=f32)
+
+    def struct(self) -> MoeRouting:
+        return MoeRouting(*[_ptr(getattr(self, n)) for n, _ in
+                            MoeRouting._fields_])
+
+
+def _ws(desc, ws: torch.Tensor):
+    need = moe_workspace_size(desc)
+    if ws.numel() * ws.element_size() < need or not ws.is_contiguous():
+        raise ValueError(f"workspace needs {need} contiguous bytes")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def moe_router_topk(desc, x, w: Weights, r: Routing, ws) -> None:
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_router_topk", _lib.lib().moe_router_topk(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), p, n, _stream(x)))
+
+
+def moe_permute(desc, r: Routing, ws) -> None:
+    p, n = _ws(desc, ws)
+    rs = r.struct()
+    check("moe_permute", _lib.lib().moe_permute(
+        ctypes.byref(desc), ctypes.byref(rs), p, n, _stream(ws)))
+
+
+def moe_grouped_ffn(desc, x, w: Weights, r: Routing, ws) -> None:
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_grouped_ffn", _lib.lib().moe_grouped_ffn(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), p, n, _stream(x)))
+
+
+def moe_ffn_up(desc, x, w: Weights, r: Routing, ws) -> None:
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_ffn_up", _lib.lib().moe_ffn_up(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), p, n, _stream(x)))
+
+
+def moe_ffn_down(desc, w: Weights, r: Routing, ws) -> None:
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_ffn_down", _lib.lib().moe_ffn_down(
+        ctypes.byref(desc), ctypes.byref(wsct), ctypes.byref(rs), p, n,
+        _stream(ws)))
+
+
+def moe_combine(desc, r: Routing, y, ws) -> None:
+    _need(y, "y", (desc.T, desc.d), y.dtype, ws.device)
+    p, n = _ws(desc, ws)
+    rs = r.struct()
+    check("moe_combine", _lib.lib().moe_combine(
+        ctypes.byref(desc), ctypes.byref(rs), y.data_ptr(), p, n,
+        _stream(y)))
+
+
+def moe_forward(desc, x, w: Weights, r: Routing, y, ws) -> None:
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    _need(y, "y", (desc.T, desc.d), w.dtype, w.device)
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_forward", _lib.lib().moe_forward(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), y.data_ptr(), p, n, _stream(x)))
+
+
+def moe_bias_update(counts, target: float, gamma: float,
+                    expert_bias) -> None:
+    E = expert_bias.numel()
+    if counts.dtype != torch.int32 or counts.numel() != E:
+        raise ValueError("counts must be int32 [E]")
+    if expert_bias.dtype != torch.float32 or not expert_bias.is_contiguous():
+        raise ValueError("expert_bias must be contiguous float32 [E]")
+    check("moe_bias_update", _lib.lib().moe_bias_update(
+        E, counts.data_ptr(), float(target), float(gamma),
+        expert_bias.data_ptr(), _stream(expert_bias)))
+
+
+class MoeLayer:
+    """One sparse MoE FFN layer on a GPU: weights plus reusable buffers.
+
+    ``forward(x)`` returns ``(y, routing)``; the routing buffers are reused
+    by the next call with the same T (copy them to keep them)."""
+
+    def __init__(self, weights: Weights, k: int,
+                 capacity_factor: Optional[float] = None,
+                 aux_alpha: float = 0.01):
+        self.w = weights
+        self.k = k
+        self.capacity_factor = capacity_factor
+        self.aux_alpha = aux_alpha
+        self._bufs = {}
+
+    def desc(self, T: int) -> MoeDesc:
+        w = self.w
+        cap = moe_capacity(T, w.E, self.capacity_factor)
+        return make_desc(T, w.d, w.E, self.k, w.d_ff, w.dtype,
+                         n_shared=w.n_shared, capacity=cap,
+                         aux_alpha=self.aux_alpha)
+
+    def buffers(self, T: int):
+        if T not in self._bufs:
+            desc = self.desc(T)
+            nbytes = moe_workspace_size(desc)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=self.w.device)
+            r = Routing(T, self.w.E, self.k, self.w.device)
+            y = torch.empty((T, self.w.d), dtype=self.w.dtype,
+                            device=self.w.device)
+            self._bufs[T] = (desc, r, ws, y)
+        return self._bufs[T]
+
+    def forward(self, x: torch.Tensor):
+        if x.dim() == 3:                    # (B, S, H) -> (B*S, H)
+            shape = x.shape
+            y, r = self.forward(x.reshape(-1, shape[-1]))
+            return y.reshape(shape), r
+        desc, r, ws, y = self.buffers(x.shape[0])
+        moe_forward(desc, x.contiguous(), self.w, r, y, ws)
+        return y, r
+
+    def bias_update(self, routing: Routing, gamma: float) -> None:
+        """One aux-loss-free step on weights.expert_bias from the counts of
+        the last forward: target is T*k/E."""
+        if self.w.expert_bias is None:
+            raise ValueError("layer has no expert_bias")
+        T = routing.topk_idx.shape[0]
+        moe_bias_update(routing.counts, T * self.k / self.w.E, gamma,
+                        self.w.expert_bias)

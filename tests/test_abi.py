@@ -1,0 +1,175 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every
+entry point that include/moe.h declares, and rejects bad arguments before
+any HIP call (so these run on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_50_amd as moe
+from sparse_mixture_experts_50_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x1000      # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(moe_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_router_topk", "moe_permute", "moe_grouped_ffn",
+                     "moe_combine", "moe_forward"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    L = _lib.lib()
+    assert L.moe_version().startswith(b"moe-gfx950")
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(-3).startswith(b"workspace")
+    assert L.moe_status_string(123) == b"unknown status"
+
+
+def test_capacity_formula():
+    L = _lib.lib()
+    assert L.moe_capacity(8192, 64, 1.25) == 160
+    assert L.moe_capacity(100, 8, 1.25) == 15
+    assert L.moe_capacity(7, 8, 1.0) == 0
+    assert L.moe_capacity(10, 2, -1.0) == -1
+    assert L.moe_capacity(-1, 2, 1.0) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_capacity(10, 0, 1.0) == _lib.MOE_ERR_INVALID_ARG
+
+
+def desc(**kw):
+    base = dict(T=64, d=128, E=8, k=2, d_ff=256, n_shared=0, dtype=1,
+                capacity=-1, aux_alpha=0.01)
+    base.update(kw)
+    return _lib.MoeDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(k=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(k=9), _lib.MOE_ERR_INVALID_ARG),
+    (dict(E=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=2), _lib.MOE_ERR_INVALID_ARG),
+    (dict(capacity=-2), _lib.MOE_ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(d=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(E=300, k=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(E=128, k=65), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_descriptor_rejected_before_any_launch(kw, status):
+    L = _lib.lib()
+    d = desc(**kw)
+    assert L.moe_workspace_size(ctypes.byref(d)) == 0
+    w = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                        None, None, None, None)
+    r = _lib.MoeRouting(*([FAKE] * 10))
+    rc = L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(w),
+                       ctypes.byref(r), FAKE, FAKE, 1 << 40, None)
+    assert rc == status
+
+
+def test_null_pointers_and_workspace():
+    L = _lib.lib()
+    d = desc()
+    ws = L.moe_workspace_size(ctypes.byref(d))
+    assert ws > 0
+    w = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                        None, None, None, None)
+    r = _lib.MoeRouting(*([FAKE] * 10))
+    # missing x / y
+    assert L.moe_forward(ctypes.byref(d), None, ctypes.byref(w),
+                         ctypes.byref(r), FAKE, FAKE, ws, None) == -1
+    assert L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(w),
+                         ctypes.byref(r), None, FAKE, ws, None) == -1
+    # missing weights
+    w2 = _lib.MoeWeights(FAKE, None, None, None, None, FAKE, None,
+                         None, None, None, None)
+    assert L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(w2),
+                         ctypes.byref(r), FAKE, FAKE, ws, None) == -1
+    # shared expert declared but absent
+    ds = desc(n_shared=1)
+    wss = L.moe_workspace_size(ctypes.byref(ds))
+    assert L.moe_forward(ctypes.byref(ds), FAKE, ctypes.byref(w),
+                         ctypes.byref(r), FAKE, FAKE, wss, None) == -1
+    # missing routing buffer
+    r2 = _lib.MoeRouting(*([FAKE] * 9 + [None]))
+    assert L.moe_permute(ctypes.byref(d), ctypes.byref(r2), FAKE, ws,
+                         None) == -1
+    # workspace too small / absent
+    assert L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(w),
+                         ctypes.byref(r), FAKE, FAKE, ws - 1, None) == -3
+    assert L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(w),
+                         ctypes.byref(r), FAKE, None, ws, None) == -3
+    assert L.moe_bias_update(0, FAKE, 1.0, 0.001, FAKE, None) == -1
+    assert L.moe_bias_update(8, None, 1.0, 0.001, FAKE, None) == -1
+
+
+def test_zero_tokens_is_a_no_op():
+    L = _lib.lib()
+    d = desc(T=0)
+    ws = L.moe_workspace_size(ctypes.byref(d))
+    assert ws > 0
+    w = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                        None, None, None, None)
+    r = _lib.MoeRouting(*([FAKE] * 10))
+    for fn, args in [
+        ("moe_forward", (FAKE, ctypes.byref(w), ctypes.byref(r), FAKE, FAKE,
+                         ws, None)),
+        ("moe_router_topk", (FAKE, ctypes.byref(w), ctypes.byref(r), FAKE,
+                             ws, None)),
+        ("moe_permute", (ctypes.byref(r), FAKE, ws, None)),
+        ("moe_grouped_ffn", (FAKE, ctypes.byref(w), ctypes.byref(r), FAKE,
+                             ws, None)),
+        ("moe_combine", (ctypes.byref(r), FAKE, FAKE, ws, None)),
+    ]:
+        assert getattr(L, fn)(ctypes.byref(d), *args) == 0, fn
+
+
+def test_workspace_grows_with_tokens():
+    L = _lib.lib()
+    a = L.moe_workspace_size(ctypes.byref(desc(T=64)))
+    b = L.moe_workspace_size(ctypes.byref(desc(T=4096)))
+    c = L.moe_workspace_size(ctypes.byref(desc(T=4096, n_shared=1)))
+    assert 0 < a < b < c
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "library_path",
+                        lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()
+
+
+def test_binding_checks_tensor_shapes():
+    import torch
+    w1 = torch.zeros(2, 64, 64, dtype=torch.bfloat16)
+    w2 = torch.zeros(2, 64, 64, dtype=torch.bfloat16)
+    wr = torch.zeros(2, 64, dtype=torch.bfloat16)
+    moe.Weights(wr, w1, w2)
+    with pytest.raises(ValueError):
+        moe.Weights(wr, w1, torch.zeros(2, 64, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        moe.Weights(wr.float(), w1, w2)
+    with pytest.raises(ValueError):
+        moe.Weights(wr, w1, w2, b_router=torch.zeros(2,
+                                                     dtype=torch.bfloat16))
