@@ -28,7 +28,9 @@ namespace {
 constexpr int BK = 64;
 
 // Global -> registers: this thread's 16-byte chunks of the A and B tiles
-// at k offset ko (A rows with offset -1 are zero).
+// at k offset ko.  Tile rows past the group's end carry offset 0 (row 0,
+// always valid memory): they only feed output rows that are never stored,
+// so they need no zeroing (and no wait on the load).
 template <int AC, int BC>
 __device__ __forceinline__ void tile_gload(u32x4 (&ra)[AC], u32x4 (&rb)[BC],
                                            const uint16_t *A,
@@ -36,12 +38,7 @@ __device__ __forceinline__ void tile_gload(u32x4 (&ra)[AC], u32x4 (&rb)[BC],
                                            const int (&aoff)[AC],
                                            const int (&boff)[BC], int ko) {
 #pragma unroll
-    for (int i = 0; i < AC; ++i) {
-        // rows past the group's end read row 0 (always valid) and are zeroed
-        u32x4 v = *(const u32x4 *)(A + max(aoff[i], 0) + ko);
-        if (aoff[i] < 0) v = u32x4{0, 0, 0, 0};
-        ra[i] = v;
-    }
+    for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4 *)(A + aoff[i] + ko);
 #pragma unroll
     for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4 *)(Wg + boff[i] + ko);
 }
@@ -62,6 +59,41 @@ __device__ __forceinline__ void tile_sstore(const u32x4 (&ra)[AC],
         const int rr = lrow + i * RPP;
         sB[rr * 8 + (lc ^ ((rr >> 1) & 7))] = rb[i];
     }
+}
+
+// LDS -> registers: the MFMA fragments of sub-step kk (16 k values) of one
+// stage for this wave's TM row tiles (A) and TN column tiles (B).
+template <int BM, int BN, int WM, int WN, int TM, int TN>
+__device__ __forceinline__ void load_frags(bf16x8 (&af)[TM], bf16x8 (&bf)[TN],
+                                           const u32x4 *stage, int wm, int wn,
+                                           int lane, int kk) {
+    const u32x4 *sA = stage;
+    const u32x4 *sB = stage + BM * 8;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int ar = wm * (BM / WM) + i * 32 + (lane & 31);
+        af[i] = as_bf16x8(sA[ar * 8 + (c ^ ((ar >> 1) & 7))]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int br = wn * (BN / WN) + j * 32 + (lane & 31);
+        bf[j] = as_bf16x8(sB[br * 8 + (c ^ ((br >> 1) & 7))]);
+    }
+}
+
+// acc[i][j] += B_j^T A_i for one 16-deep sub-step (weight fragment as the
+// MFMA A operand: each lane ends with 4 consecutive features of one row).
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_block(floatx16 (&acc)[TM][TN],
+                                           const bf16x8 (&af)[TM],
+                                           const bf16x8 (&bf)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i],
+                                                               acc[i][j], 0, 0, 0);
 }
 
 template <int BM, int BN, int WM, int WN, bool UP>
@@ -114,7 +146,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
             const int rr = lrow + i * RPP;
-            aoff[i] = -1;
+            aoff[i] = lc * 8;
             if (rr < nrows) {
                 const int slot = row0 + rr;
                 int src = slot;
@@ -134,42 +166,42 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+        // Software pipeline: global loads of step kt+1 are in flight while
+        // step kt computes; within a step the LDS fragments of sub-step
+        // kk+1 are read while the MFMAs of sub-step kk run, and the first
+        // fragments of the next step are read right after the barrier,
+        // under the last sub-step's MFMAs.
         u32x4 ra[AC], rb[BC];
         tile_gload<AC, BC>(ra, rb, A, Wg, aoff, boff, 0);
         tile_sstore<AC, BC, BM, RPP>(ra, rb, smem, lrow, lc);
         __syncthreads();
+        bf16x8 fa[2][TM], fb[2][TN];
+        load_frags<BM, BN, WM, WN, TM, TN>(fa[0], fb[0], smem, wm, wn, lane, 0);
         for (int kt = 0; kt < KT; ++kt) {
             const int cur = kt & 1;
-            if (kt + 1 < KT)
+            const bool more = kt + 1 < KT;
+            if (more)
                 tile_gload<AC, BC>(ra, rb, A, Wg, aoff, boff, (kt + 1) * BK);
-            const u32x4 *sA = smem + cur * STAGE;
-            const u32x4 *sB = sA + BM * 8;
+            const u32x4 *stage = smem + cur * STAGE;
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int c = kk * 2 + (lane >> 5);
-                bf16x8 af[TM], bfr[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int ar = wm * (BM / WM) + i * 32 + (lane & 31);
-                    af[i] = as_bf16x8(sA[ar * 8 + (c ^ ((ar >> 1) & 7))]);
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int br = wn * (BN / WN) + j * 32 + (lane & 31);
-                    bfr[j] = as_bf16x8(sB[br * 8 + (c ^ ((br >> 1) & 7))]);
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            bfr[j], af[i], acc[i][j], 0, 0, 0);
+            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+                load_frags<BM, BN, WM, WN, TM, TN>(fa[(kk + 1) & 1],
+                                                   fb[(kk + 1) & 1], stage,
+                                                   wm, wn, lane, kk + 1);
+                mfma_block<TM, TN>(acc, fa[kk & 1], fb[kk & 1]);
             }
-            if (kt + 1 < KT)
+            if (more)
                 tile_sstore<AC, BC, BM, RPP>(ra, rb, smem + (cur ^ 1) * STAGE,
                                              lrow, lc);
             __syncthreads();
+            constexpr int LAST = (BK / 16 - 1) & 1;
+            if (more)
+                load_frags<BM, BN, WM, WN, TM, TN>(fa[LAST ^ 1], fb[LAST ^ 1],
+                                                   smem + (cur ^ 1) * STAGE,
+                                                   wm, wn, lane, 0);
+            mfma_block<TM, TN>(acc, fa[LAST], fb[LAST]);
         }
+        __syncthreads();   // LDS is reused by the next tile's prologue
 
         // Epilogue.  Lane holds row m = lane%32 of each 32x32 tile and
         // features 8*q + 4*(lane/32) + 0..3 for q = 0..3.
@@ -206,6 +238,372 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
                     *(u32x2 *)(orow + n) = o;
                 }
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------
+// bf16 kernel with direct global->LDS loads (global_load_lds_dwordx4) into
+// an NS-stage ring of BM x 32 / BN x 32 tiles.  Loads run NS-1 stages ahead
+// of the MFMAs without holding registers, which hides L2-miss latency that
+// a one-step register prefetch cannot.  One wave instruction fills 16 rows
+// (64 bytes each) of a tile; lane i writes row i/4, 16-byte slot i%4, and
+// fetches the k-chunk (i%4) ^ ((row/4) % 4) so that the fragment reads
+// (32 rows at one chunk) are free of bank conflicts.
+constexpr int BKD = 32;
+
+__device__ __forceinline__ void dma16(const uint16_t *src, u32x4 *lds_row16) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src,
+        (__attribute__((address_space(3))) void *)lds_row16, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) |
+                               (0xF << 8));
+}
+
+// LDS -> registers: both 16-deep sub-steps of one BKD = 32 stage.
+template <int BM, int BN, int WM, int WN, int TM, int TN>
+__device__ __forceinline__ void read_stage(bf16x8 (&fa)[2][TM],
+                                           bf16x8 (&fb)[2][TN],
+                                           const u32x4 *stage, int wm, int wn,
+                                           int lane) {
+    const u32x4 *sA = stage;
+    const u32x4 *sB = stage + BM * 4;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int ar = wm * (BM / WM) + i * 32 + (lane & 31);
+            fa[kk][i] = as_bf16x8(sA[ar * 4 + (c ^ ((ar >> 2) & 3))]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int br = wn * (BN / WN) + j * 32 + (lane & 31);
+            fb[kk][j] = as_bf16x8(sB[br * 4 + (c ^ ((br >> 2) & 3))]);
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool UP, int NS>
+__global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / (WM * 32);
+    constexpr int TN = BN / (WN * 32);
+    constexpr int IA = BM / 16 / NW;      // A load instructions per wave
+    constexpr int IB = BN / 16 / NW;      // B load instructions per wave
+    constexpr int PER = IA + IB;          // per wave per stage
+    constexpr int STAGE = (BM + BN) * 4;  // 16-byte units per stage
+    static_assert(IA * NW * 16 == BM && IB * NW * 16 == BN, "tile split");
+    static_assert(NS >= 3 && (NS - 2) * PER < 64, "vmcnt range");
+    extern __shared__ u32x4 smem[];
+    __shared__ TileTable tt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int N = p.N, K = p.K, KT = K / BKD;
+    const int NTN = N / BN;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
+                     NTN);
+    const int total = tt.base[G];
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const uint16_t *A = (const uint16_t *)p.A;
+    const int lr = lane >> 2;                       // row within 16
+    const int lp = lane & 3;                        // 16-byte slot
+
+    for (int r = 0;; ++r) {
+        const int L = r * nb + xcd * per + loc;
+        if (L >= total) break;
+        const int g = find_group(tt, G, L);
+        const int local = L - tt.base[g];
+        const int mt = tt.mt[g];
+        const int n_tile = local / mt, m_tile = local - n_tile * mt;
+        const int row0 = tt.start[g] + m_tile * BM;
+        const int nrows = min(BM, tt.rows[g] - m_tile * BM);
+        const int n0 = n_tile * BN;
+        const bool routed = g < p.E;
+        const uint16_t *Wg = routed
+            ? (const uint16_t *)p.W + (size_t)g * N * K
+            : (const uint16_t *)p.Ws;
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+
+        // per-lane source offsets (elements) of each load instruction;
+        // tile rows past the group's end read row 0 and are never stored
+        int aoff[IA], boff[IB];
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            const int rr = (wave + j * NW) * 16 + lr;
+            const int ch = lp ^ ((rr >> 2) & 3);
+            int src = 0;
+            if (rr < nrows) {
+                const int slot = row0 + rr;
+                src = slot;
+                if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+            }
+            aoff[j] = src * K + ch * 8;
+        }
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int rr = (wave + j * NW) * 16 + lr;
+            const int ch = lp ^ ((rr >> 2) & 3);
+            boff[j] = (n0 + rr) * K + ch * 8;
+        }
+        auto issue = [&](int ks) __attribute__((always_inline)) {
+            u32x4 *st = smem + (ks % NS) * STAGE;
+            const int ko = ks * BKD;
+#pragma unroll
+            for (int j = 0; j < IA; ++j)
+                dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
+#pragma unroll
+            for (int j = 0; j < IB; ++j)
+                dma16(Wg + boff[j] + ko, st + BM * 4 + (wave + j * NW) * 64);
+        };
+
+        floatx16 acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+        // Stage kt's fragments sit in registers while stage kt+1's are
+        // read from LDS, so every wave's LDS reads overlap its own (and its
+        // SIMD neighbour's) MFMAs instead of all waves reading, then all
+        // computing, between barriers.  At iteration kt: wait until this
+        // wave's loads of stage kt+1 have landed, barrier (all waves' loads
+        // landed; all waves finished reading stage kt-1), refill the slot of
+        // stage kt-1 with stage kt+NS-1, read stage kt+1, compute stage kt.
+        wait_vmcnt<0>();   // previous tile's stores and loads are done
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < KT) issue(s);
+        bf16x8 fa[2][2][TM], fb[2][2][TN];   // [buffer][sub-step][tile]
+        if (KT > 1) wait_vmcnt<(NS - 2) * PER>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        read_stage<BM, BN, WM, WN, TM, TN>(fa[0], fb[0], smem, wm, wn, lane);
+        auto step = [&](int kt, bf16x8 (&fa_cur)[2][TM],
+                        bf16x8 (&fb_cur)[2][TN], bf16x8 (&fa_nxt)[2][TM],
+                        bf16x8 (&fb_nxt)[2][TN]) __attribute__((always_inline)) {
+            if (kt + 1 < KT) {
+                if (kt + NS - 2 < KT) wait_vmcnt<(NS - 3) * PER>();
+                else wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
+                if (kt + NS - 1 < KT) issue(kt + NS - 1);
+                read_stage<BM, BN, WM, WN, TM, TN>(
+                    fa_nxt, fb_nxt, smem + ((kt + 1) % NS) * STAGE, wm, wn,
+                    lane);
+            }
+            mfma_block<TM, TN>(acc, fa_cur[0], fb_cur[0]);
+            mfma_block<TM, TN>(acc, fa_cur[1], fb_cur[1]);
+        };
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(kt, fa[0], fb[0], fa[1], fb[1]);
+            if (kt + 1 < KT) step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+        }
+        __syncthreads();   // the ring is reused by the next tile
+
+        uint16_t *out = (uint16_t *)p.out;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+            if (m >= nrows) continue;
+            uint16_t *orow = out + (size_t)(row0 + m) * N;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
+                                  4 * (lane >> 5);
+                    float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                    float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                    if (bg) {
+                        const u32x2 bb = *(const u32x2 *)(bg + n);
+                        v0 += bf16_lo(bb.x);
+                        v1 += bf16_hi(bb.x);
+                        v2 += bf16_lo(bb.y);
+                        v3 += bf16_hi(bb.y);
+                    }
+                    if (UP) {
+                        v0 = gelu_erf(v0);
+                        v1 = gelu_erf(v1);
+                        v2 = gelu_erf(v2);
+                        v3 = gelu_erf(v3);
+                    }
+                    u32x2 o;
+                    o.x = pack_bf16x2(v0, v1);
+                    o.y = pack_bf16x2(v2, v3);
+                    *(u32x2 *)(orow + n) = o;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------
+// Weight-streaming kernel for groups of at most a few dozen rows (decode).
+// Work units are (group, 32-column slab) over the full K; the grid is
+// persistent and walks the units with a stride, so equal-cost units spread
+// evenly over the resident blocks.  A unit loops over 32-row chunks of its
+// group (normally one).  The four waves split K into quarters; each wave
+// streams its weight rows straight into v_mfma_f32_16x16x32_bf16 fragments
+// (no LDS staging: every weight byte feeds exactly one MFMA).  In that
+// layout four lanes read one 64-byte run of a weight row, and the token
+// rows are read as 16-row halves, the second half only when the chunk has
+// more than 16 rows.  Two batches of SU sub-steps are kept in flight, and
+// the four partial accumulators are summed through LDS in a fixed order
+// before the epilogue.
+template <int MT, int SU>
+__device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][2],
+                                             const uint16_t *w0,
+                                             const uint16_t *w1,
+                                             const uint16_t *a0,
+                                             const uint16_t *a1, int kq) {
+    u32x4 av[2][SU][MT], bv[2][SU][2];
+    auto load = [&](int buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SU; ++s) {
+            bv[buf][s][0] = *(const u32x4 *)(w0 + k0 + s * 32);
+            bv[buf][s][1] = *(const u32x4 *)(w1 + k0 + s * 32);
+            av[buf][s][0] = *(const u32x4 *)(a0 + k0 + s * 32);
+            if (MT == 2) av[buf][s][MT - 1] = *(const u32x4 *)(a1 + k0 + s * 32);
+        }
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SU; ++s)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(bv[buf][s][n]), as_bf16x8(av[buf][s][m]),
+                        acc[m][n], 0, 0, 0);
+    };
+    constexpr int STEP = 32 * SU;
+    load(0, 0);
+    for (int k0 = 0; k0 < kq; k0 += 2 * STEP) {
+        if (k0 + STEP < kq) load(1, k0 + STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k0 + STEP < kq) {
+            if (k0 + 2 * STEP < kq) load(0, k0 + 2 * STEP);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <bool UP>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
+    constexpr int NB = 32;         // columns per unit (2 MFMA tiles)
+    constexpr int SU = 4;          // 32-deep sub-steps per load batch
+    __shared__ float part[4][32][NB + 1];
+    __shared__ TileTable tt;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int N = p.N, K = p.K;
+    const int NTN = N / NB;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, 32,
+                     NTN);
+    const uint16_t *A = (const uint16_t *)p.A;
+    const int kq = K / 4;                     // this wave's K range
+    const int kbeg = wave * kq;
+    const int kg = (lane >> 4) * 8;           // k group of this lane
+    const int r16 = lane & 15;
+    uint16_t *out = (uint16_t *)p.out;
+
+    for (int u = blockIdx.x; u < G * NTN; u += gridDim.x) {
+        const int g = u / NTN, n_tile = u - g * NTN;
+        if (tt.rows[g] == 0) continue;
+        const bool routed = g < p.E;
+        const uint16_t *Wg = routed ? (const uint16_t *)p.W + (size_t)g * N * K
+                                    : (const uint16_t *)p.Ws;
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const int n0 = n_tile * NB;
+        const uint16_t *w0 = Wg + (size_t)(n0 + r16) * K + kbeg + kg;
+        const uint16_t *w1 = w0 + (size_t)16 * K;
+
+        for (int mc = 0; mc < tt.mt[g]; ++mc) {
+            const int row0 = tt.start[g] + mc * 32;
+            const int nrows = min(32, tt.rows[g] - mc * 32);
+            int src[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = h * 16 + r16;
+                src[h] = 0;
+                if (rr < nrows) {
+                    const int slot = row0 + rr;
+                    src[h] = slot;
+                    if (UP)
+                        src[h] = routed ? p.slot_token[slot]
+                                        : slot - p.shared_base;
+                }
+            }
+            const uint16_t *a0 = A + (size_t)src[0] * K + kbeg + kg;
+            const uint16_t *a1 = A + (size_t)src[1] * K + kbeg + kg;
+            floatx4 acc[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[m][n][v] = 0.0f;
+            if (nrows > 16)
+                stream_chunk<2, SU>(acc, w0, w1, a0, a1, kq);
+            else
+                stream_chunk<1, SU>(acc, w0, w1, a0, a1, kq);
+            // lane holds row m = 16*mt + lane%16, features
+            // 16*nt + 4*(lane/16) + 0..3
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        part[wave][16 * m + r16][16 * n + 4 * (lane >> 4) + v] =
+                            acc[m][n][v];
+            __syncthreads();
+            for (int e = tid; e < 32 * NB / 2; e += 256) {
+                const int m = e / (NB / 2);
+                const int c = (e - m * (NB / 2)) * 2;
+                if (m < nrows) {
+                    float v0 = part[0][m][c] + part[1][m][c];
+                    v0 += part[2][m][c];
+                    v0 += part[3][m][c];
+                    float v1 = part[0][m][c + 1] + part[1][m][c + 1];
+                    v1 += part[2][m][c + 1];
+                    v1 += part[3][m][c + 1];
+                    if (bg) {
+                        v0 += bf16_to_f32(bg[n0 + c]);
+                        v1 += bf16_to_f32(bg[n0 + c + 1]);
+                    }
+                    if (UP) {
+                        v0 = gelu_erf(v0);
+                        v1 = gelu_erf(v1);
+                    }
+                    *(uint32_t *)(out + (size_t)(row0 + m) * N + n0 + c) =
+                        pack_bf16x2(v0, v1);
+                }
+            }
+            __syncthreads();
         }
     }
 }
@@ -300,6 +698,18 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
     }
 }
 
+template <int BM, int BN, int WM, int WN, bool UP, int NS>
+hipError_t launch_dma(const GemmParams &p, int grid, hipStream_t s) {
+    const int lds = NS * (BM + BN) * 64;
+    auto kern = gemm_bf16_dma<BM, BN, WM, WN, UP, NS>;
+    hipError_t err = hipFuncSetAttribute((const void *)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WM * WN * 64), lds, s, p);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, bool UP>
 hipError_t launch_lds(const GemmParams &p, int grid, hipStream_t s) {
     const int lds = 2 * (BM + BN) * 8 * 16;
@@ -320,6 +730,9 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_128x256: return {128, 256, 256, 2 * 384 * 128};
     case GEMM_BF16_32x256: return {32, 256, 256, 2 * 288 * 128};
     case GEMM_BF16_64x64: return {64, 64, 256, 2 * 128 * 128};
+    case GEMM_BF16_DMA_256x256: return {256, 256, 512, 4 * 512 * 64};
+    case GEMM_BF16_DMA_128x256: return {128, 256, 256, 4 * 384 * 64};
+    case GEMM_BF16_STREAM_32x64: return {32, 32, 256, 0};
     default: return {64, 64, 256, 0};
     }
 }
@@ -339,6 +752,20 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_64x64:
         return up ? launch_lds<64, 64, 2, 2, true>(p, grid, s)
                   : launch_lds<64, 64, 2, 2, false>(p, grid, s);
+    case GEMM_BF16_DMA_256x256:
+        return up ? launch_dma<256, 256, 2, 4, true, 4>(p, grid, s)
+                  : launch_dma<256, 256, 2, 4, false, 4>(p, grid, s);
+    case GEMM_BF16_DMA_128x256:
+        return up ? launch_dma<128, 256, 2, 2, true, 4>(p, grid, s)
+                  : launch_dma<128, 256, 2, 2, false, 4>(p, grid, s);
+    case GEMM_BF16_STREAM_32x64:
+        if (up)
+            hipLaunchKernelGGL(gemm_bf16_stream<true>, dim3(grid), dim3(256), 0,
+                               s, p);
+        else
+            hipLaunchKernelGGL(gemm_bf16_stream<false>, dim3(grid), dim3(256),
+                               0, s, p);
+        return hipGetLastError();
     default:
         if (up)
             hipLaunchKernelGGL(gemm_f32_simt<true>, dim3(grid), dim3(256), 0, s, p);

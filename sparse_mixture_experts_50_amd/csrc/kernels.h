@@ -48,6 +48,9 @@ enum GemmVariant {
     GEMM_BF16_32x256 = 2,
     GEMM_BF16_64x64 = 3,
     GEMM_F32_64x64 = 4,
+    GEMM_BF16_DMA_256x256 = 5,
+    GEMM_BF16_DMA_128x256 = 6,
+    GEMM_BF16_STREAM_32x64 = 7,
 };
 
 struct GemmVariantInfo {

@@ -2,6 +2,7 @@
 // workspace layout, kernel-variant choice and launches.  Every check runs
 // before the first HIP call, so a rejected call enqueues nothing.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -83,10 +84,30 @@ int device_cus() {
     return cached[dev];
 }
 
+// Tuning override: MOE_GEMM_VARIANT_UP / MOE_GEMM_VARIANT_DOWN name a
+// GemmVariant; it is used only if valid for this dtype and width.
+int variant_override(bool up, const moe_desc *d, int N) {
+    const char *v = getenv(up ? "MOE_GEMM_VARIANT_UP" : "MOE_GEMM_VARIANT_DOWN");
+    if (!v || !*v) return -1;
+    const int id = atoi(v);
+    if (d->dtype == MOE_F32) return -1;
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_STREAM_32x64 ||
+        id == GEMM_F32_64x64)
+        return -1;
+    if (N % gemm_variant_info(id).bn != 0) return -1;
+    if (id == GEMM_BF16_STREAM_32x64 && (d->d % 512 != 0 || d->d_ff % 512 != 0))
+        return -1;
+    return id;
+}
+
 int pick_variant(const moe_desc *d, int N) {
     if (d->dtype == MOE_F32) return GEMM_F32_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
     const double avg = (double)d->T * d->k / d->E;
+    // the streaming kernel splits K in four quarters of whole 128-deep
+    // load batches
+    if (avg <= 32.0 && d->d % 512 == 0 && d->d_ff % 512 == 0)
+        return GEMM_BF16_STREAM_32x64;
     if (avg <= 48.0) return GEMM_BF16_32x256;
     if (avg <= 192.0) return GEMM_BF16_128x256;
     return GEMM_BF16_256x256;
@@ -94,6 +115,11 @@ int pick_variant(const moe_desc *d, int N) {
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
     const GemmVariantInfo vi = gemm_variant_info(variant);
+    if (variant == GEMM_BF16_STREAM_32x64) {    // persistent over units
+        const long long units = (long long)(d->E + d->n_shared) * (N / vi.bn);
+        const long long slots = (long long)device_cus() * 2;
+        return (int)(units < slots ? units : slots);
+    }
     const long long mtiles = ((long long)d->T * d->k + vi.bm - 1) / vi.bm +
                              d->E +
                              (long long)d->n_shared * ((d->T + vi.bm - 1) / vi.bm);
@@ -175,7 +201,8 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
 int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
              bool up, const void *x, void *ws, hipStream_t s) {
     const GemmParams p = gemm_params(d, w, r, up, x, ws);
-    const int variant = pick_variant(d, p.N);
+    int variant = variant_override(up, d, p.N);
+    if (variant < 0) variant = pick_variant(d, p.N);
     const int grid = gemm_grid(d, variant, p.N);
     return to_status(launch_gemm(p, variant, up, grid, s));
 }

@@ -46,7 +46,19 @@ __global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
     const int e = threadIdx.x;
     int cnt = 0, kept = 0;
     if (e < p.E) {
-        for (int b = 0; b < p.n_chunks; ++b) {
+        // batches of 8 independent loads keep the serial scans short
+        int b = 0;
+        for (; b + 8 <= p.n_chunks; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                p.blk[(size_t)(b + u) * p.E + e] = cnt;  // rank base
+                cnt += v[u];
+            }
+        }
+        for (; b < p.n_chunks; ++b) {
             const size_t i = (size_t)b * p.E + e;
             const int v = p.blk[i];
             p.blk[i] = cnt;           // rank base of expert e in chunk b
@@ -56,7 +68,15 @@ __global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
         p.counts[e] = cnt;
         p.kept[e] = kept;
         float ps = 0.0f;
-        for (int b = 0; b < p.n_rtiles; ++b) ps += p.p_part[(size_t)b * p.E + e];
+        b = 0;
+        for (; b + 8 <= p.n_rtiles; b += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p.p_part[(size_t)(b + u) * p.E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ps += v[u];
+        }
+        for (; b < p.n_rtiles; ++b) ps += p.p_part[(size_t)b * p.E + e];
         const float pe = ps / (float)p.T;
         const float fe = (float)cnt / ((float)p.T * (float)p.k);
         p.p[e] = pe;

@@ -5,9 +5,9 @@
 // sum 1; sec. 2.4: routing uses logits - b_i.  "AI-Research-SKILLs MoE
 // training guide", sec. 3.1: the router is an nn.Linear (additive bias).
 //
-// One block routes 32 tokens.  bf16 logits come from MFMA
+// One block (16 waves) routes 32 tokens.  bf16 logits come from MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate); fp32 logits from plain FMA.
-// The logits never leave the chip: each wave then takes 8 tokens and does
+// The logits never leave the chip: each wave then takes 2 tokens and does
 // max, exp-sum, selection and renormalisation across its 64 lanes.  The
 // selection compares fp32 logits (softmax is monotonic), ties to the lower
 // expert index.  Each block also writes its column sums of the softmax
@@ -17,12 +17,14 @@
 namespace {
 
 constexpr int RT = MOE_ROUTER_TOKENS;
+constexpr int RW = 16;            // waves per router block
 
 // Softmax + top-k phase over logits staged in LDS (KS partial planes).
 template <int EP, int KS>
 __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
                                              const RouterParams &p,
                                              float (*pp)[EP]) {
+    static_assert(RT % RW == 0, "tokens per wave");
     constexpr int PER = EP >= 64 ? EP / 64 : 1;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -38,8 +40,8 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
         addv[i] = (valid[i] && p.add) ? p.add[e] : 0.0f;
         subv[i] = (valid[i] && p.sub) ? p.sub[e] : 0.0f;
     }
-    for (int q = 0; q < RT / 4; ++q) {
-        const int tl = wave * (RT / 4) + q;
+    for (int q = 0; q < RT / RW; ++q) {
+        const int tl = wave * (RT / RW) + q;
         const int t = t0 + tl;
         if (t >= p.T) break;
         float v[PER];
@@ -119,26 +121,27 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
     __syncthreads();
     for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
         float s = pp[0][e];
-        s += pp[1][e];
-        s += pp[2][e];
-        s += pp[3][e];
+#pragma unroll
+        for (int w = 1; w < RW; ++w) s += pp[w][e];
         p.p_part[(size_t)blockIdx.x * p.E + e] = s;
     }
 }
 
-// bf16 logits with MFMA.  EP = E rounded up to 32/64/128/256.
+// bf16 logits with MFMA.  EP = E rounded up to 32/64/128/256.  The 16
+// waves split the 32-expert tiles and, beyond that, the depth d, so even a
+// single block (a 32-token decode step) keeps 16 waves of loads in flight.
 template <int EP>
-__global__ __launch_bounds__(256) void router_bf16(RouterParams p) {
+__global__ __launch_bounds__(RW * 64) void router_bf16(RouterParams p) {
     constexpr int NTE = EP / 32;                  // 32-expert tiles
-    constexpr int KS = NTE >= 4 ? 1 : 4 / NTE;    // k-splits across waves
-    constexpr int TPW = NTE >= 4 ? NTE / 4 : 1;   // tiles per wave
+    constexpr int KS = NTE >= RW ? 1 : RW / NTE;  // k-splits across waves
+    constexpr int TPW = NTE >= RW ? NTE / RW : 1; // tiles per wave
     __shared__ float lg[KS][RT][EP];
-    __shared__ float pp[4][EP];
+    __shared__ float pp[RW][EP];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * RT;
-    const int ks = NTE >= 4 ? 0 : wave / NTE;
+    const int ks = NTE >= RW ? 0 : wave / NTE;
     const int tok = t0 + (lane & 31);
     const bool tok_ok = tok < p.T;
     const int kg = (lane >> 5) * 8;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256) void router_bf16(RouterParams p) {
     int tile[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-        tile[i] = NTE >= 4 ? wave + 4 * i : wave % NTE;
+        tile[i] = NTE >= RW ? wave + RW * i : wave % NTE;
         const int e = tile[i] * 32 + (lane & 31);
         w_ok[i] = e < p.E;
         wrow[i] = (const uint16_t *)p.wr + (size_t)(w_ok[i] ? e : 0) * p.d +
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256) void router_bf16(RouterParams p) {
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
     const u32x4 zero = {0, 0, 0, 0};
-#pragma unroll 4
+#pragma unroll 8
     for (int k0 = ks * 16; k0 < p.d; k0 += 16 * KS) {
         const u32x4 av = tok_ok ? *(const u32x4 *)(xrow + k0) : zero;
 #pragma unroll
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(256) void router_bf16(RouterParams p) {
 
 // fp32 logits with plain FMA (sequential over d).
 template <int EP>
-__global__ __launch_bounds__(256) void router_f32(RouterParams p) {
+__global__ __launch_bounds__(RW * 64) void router_f32(RouterParams p) {
     __shared__ float lg[1][RT][EP];
-    __shared__ float pp[4][EP];
+    __shared__ float pp[RW][EP];
     const int t0 = blockIdx.x * RT;
     const float *x = (const float *)p.x;
     const float *wr = (const float *)p.wr;
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(256) void router_f32(RouterParams p) {
 
 hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
     const int blocks = (p.T + RT - 1) / RT;
-    const dim3 grid(blocks), block(256);
+    const dim3 grid(blocks), block(RW * 64);
     const int EP = p.E <= 32 ? 32 : p.E <= 64 ? 64 : p.E <= 128 ? 128 : 256;
     if (dtype == 1) {
         switch (EP) {

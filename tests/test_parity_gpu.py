@@ -52,6 +52,9 @@ SMALL = {
     # ragged T, k = 3
     "ragged": scaled(W["mixtral_prefill"], T=77, d=256, E=8, k=3,
                      d_ff=512),
+    # decode shape with a shared expert (48-row shared group)
+    "stream_shared": scaled(W["deepseek_v3"], T=48, d=512, E=16, k=4,
+                            d_ff=512),
 }
 
 
@@ -63,6 +66,19 @@ def test_small_full_parity(name):
     gpu = gpu_forward(w, inp)
     rep = check_layer(w, inp, gpu)
     say(f"[parity small] {name}: {rep}")
+
+
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7"])
+def test_every_gemm_variant(variant, monkeypatch):
+    """Each bf16 tile variant forced on a shape with groups of 0 to ~100
+    rows (several row chunks for the small-tile kernels)."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", variant)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", variant)
+    w = scaled(W["deepseek_v3"], T=150, d=512, E=6, k=2, d_ff=1024)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    rep = check_layer(w, inp, gpu)
+    say(f"[variant {variant}] {rep}")
 
 
 def test_step_entry_points_match_forward():
