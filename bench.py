@@ -11,6 +11,7 @@ on the stream it runs on, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,9 +35,43 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (a kernel of "
+                         "known traffic for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_50_amd", "csrc",
+                           "gemm.hip")
+
+
+def source_digest() -> str:
+    with open(GEMM_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the up-projection GEMM from the committed
+    counter summary of this workload, or None if there is none or the GEMM
+    source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles",
+                        f"gemm_up_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("gemm_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic(wl, counts, kept):
@@ -78,7 +113,7 @@ def cpu_baseline(wl, inp, budget_s):
 
     n = min(wl.T, max(1, cores))
     dt = run(n)
-    while dt < budget_s / 4 and n < wl.T:
+    while dt < budget_s / 2 and n < wl.T:
         n = min(wl.T, max(n + 1, int(n * min(8.0, budget_s / max(dt, 1e-3)
                                               / 2))))
         dt = run(n)
@@ -106,6 +141,22 @@ def main():
     warmup = args.warmup
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    # measured HBM copy bandwidth (1 GiB read + 1 GiB write), beside the
+    # nominal peak; with --copy-calibration this is also the known-size
+    # kernel the byte counters are scaled by
+    ca = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    cb = torch.empty_like(ca)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    copies = 1 if args.copy_calibration else 5
+    e0.record()
+    for _ in range(copies):
+        cb.copy_(ca)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) * copies / (e0.elapsed_time(e1) * 1e6)
+    del ca, cb
     log(f"[bench] {wl.name}: generating inputs on {dev}")
     inp = workloads.make_inputs(wl, dev)
     n_x = wl.calls
@@ -168,7 +219,7 @@ def main():
         roof = dict(bound="mfma", achieved=alg["up_flops"] /
                     (up_avg_ms * 1e9), peak=peak, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(wl.name)
     roof["kernel"] = "grouped GEMM up (moe_ffn_up)"
     roof["kernel_ms"] = up_avg_ms
 
@@ -197,6 +248,7 @@ def main():
         "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
         "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),
         "wall_s": wall,
+        "measured_hbm_copy_gbs": copy_gbs,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

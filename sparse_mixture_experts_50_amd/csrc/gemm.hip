@@ -453,6 +453,159 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------
+// bf16 kernel with direct global->LDS loads and 64-deep stages: every row
+// of a stage is one whole 128-byte line, so each L1->L2 request moves a
+// full line (32-deep stages move half lines and double the L2 request
+// rate, which is what saturates the L2 first).  Two stages: the loads of
+// stage kt+1 are issued at the start of step kt and land during its
+// MFMAs.  One wave instruction fills 8 rows; lane i writes row i/8, slot
+// i%8 and fetches k-chunk (i%8) ^ ((row/2) % 8), the swizzle that keeps
+// the fragment reads conflict-free.
+template <int BM, int BN, int WM, int WN, bool UP>
+__global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / (WM * 32);
+    constexpr int TN = BN / (WN * 32);
+    constexpr int IA = BM / 8 / NW;       // A load instructions per wave
+    constexpr int IB = BN / 8 / NW;       // B load instructions per wave
+    constexpr int STAGE = (BM + BN) * 8;  // 16-byte units per stage
+    static_assert(IA * NW * 8 == BM && IB * NW * 8 == BN, "tile split");
+    extern __shared__ u32x4 smem[];
+    __shared__ TileTable tt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int N = p.N, K = p.K, KT = K / BK;
+    const int NTN = N / BN;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
+                     NTN);
+    const int total = tt.base[G];
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const uint16_t *A = (const uint16_t *)p.A;
+    const int lr = lane >> 3;                       // row within 8
+    const int lp = lane & 7;                        // 16-byte slot
+
+    for (int r = 0;; ++r) {
+        const int L = r * nb + xcd * per + loc;
+        if (L >= total) break;
+        const int g = find_group(tt, G, L);
+        const int local = L - tt.base[g];
+        const int mt = tt.mt[g];
+        const int n_tile = local / mt, m_tile = local - n_tile * mt;
+        const int row0 = tt.start[g] + m_tile * BM;
+        const int nrows = min(BM, tt.rows[g] - m_tile * BM);
+        const int n0 = n_tile * BN;
+        const bool routed = g < p.E;
+        const uint16_t *Wg = routed
+            ? (const uint16_t *)p.W + (size_t)g * N * K
+            : (const uint16_t *)p.Ws;
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+
+        int aoff[IA], boff[IB];
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            const int rr = (wave + j * NW) * 8 + lr;
+            const int ch = lp ^ ((rr >> 1) & 7);
+            int src = 0;
+            if (rr < nrows) {
+                const int slot = row0 + rr;
+                src = slot;
+                if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+            }
+            aoff[j] = src * K + ch * 8;
+        }
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int rr = (wave + j * NW) * 8 + lr;
+            const int ch = lp ^ ((rr >> 1) & 7);
+            boff[j] = (n0 + rr) * K + ch * 8;
+        }
+        auto issue = [&](int ks) __attribute__((always_inline)) {
+            u32x4 *st = smem + (ks & 1) * STAGE;
+            const int ko = ks * BK;
+#pragma unroll
+            for (int j = 0; j < IA; ++j)
+                dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
+#pragma unroll
+            for (int j = 0; j < IB; ++j)
+                dma16(Wg + boff[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+        };
+
+        floatx16 acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+        wait_vmcnt<0>();   // previous tile's stores are done
+        issue(0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        bf16x8 fa[2][TM], fb[2][TN];
+        for (int kt = 0; kt < KT; ++kt) {
+            // the other slot was last read in step kt-1, before its barrier
+            if (kt + 1 < KT) issue(kt + 1);
+            const u32x4 *stage = smem + (kt & 1) * STAGE;
+            load_frags<BM, BN, WM, WN, TM, TN>(fa[0], fb[0], stage, wm, wn,
+                                               lane, 0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                if (kk + 1 < BK / 16)
+                    load_frags<BM, BN, WM, WN, TM, TN>(
+                        fa[(kk + 1) & 1], fb[(kk + 1) & 1], stage, wm, wn, lane,
+                        kk + 1);
+                mfma_block<TM, TN>(acc, fa[kk & 1], fb[kk & 1]);
+            }
+            wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+        }
+
+        uint16_t *out = (uint16_t *)p.out;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+            if (m >= nrows) continue;
+            uint16_t *orow = out + (size_t)(row0 + m) * N;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
+                                  4 * (lane >> 5);
+                    float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                    float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                    if (bg) {
+                        const u32x2 bb = *(const u32x2 *)(bg + n);
+                        v0 += bf16_lo(bb.x);
+                        v1 += bf16_hi(bb.x);
+                        v2 += bf16_lo(bb.y);
+                        v3 += bf16_hi(bb.y);
+                    }
+                    if (UP) {
+                        v0 = gelu_erf(v0);
+                        v1 = gelu_erf(v1);
+                        v2 = gelu_erf(v2);
+                        v3 = gelu_erf(v3);
+                    }
+                    u32x2 o;
+                    o.x = pack_bf16x2(v0, v1);
+                    o.y = pack_bf16x2(v2, v3);
+                    *(u32x2 *)(orow + n) = o;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------
 // Weight-streaming kernel for groups of at most a few dozen rows (decode).
 // Work units are (group, 32-column slab) over the full K; the grid is
 // persistent and walks the units with a stride, so equal-cost units spread
@@ -711,6 +864,18 @@ hipError_t launch_dma(const GemmParams &p, int grid, hipStream_t s) {
 }
 
 template <int BM, int BN, int WM, int WN, bool UP>
+hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
+    const int lds = 2 * (BM + BN) * 128;
+    auto kern = gemm_bf16_dma64<BM, BN, WM, WN, UP>;
+    hipError_t err = hipFuncSetAttribute((const void *)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WM * WN * 64), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, bool UP>
 hipError_t launch_lds(const GemmParams &p, int grid, hipStream_t s) {
     const int lds = 2 * (BM + BN) * 8 * 16;
     auto kern = gemm_bf16_lds<BM, BN, WM, WN, UP>;
@@ -733,6 +898,8 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA_256x256: return {256, 256, 512, 4 * 512 * 64};
     case GEMM_BF16_DMA_128x256: return {128, 256, 256, 4 * 384 * 64};
     case GEMM_BF16_STREAM_32x64: return {32, 32, 256, 0};
+    case GEMM_BF16_DMA64_256x256: return {256, 256, 512, 2 * 512 * 128};
+    case GEMM_BF16_DMA64_128x256: return {128, 256, 256, 2 * 384 * 128};
     default: return {64, 64, 256, 0};
     }
 }
@@ -758,6 +925,12 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_DMA_128x256:
         return up ? launch_dma<128, 256, 2, 2, true, 4>(p, grid, s)
                   : launch_dma<128, 256, 2, 2, false, 4>(p, grid, s);
+    case GEMM_BF16_DMA64_256x256:
+        return up ? launch_dma64<256, 256, 2, 4, true>(p, grid, s)
+                  : launch_dma64<256, 256, 2, 4, false>(p, grid, s);
+    case GEMM_BF16_DMA64_128x256:
+        return up ? launch_dma64<128, 256, 2, 2, true>(p, grid, s)
+                  : launch_dma64<128, 256, 2, 2, false>(p, grid, s);
     case GEMM_BF16_STREAM_32x64:
         if (up)
             hipLaunchKernelGGL(gemm_bf16_stream<true>, dim3(grid), dim3(256), 0,

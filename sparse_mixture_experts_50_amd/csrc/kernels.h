@@ -51,6 +51,8 @@ enum GemmVariant {
     GEMM_BF16_DMA_256x256 = 5,
     GEMM_BF16_DMA_128x256 = 6,
     GEMM_BF16_STREAM_32x64 = 7,
+    GEMM_BF16_DMA64_256x256 = 8,
+    GEMM_BF16_DMA64_128x256 = 9,
 };
 
 struct GemmVariantInfo {

@@ -91,7 +91,7 @@ int variant_override(bool up, const moe_desc *d, int N) {
     if (!v || !*v) return -1;
     const int id = atoi(v);
     if (d->dtype == MOE_F32) return -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_STREAM_32x64 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_DMA64_128x256 ||
         id == GEMM_F32_64x64)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
@@ -109,8 +109,8 @@ int pick_variant(const moe_desc *d, int N) {
     if (avg <= 32.0 && d->d % 512 == 0 && d->d_ff % 512 == 0)
         return GEMM_BF16_STREAM_32x64;
     if (avg <= 48.0) return GEMM_BF16_32x256;
-    if (avg <= 192.0) return GEMM_BF16_128x256;
-    return GEMM_BF16_256x256;
+    if (avg <= 192.0) return GEMM_BF16_DMA64_128x256;
+    return GEMM_BF16_DMA64_256x256;
 }
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
