@@ -266,6 +266,7 @@ __device__ __forceinline__ void wait_vmcnt() {
                                (0xF << 8));
 }
 
+
 // LDS -> registers: both 16-deep sub-steps of one BKD = 32 stage.
 template <int BM, int BN, int WM, int WN, int TM, int TN>
 __device__ __forceinline__ void read_stage(bf16x8 (&fa)[2][TM],

@@ -7,7 +7,8 @@
 // most floor(T/E * cf) tokens, the overflow skips the experts; sec. 2.4:
 // the per-expert bias moves up for an overloaded expert.
 //
-// Three launches, no float atomics, deterministic:
+// Three launches (one when T*k fits a single chunk), no float atomics,
+// deterministic:
 //   hist    one block per 256-assignment chunk: LDS-atomic histogram
 //   scan    one block: per-expert exclusive scan over chunks (rank bases),
 //           counts, kept = min(count, C), offsets, f, p, L_aux
@@ -148,6 +149,99 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
         if (s >= total) p.slot_token[s] = -1;
 }
 
+// All three steps in one block when every assignment fits one chunk
+// (T*k <= 256, e.g. a decode step): same arithmetic, one launch.
+__global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
+    __shared__ int h[MOE_MAX_E];
+    __shared__ int off_s[MOE_MAX_E + 1];
+    __shared__ float fp_s[MOE_MAX_E];
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = p.T * p.k;
+    for (int e = tid; e < p.E; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    for (int a = tid; a < n; a += blockDim.x) {
+        const int e = p.topk_idx[a];
+        if ((unsigned)e < (unsigned)p.E) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    // counts, capacity, statistics, offsets (thread e = expert e)
+    const int e = tid;
+    int cnt = 0, kept = 0;
+    if (e < p.E) {
+        cnt = h[e];
+        kept = (p.capacity >= 0 && cnt > p.capacity) ? p.capacity : cnt;
+        p.counts[e] = cnt;
+        p.kept[e] = kept;
+        float ps = 0.0f;
+        for (int b = 0; b < p.n_rtiles; ++b) ps += p.p_part[(size_t)b * p.E + e];
+        const float pe = ps / (float)p.T;
+        const float fe = (float)cnt / ((float)p.T * (float)p.k);
+        p.p[e] = pe;
+        p.f[e] = fe;
+        fp_s[e] = fe * pe;
+    }
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (e < p.E) {
+        off_s[e] = before + incl - kept;
+        p.offsets[e] = before + incl - kept;
+        h[e] = 0;                       // becomes the running rank
+    }
+    if (e == p.E - 1) {
+        off_s[p.E] = before + incl;
+        p.offsets[p.E] = before + incl;
+    }
+    if (tid == 0) {
+        float s = 0.0f;
+        for (int i = 0; i < p.E; ++i) s += fp_s[i];
+        p.l_aux[0] = p.alpha * (float)p.E * s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        for (int base = 0; base < n; base += 64) {
+            const int a = base + lane;
+            int ex = a < n ? p.topk_idx[a] : -1;
+            if ((unsigned)ex >= (unsigned)p.E) ex = -1;
+            const bool ok = ex >= 0;
+            int rank = 0;
+            unsigned long long pending = __ballot(ok);
+            while (pending) {
+                const int leader = __ffsll((long long)pending) - 1;
+                const int le = __shfl(ex, leader, 64);
+                const unsigned long long same = __ballot(ex == le);
+                const int r0 = h[le];
+                if (ex == le) rank = r0 + __popcll(same & lt);
+                __builtin_amdgcn_wave_barrier();
+                if (lane == leader) h[le] = r0 + __popcll(same);
+                __builtin_amdgcn_wave_barrier();
+                pending &= ~same;
+            }
+            if (a < n) {
+                int slot = -1;
+                if (ok && (p.capacity < 0 || rank < p.capacity)) {
+                    slot = off_s[ex] + rank;
+                    p.slot_token[slot] = a / p.k;
+                }
+                p.slot_of[a] = slot;
+            }
+        }
+    }
+    __syncthreads();
+    for (int sl = tid; sl < n; sl += blockDim.x)
+        if (sl >= off_s[p.E]) p.slot_token[sl] = -1;
+}
+
 __global__ void bias_update_kernel(int E, const int32_t *counts, float target,
                                    float gamma, float *bias) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -161,6 +255,10 @@ __global__ void bias_update_kernel(int E, const int32_t *counts, float target,
 }  // namespace
 
 hipError_t launch_permute(const PermuteParams &p, hipStream_t s) {
+    if (p.n_chunks == 1) {
+        hipLaunchKernelGGL(permute_small, dim3(1), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(permute_hist, dim3(p.n_chunks), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -142,21 +142,16 @@ __global__ __launch_bounds__(RW * 64) void router_bf16(RouterParams p) {
     const int wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * RT;
     const int ks = NTE >= RW ? 0 : wave / NTE;
-    const int tok = t0 + (lane & 31);
-    const bool tok_ok = tok < p.T;
+    const int tok = min(t0 + (lane & 31), p.T - 1);
     const int kg = (lane >> 5) * 8;
-    const uint16_t *xrow =
-        (const uint16_t *)p.x + (size_t)(tok_ok ? tok : 0) * p.d + kg;
+    const uint16_t *xrow = (const uint16_t *)p.x + (size_t)tok * p.d + kg;
     const uint16_t *wrow[TPW];
-    bool w_ok[TPW];
     int tile[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         tile[i] = NTE >= RW ? wave + RW * i : wave % NTE;
-        const int e = tile[i] * 32 + (lane & 31);
-        w_ok[i] = e < p.E;
-        wrow[i] = (const uint16_t *)p.wr + (size_t)(w_ok[i] ? e : 0) * p.d +
-                  kg;
+        const int e = min(tile[i] * 32 + (lane & 31), p.E - 1);
+        wrow[i] = (const uint16_t *)p.wr + (size_t)e * p.d + kg;
     }
     floatx16 acc[TPW];
 #pragma unroll
@@ -164,13 +159,15 @@ __global__ __launch_bounds__(RW * 64) void router_bf16(RouterParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
-    const u32x4 zero = {0, 0, 0, 0};
+    // Rows past T and experts past E read a clamped valid row: their
+    // logits land in lanes that the selection never looks at, so the loads
+    // need no predicate (predicated loads serialise the k-loop).
 #pragma unroll 8
     for (int k0 = ks * 16; k0 < p.d; k0 += 16 * KS) {
-        const u32x4 av = tok_ok ? *(const u32x4 *)(xrow + k0) : zero;
+        const u32x4 av = *(const u32x4 *)(xrow + k0);
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const u32x4 bv = w_ok[i] ? *(const u32x4 *)(wrow[i] + k0) : zero;
+            const u32x4 bv = *(const u32x4 *)(wrow[i] + k0);
             acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 as_bf16x8(av), as_bf16x8(bv), acc[i], 0, 0, 0);
         }
