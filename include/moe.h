@@ -114,13 +114,27 @@ typedef struct moe_weights {
  *                            and beyond offsets[E] hold -1
  *   slot_of    [T][k] int32  slot of each assignment, -1 if it overflowed
  *   f, p       [E]    fp32   f_i = counts_i/(T k), p_i = mean_t p[t,i]
- *   l_aux      [1]    fp32   alpha * E * sum_i f_i p_i */
+ *   l_aux      [1]    fp32   alpha * E * sum_i f_i p_i
+ *   monitor    [6]    fp32   optional (NULL = not computed) router and load
+ *                            monitors, in this order:
+ *                            z-loss = mean_t (logsumexp_e logit[t,e])^2
+ *                            ("AI-Research-SKILLs MoE training guide",
+ *                            sec. 4.3), routing entropy in bits =
+ *                            mean_t -sum_e p log2 p ("The expert group
+ *                            activated per token", sec. 4.4), load imbalance
+ *                            = max count / min count (+inf if an expert is
+ *                            empty), utilization = nonempty experts / E,
+ *                            drop rate = assignments over capacity / (T k)
+ *                            (training guide, sec. 10.1), max share =
+ *                            largest count / T ("MoE architecture deep
+ *                            dive", sec. 4: collapse above 0.4) */
 typedef struct moe_routing {
     int32_t *topk_idx;
     float *topk_w;
     int32_t *counts, *kept, *offsets;
     int32_t *slot_token, *slot_of;
     float *f, *p, *l_aux;
+    float *monitor;
 } moe_routing;
 
 /* Host.  floor((double)T / E * cf): the capacity formula of "MoE
@@ -145,7 +159,8 @@ int moe_router_topk(const moe_desc *desc, const void *x,
 
 /* Counts, capacity, stable dispatch and statistics (layer steps 3 and 6).
  * Reads r->topk_idx and the router partial sums in the workspace; writes
- * counts, kept, offsets, slot_token, slot_of, f, p and l_aux. */
+ * counts, kept, offsets, slot_token, slot_of, f, p, l_aux and, if
+ * r->monitor is not NULL, the six monitors. */
 int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
                 size_t ws_bytes, void *stream);
 

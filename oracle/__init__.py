@@ -24,7 +24,7 @@ import numpy as np
 from . import build as _build
 
 __all__ = ["capacity", "router", "topk", "renorm_selection", "dispatch",
-           "stats", "layer_rows", "bias_update", "forward", "lib"]
+           "stats", "monitor", "layer_rows", "bias_update", "forward", "lib"]
 
 _LIB = None
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -62,6 +62,9 @@ def lib():
         L.oracle_layer_rows.argtypes = [ctypes.c_int, _i32p] + \
             [ctypes.c_int] * 4 + [_vp, _i32p, _f64p, _i32p] + \
             [ctypes.POINTER(_vp)] * 4 + [_vp] * 4 + [_f64p]
+        L.oracle_monitor.restype = None
+        L.oracle_monitor.argtypes = [ctypes.c_int] * 3 + [_f64p, _f64p, _i32p,
+                                                          _i32p, _f64p]
         L.oracle_bias_update.restype = None
         L.oracle_bias_update.argtypes = [ctypes.c_int, _i32p, ctypes.c_float,
                                          ctypes.c_float, _f32p]
@@ -265,6 +268,23 @@ def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
     return y
 
 
+MONITOR_NAMES = ("z_loss", "entropy_bits", "load_imbalance", "utilization",
+                 "drop_rate", "max_share")
+
+
+def monitor(logits, probs, counts, kept, k: int) -> np.ndarray:
+    """The six router/load monitors (see oracle_monitor), float64 [6]."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    probs = np.ascontiguousarray(probs, dtype=np.float64)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    kept = np.ascontiguousarray(kept, dtype=np.int32)
+    T, E = probs.shape
+    out = np.empty(6, np.float64)
+    lib().oracle_monitor(T, E, k, _p(logits, _f64p), _p(probs, _f64p),
+                         _p(counts, _i32p), _p(kept, _i32p), _p(out, _f64p))
+    return out
+
+
 def bias_update(counts, target: float, gamma: float, bias) -> np.ndarray:
     """One float32 balancing step; returns the new bias (input untouched)."""
     counts = np.ascontiguousarray(counts, dtype=np.int32)
@@ -292,8 +312,9 @@ def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
     x = inp["x"]
     T = x.shape[0]
     E = inp["wr"].shape[0]
+    logits = None
     if probs is None:
-        _, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
+        logits, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
     idx, w, margin = topk(probs, k)
     if selection is not None:
         idx = np.ascontiguousarray(selection, dtype=np.int32)
@@ -309,8 +330,11 @@ def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
     if inp.get("ws1") is not None:
         shared = (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
     y = layer_rows(tokens, x, idx, w, disp["slot_of"], experts, shared)
-    out = dict(probs=probs, topk_idx=idx, topk_w=w, margin=margin,
-               capacity=cap, f=f, p=p, l_aux=l_aux, y=y,
+    out = dict(probs=probs, logits=logits, topk_idx=idx, topk_w=w,
+               margin=margin, capacity=cap, f=f, p=p, l_aux=l_aux, y=y,
                tokens=np.asarray(tokens, dtype=np.int32))
+    if logits is not None:
+        out["monitor"] = monitor(logits, probs, disp["counts"], disp["kept"],
+                                 k)
     out.update(disp)
     return out

@@ -19,7 +19,9 @@
  *            capacity, sec. 2.4 auxiliary-loss-free balancing,
  *            sec. 3 DeepSeek-V3 shared expert.
  *   [GROUP]  "The expert group activated per token" (wmrh.cn):
- *            sec. 3.1 anatomy of an MoE layer (FFN formula, router).
+ *            sec. 3.1 anatomy of an MoE layer (FFN formula, router),
+ *            sec. 4.4 routing monitors (entropy).
+ *   [DIVE]   also sec. 4 (expert-collapse threshold of 40 percent).
  *
  * Precision: every floating-point step is IEEE double, except the
  * balancing-bias update, which the layer defines on float32 state.
@@ -304,6 +306,61 @@ int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
         free(o);
     }
     return status;
+}
+
+/* Router and load monitors, six values:
+ *   out[0] z-loss   = mean over tokens of (logsumexp_e logit[t,e])^2
+ *                     ([SKILL] sec. 4.3, router z-loss)
+ *   out[1] entropy  = mean over tokens of -sum_e p log2 p, in bits
+ *                     ([GROUP] sec. 4.4, routing entropy vs log2(E))
+ *   out[2] imbalance = max count / min count, +inf if an expert is empty
+ *   out[3] utilization = experts with a nonzero count / E
+ *   out[4] drop rate = assignments over capacity / (T k)
+ *                     (out[2..4]: [SKILL] sec. 10.1)
+ *   out[5] max share = largest count / T, the fraction of tokens sent to
+ *                     the busiest expert ([DIVE] sec. 4, collapse above 0.4)
+ * logits and probs are the router's (the adjusted logits actually used). */
+void oracle_monitor(int T, int E, int k, const double *logits,
+                    const double *probs, const int32_t *counts,
+                    const int32_t *kept, double *out)
+{
+    double z = 0.0, h = 0.0;
+    for (int t = 0; t < T; ++t) {
+        const double *lg = logits + (size_t)t * E;
+        const double *pr = probs + (size_t)t * E;
+        double m = lg[0];
+        for (int e = 1; e < E; ++e)
+            if (lg[e] > m)
+                m = lg[e];
+        double s = 0.0;
+        for (int e = 0; e < E; ++e)
+            s += exp(lg[e] - m);
+        const double lse = m + log(s);
+        z += lse * lse;
+        double ht = 0.0;
+        for (int e = 0; e < E; ++e)
+            if (pr[e] > 0.0)
+                ht -= pr[e] * log2(pr[e]);
+        h += ht;
+    }
+    out[0] = T > 0 ? z / T : 0.0;
+    out[1] = T > 0 ? h / T : 0.0;
+    int cmax = 0, cmin = 0, used = 0;
+    long total_kept = 0;
+    for (int e = 0; e < E; ++e) {
+        if (e == 0 || counts[e] > cmax)
+            cmax = counts[e];
+        if (e == 0 || counts[e] < cmin)
+            cmin = counts[e];
+        if (counts[e] > 0)
+            used += 1;
+        total_kept += kept[e];
+    }
+    out[2] = cmin > 0 ? (double)cmax / (double)cmin : INFINITY;
+    out[3] = (double)used / (double)E;
+    const double n = (double)T * (double)k;
+    out[4] = n > 0 ? (n - (double)total_kept) / n : 0.0;
+    out[5] = T > 0 ? (double)cmax / (double)T : 0.0;
 }
 
 /* Auxiliary-loss-free balancing, one step on float32 state:

@@ -42,7 +42,7 @@ class MoeRouting(ctypes.Structure):
     _fields_ = [("topk_idx", c_vp), ("topk_w", c_vp), ("counts", c_vp),
                 ("kept", c_vp), ("offsets", c_vp), ("slot_token", c_vp),
                 ("slot_of", c_vp), ("f", c_vp), ("p", c_vp),
-                ("l_aux", c_vp)]
+                ("l_aux", c_vp), ("monitor", c_vp)]
 
 
 # (name, restype, argtypes) of every entry point of include/moe.h

@@ -20,15 +20,18 @@ struct RouterParams {
     int32_t *topk_idx;    // [T][k]
     float *topk_w;        // [T][k]
     float *p_part;        // [ceil(T/32)][E]
+    float *zh_part;       // [ceil(T/32)][2]: sum lse^2, sum entropy (nats)
     int T, d, E, k;
 };
 
 struct PermuteParams {
     const int32_t *topk_idx;  // [T*k]
     const float *p_part;      // [n_rtiles][E]
+    const float *zh_part;     // [n_rtiles][2]
     int32_t *blk;             // [n_chunks][E] scratch
     int32_t *counts, *kept, *offsets, *slot_token, *slot_of;
     float *f, *p, *l_aux;
+    float *monitor;           // [6] or null
     int T, E, k, capacity, n_rtiles, n_chunks;
     float alpha;
 };

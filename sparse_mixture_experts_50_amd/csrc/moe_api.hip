@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t p_part, blk, h, yp, total;
+    size_t p_part, zh_part, blk, h, yp, total;
     int n_rtiles, n_chunks;
     size_t rows;
 };
@@ -49,6 +49,8 @@ WsLayout layout(const moe_desc *d) {
     size_t off = 0;
     L.p_part = off;
     off += align_up((size_t)L.n_rtiles * d->E * sizeof(float));
+    L.zh_part = off;
+    off += align_up((size_t)L.n_rtiles * 2 * sizeof(float));
     L.blk = off;
     off += align_up((size_t)L.n_chunks * d->E * sizeof(int32_t));
     L.h = off;
@@ -242,6 +244,7 @@ int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
     p.topk_idx = r->topk_idx;
     p.topk_w = r->topk_w;
     p.p_part = (float *)at(ws, L.p_part);
+    p.zh_part = (float *)at(ws, L.zh_part);
     p.T = desc->T;
     p.d = desc->d;
     p.E = desc->E;
@@ -260,6 +263,7 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     PermuteParams p;
     p.topk_idx = r->topk_idx;
     p.p_part = (const float *)at(ws, L.p_part);
+    p.zh_part = (const float *)at(ws, L.zh_part);
     p.blk = (int32_t *)at(ws, L.blk);
     p.counts = r->counts;
     p.kept = r->kept;
@@ -269,6 +273,7 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     p.f = r->f;
     p.p = r->p;
     p.l_aux = r->l_aux;
+    p.monitor = r->monitor;
     p.T = desc->T;
     p.E = desc->E;
     p.k = desc->k;

@@ -22,6 +22,31 @@ namespace {
 
 constexpr int CH = MOE_PERMUTE_CHUNK;
 
+// The six monitors from counts and kept (thread 0 of the block; the
+// per-router-block lse^2 and entropy sums are reduced in block order).
+__device__ void write_monitor(const PermuteParams &p, const int *cnt_s,
+                              const int *kept_s) {
+    float z = 0.0f, h = 0.0f;
+    for (int b = 0; b < p.n_rtiles; ++b) {
+        z += p.zh_part[(size_t)b * 2];
+        h += p.zh_part[(size_t)b * 2 + 1];
+    }
+    int cmax = cnt_s[0], cmin = cnt_s[0], used = 0, kept = 0;
+    for (int e = 0; e < p.E; ++e) {
+        cmax = max(cmax, cnt_s[e]);
+        cmin = min(cmin, cnt_s[e]);
+        used += cnt_s[e] > 0;
+        kept += kept_s[e];
+    }
+    const float n = (float)p.T * (float)p.k;
+    p.monitor[0] = z / (float)p.T;
+    p.monitor[1] = h / (float)p.T * 1.44269504088896340736f;  // nats -> bits
+    p.monitor[2] = cmin > 0 ? (float)cmax / (float)cmin : INFINITY;
+    p.monitor[3] = (float)used / (float)p.E;
+    p.monitor[4] = (n - (float)kept) / n;
+    p.monitor[5] = (float)cmax / (float)p.T;
+}
+
 __global__ __launch_bounds__(256) void permute_hist(PermuteParams p) {
     __shared__ int h[MOE_MAX_E];
     for (int e = threadIdx.x; e < p.E; e += blockDim.x) h[e] = 0;
@@ -42,6 +67,7 @@ __global__ __launch_bounds__(256) void permute_hist(PermuteParams p) {
 
 __global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
     __shared__ int kept_s[MOE_MAX_E];
+    __shared__ int cnt_s[MOE_MAX_E];
     __shared__ float fp_s[MOE_MAX_E];
     __shared__ int wsum[4];
     const int e = threadIdx.x;
@@ -85,6 +111,7 @@ __global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
         fp_s[e] = fe * pe;
     }
     kept_s[e] = kept;
+    cnt_s[e] = cnt;
     // exclusive scan of kept over experts (256 threads = 4 waves)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = kept;
@@ -103,6 +130,7 @@ __global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
         float s = 0.0f;
         for (int i = 0; i < p.E; ++i) s += fp_s[i];
         p.l_aux[0] = p.alpha * (float)p.E * s;
+        if (p.monitor) write_monitor(p, cnt_s, kept_s);
     }
 }
 
@@ -155,6 +183,8 @@ __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
     __shared__ int h[MOE_MAX_E];
     __shared__ int off_s[MOE_MAX_E + 1];
     __shared__ float fp_s[MOE_MAX_E];
+    __shared__ int cnt_s[MOE_MAX_E];
+    __shared__ int kept_s[MOE_MAX_E];
     __shared__ int wsum[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -181,6 +211,8 @@ __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
         p.p[e] = pe;
         p.f[e] = fe;
         fp_s[e] = fe * pe;
+        cnt_s[e] = cnt;
+        kept_s[e] = kept;
     }
     int incl = kept;
 #pragma unroll
@@ -205,6 +237,7 @@ __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
         float s = 0.0f;
         for (int i = 0; i < p.E; ++i) s += fp_s[i];
         p.l_aux[0] = p.alpha * (float)p.E * s;
+        if (p.monitor) write_monitor(p, cnt_s, kept_s);
     }
     __syncthreads();
     if (wave == 0) {

@@ -40,6 +40,7 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
         addv[i] = (valid[i] && p.add) ? p.add[e] : 0.0f;
         subv[i] = (valid[i] && p.sub) ? p.sub[e] : 0.0f;
     }
+    float zsum = 0.0f, hsum = 0.0f;
     for (int q = 0; q < RT / RW; ++q) {
         const int tl = wave * (RT / RW) + q;
         const int t = t0 + tl;
@@ -68,8 +69,17 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
             ls += ex[i];
         }
         const float S = wave_sum(ls);
+        float pl = 0.0f;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) psum[i] += ex[i] / S;
+        for (int i = 0; i < PER; ++i) {
+            psum[i] += ex[i] / S;
+            if (valid[i]) pl += ex[i] * (v[i] - m);
+        }
+        // monitors: logsumexp = m + ln S; entropy (nats) = ln S - sum p (l - m)
+        const float lnS = logf(S);
+        const float lse = m + lnS;
+        zsum += lse * lse;
+        hsum += lnS - wave_sum(pl) / S;
 
         // top-k: k rounds of a wave-wide (max logit, min index) search
         bool taken[PER];
@@ -118,7 +128,18 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
         const int e = lane + 64 * i;
         if (e < EP) pp[wave][e] = psum[i];
     }
+    __shared__ float zh[RW][2];
+    if (lane == 0) {
+        zh[wave][0] = zsum;
+        zh[wave][1] = hsum;
+    }
     __syncthreads();
+    if (threadIdx.x < 2) {
+        float s = zh[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < RW; ++w) s += zh[w][threadIdx.x];
+        p.zh_part[(size_t)blockIdx.x * 2 + threadIdx.x] = s;
+    }
     for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
         float s = pp[0][e];
 #pragma unroll

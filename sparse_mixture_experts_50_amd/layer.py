@@ -134,6 +134,9 @@ class Routing:
         self.f = z(E, dt=f32)
         self.p = z(E, dt=f32)
         self.l_aux = z(1, dt=f32)
+        # z-loss, entropy (bits), load imbalance, utilization, drop rate,
+        # max share
+        self.monitor = z(6, dt=f32)
 
     def struct(self) -> MoeRouting:
         return MoeRouting(*[_ptr(getattr(self, n)) for n, _ in

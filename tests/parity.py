@@ -54,7 +54,7 @@ def gpu_forward(w: workloads.Workload, inp: dict, steps: bool = False):
     torch.cuda.synchronize()
     out = {name: getattr(r, name).cpu().numpy() for name in (
         "topk_idx", "topk_w", "counts", "kept", "offsets", "slot_token",
-        "slot_of", "f", "p", "l_aux")}
+        "slot_of", "f", "p", "l_aux", "monitor")}
     out["y"] = y.float().cpu().numpy().astype(np.float64)
     out["layer"] = layer
     return out
@@ -114,6 +114,18 @@ def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
     assert np.allclose(gpu["p"], cond["p"], rtol=1e-4, atol=2e-6)
     assert abs(gpu["l_aux"][0] - cond["l_aux"]) <= 1e-4 * abs(cond["l_aux"]) \
         + 1e-7
+    # monitors: z-loss, entropy (bits), imbalance, utilization, drop rate,
+    # max share
+    mon = oracle.monitor(ref["logits"], probs, cond["counts"], cond["kept"],
+                         w.k)
+    g = gpu["monitor"].astype(np.float64)
+    assert abs(g[0] - mon[0]) <= 1e-4 * abs(mon[0]) + 1e-6, (g, mon)
+    assert abs(g[1] - mon[1]) <= 2e-4, (g, mon)
+    if np.isinf(mon[2]):
+        assert np.isinf(g[2])
+    else:
+        assert abs(g[2] - mon[2]) <= 1e-6 * mon[2], (g, mon)
+    assert np.allclose(g[3:], mon[3:], rtol=1e-6, atol=1e-7), (g, mon)
     # outputs on the checked rows
     y_ref = cond["y"]
     y_gpu = gpu["y"][tokens]

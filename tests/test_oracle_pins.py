@@ -417,3 +417,63 @@ def test_capacity_top2_keeps_pre_drop_weight():
             inp["x"][t:t + 1], inp["w1"][e], None, inp["w2"][e], None)[0]
         assert out["topk_w"][t, j] < 1.0
         assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------- monitors
+def test_monitor_uniform_closed_forms():
+    # zero router weights: logits all 0, so logsumexp = ln E and the
+    # entropy is log2 E bits ([GROUP] 4.4 compares against log2(16) = 4)
+    for E in (4, 8, 16):
+        T, d, k = 10, 8, 2
+        x = np.random.default_rng(E).standard_normal((T, d)).astype(np.float32)
+        lg, pr = oracle.router(x, np.zeros((E, d), np.float32))
+        idx, _, _ = oracle.topk(pr, k)
+        disp = oracle.dispatch(idx, E, -1)
+        m = oracle.monitor(lg, pr, disp["counts"], disp["kept"], k)
+        assert abs(m[0] - math.log(E) ** 2) < 1e-12
+        assert abs(m[1] - math.log2(E)) < 1e-12
+    assert abs(math.log2(16) - 4.0) == 0.0
+
+
+def test_monitor_confident_router_has_zero_entropy():
+    wr = np.zeros((4, 2), np.float32)
+    wr[2, 0] = 1.0
+    x = np.array([[800.0, 0.0]], np.float32)
+    lg, pr = oracle.router(x, wr)
+    m = oracle.monitor(lg, pr, np.array([0, 0, 1, 0], np.int32),
+                       np.array([0, 0, 1, 0], np.int32), 1)
+    assert m[1] == 0.0
+    assert abs(m[0] - 800.0 ** 2) < 1e-6 * 800.0 ** 2
+
+
+def test_monitor_count_statistics_golden():
+    # [SKILL] 10.1: imbalance max/min (healthy near 1, act above 2),
+    # utilization used/E, drop rate dropped/total; [DIVE] 4: collapse when
+    # one expert takes over 40 percent of the tokens
+    T, E, k = 10, 4, 2
+    probs = np.full((T, E), 0.25)
+    logits = np.zeros((T, E))
+    counts = np.array([8, 6, 4, 2], np.int32)
+    kept = np.array([5, 5, 4, 2], np.int32)
+    m = oracle.monitor(logits, probs, counts, kept, k)
+    assert m[2] == 4.0 and m[3] == 1.0
+    assert abs(m[4] - 4 / 20) < 1e-15
+    assert m[5] == 0.8
+    m2 = oracle.monitor(logits, probs, np.array([10, 10, 0, 0], np.int32),
+                        np.array([10, 10, 0, 0], np.int32), k)
+    assert math.isinf(m2[2]) and m2[3] == 0.5 and m2[4] == 0.0
+
+
+def test_monitor_matches_direct_definitions():
+    # library re-statement on random routing: scipy logsumexp and entropy
+    from scipy.special import logsumexp
+    from scipy.stats import entropy
+    w, inp = tiny_inputs(E=6, T=30)
+    out = oracle.forward(inp, k=2, capacity_factor=0.5)
+    lg = out["logits"]
+    assert abs(out["monitor"][0] - np.mean(logsumexp(lg, axis=1) ** 2)) \
+        < 1e-12
+    assert abs(out["monitor"][1] -
+               np.mean(entropy(out["probs"], base=2, axis=1))) < 1e-12
+    c, kp = out["counts"], out["kept"]
+    assert out["monitor"][4] == (60 - kp.sum()) / 60
