@@ -62,6 +62,13 @@ def lib():
         L.oracle_layer_rows.argtypes = [ctypes.c_int, _i32p] + \
             [ctypes.c_int] * 4 + [_vp, _i32p, _f64p, _i32p] + \
             [ctypes.POINTER(_vp)] * 4 + [_vp] * 4 + [_f64p]
+        L.oracle_expert_choice.restype = ctypes.c_int
+        L.oracle_expert_choice.argtypes = [ctypes.c_int] * 3 + [
+            _f64p, _f64p, _i32p, _i32p, _f64p, _i32p]
+        L.oracle_expert_choice_rows.restype = ctypes.c_int
+        L.oracle_expert_choice_rows.argtypes = [ctypes.c_int, _i32p] + \
+            [ctypes.c_int] * 4 + [_vp, _f64p] + [ctypes.POINTER(_vp)] * 4 + \
+            [_vp] * 4 + [_f64p]
         L.oracle_monitor.restype = None
         L.oracle_monitor.argtypes = [ctypes.c_int] * 3 + [_f64p, _f64p, _i32p,
                                                           _i32p, _f64p]
@@ -212,26 +219,12 @@ class Experts:
                                      w2[e], None if b2 is None else b2[e]))
 
 
-def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
-               shared=None) -> np.ndarray:
-    """Layer output rows y[tokens] (float64 [n, d]) for the given routing.
-    ``slot_of`` None means every assignment is kept.  ``shared`` is
-    ``(Ws1, bs1, Ws2, bs2)`` or None."""
-    tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
-    xa, dt = _raw(x)
-    T, d = xa.shape
-    idx = np.ascontiguousarray(idx, dtype=np.int32)
-    k = idx.shape[1]
-    w = np.ascontiguousarray(w, dtype=np.float64)
-    so = None if slot_of is None else np.ascontiguousarray(slot_of,
-                                                          dtype=np.int32)
+def _weight_tables(need, experts: Experts, dt: int, shared):
+    """Pointer tables (w1, b1, w2, b2) over the experts in ``need`` (None
+    for an absent bias family), the shared expert's four pointers, d_ff,
+    and the converted arrays that must stay alive during the call."""
     E = experts.E
-    need = set()
-    for t in tokens.tolist():
-        for j in range(k):
-            if so is None or so[t, j] >= 0:
-                need.add(int(idx[t, j]))
-    keep = []           # keeps converted arrays alive during the call
+    keep = []
     tabs = [(_vp * E)() for _ in range(4)]
     d_ff = None
     for e in sorted(need):
@@ -249,23 +242,138 @@ def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
         for i, a in enumerate(shared):
             ra, rdt = _raw(a)
             if ra is not None:
-                assert rdt == dt
+                assert rdt == dt, "weights and x must share a dtype"
                 keep.append(ra)
                 sh[i] = ra.ctypes.data
         d_ff = shared[0].shape[0]
-    if d_ff is None:
-        d_ff = 1
+    for i in (1, 3):
+        if not any(tabs[i][e] for e in range(E)):
+            tabs[i] = None
+    return tabs, sh, (1 if d_ff is None else d_ff), keep
+
+
+def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
+               shared=None) -> np.ndarray:
+    """Layer output rows y[tokens] (float64 [n, d]) for the given routing.
+    ``slot_of`` None means every assignment is kept.  ``shared`` is
+    ``(Ws1, bs1, Ws2, bs2)`` or None."""
+    tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    xa, dt = _raw(x)
+    T, d = xa.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    k = idx.shape[1]
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    so = None if slot_of is None else np.ascontiguousarray(slot_of,
+                                                          dtype=np.int32)
+    need = set()
+    for t in tokens.tolist():
+        for j in range(k):
+            if so is None or so[t, j] >= 0:
+                need.add(int(idx[t, j]))
+    tabs, sh, d_ff, keep = _weight_tables(need, experts, dt, shared)
     y = np.zeros((len(tokens), d), np.float64)
-    has_b1 = any(tabs[1][e] for e in range(E))
-    has_b2 = any(tabs[3][e] for e in range(E))
     rc = lib().oracle_layer_rows(
         len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, xa.ctypes.data,
-        _p(idx, _i32p), _p(w, _f64p), _p(so, _i32p), tabs[0],
-        tabs[1] if has_b1 else None, tabs[2], tabs[3] if has_b2 else None,
-        sh[0], sh[1], sh[2], sh[3], _p(y, _f64p))
+        _p(idx, _i32p), _p(w, _f64p), _p(so, _i32p), *tabs, *sh,
+        _p(y, _f64p))
     if rc != 0:
         raise RuntimeError(f"oracle_layer_rows failed ({rc})")
     return y
+
+
+def expert_choice(logits: np.ndarray, probs: np.ndarray, C: int) -> dict:
+    """Expert-Choice selection: slot_token [E*C] (expert-major, tokens
+    ascending within an expert), slot_of [T,E] (slot or -1), gate [T,E]
+    (picked probabilities, else 0), picks [T]."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    probs = np.ascontiguousarray(probs, dtype=np.float64)
+    T, E = probs.shape
+    st = np.empty(max(E * C, 0), np.int32)
+    so = np.empty((T, E), np.int32)
+    gate = np.empty((T, E), np.float64)
+    picks = np.empty(T, np.int32)
+    rc = lib().oracle_expert_choice(T, E, C, _p(logits, _f64p),
+                                    _p(probs, _f64p), _p(st, _i32p),
+                                    _p(so, _i32p), _p(gate, _f64p),
+                                    _p(picks, _i32p))
+    if rc != 0:
+        raise ValueError("capacity must lie in [0, T]")
+    return dict(slot_token=st, slot_of=so, gate=gate, picks=picks)
+
+
+def expert_choice_rows(tokens, x, gate: np.ndarray, experts: "Experts",
+                       shared=None) -> np.ndarray:
+    """Expert-Choice layer output rows y[tokens] (float64 [n, d])."""
+    tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    xa, dt = _raw(x)
+    T, d = xa.shape
+    gate = np.ascontiguousarray(gate, dtype=np.float64)
+    E = experts.E
+    need = set()
+    for t in tokens.tolist():
+        need.update(int(e) for e in np.nonzero(gate[t])[0])
+    tabs, sh, d_ff, keep = _weight_tables(need, experts, dt, shared)
+    y = np.zeros((len(tokens), d), np.float64)
+    rc = lib().oracle_expert_choice_rows(
+        len(tokens), _p(tokens, _i32p), d, E, d_ff, dt, xa.ctypes.data,
+        _p(gate, _f64p), *tabs, *sh, _p(y, _f64p))
+    if rc != 0:
+        raise RuntimeError(f"oracle_expert_choice_rows failed ({rc})")
+    return y
+
+
+def _selection_from_slots(slot_token: np.ndarray, probs: np.ndarray,
+                         C: int) -> dict:
+    """slot_of, gate and picks implied by given per-expert picks."""
+    T, E = probs.shape
+    so = np.full((T, E), -1, np.int32)
+    gate = np.zeros((T, E))
+    picks = np.zeros(T, np.int32)
+    for e in range(E):
+        for r, t in enumerate(slot_token[e * C:(e + 1) * C].tolist()):
+            so[t, e] = e * C + r
+            gate[t, e] = probs[t, e]
+            picks[t] += 1
+    return dict(slot_token=np.ascontiguousarray(slot_token, dtype=np.int32),
+                slot_of=so, gate=gate, picks=picks)
+
+
+def forward_expert_choice(inp: dict, capacity: int, alpha: float = 0.01,
+                          tokens: Optional[Sequence[int]] = None,
+                          selection: Optional[np.ndarray] = None) -> dict:
+    """The Expert-Choice layer step by step.
+
+    Every token is a candidate of every expert, so the routing statistics
+    are those of top-k routing with k = E: counts = T per expert, kept = C,
+    offsets e*C.  ``selection`` [E*C] replaces the oracle's own picks (a
+    checker adopting equally valid picks at near-ties); the gates then
+    come from the oracle's probabilities."""
+    x = inp["x"]
+    T = x.shape[0]
+    logits, probs = router(x, inp["wr"], inp.get("br"), inp.get("ebias"))
+    E = probs.shape[1]
+    if selection is None:
+        ec = expert_choice(logits, probs, capacity)
+    else:
+        ec = _selection_from_slots(selection, probs, capacity)
+    counts = np.full(E, T, np.int32)
+    kept = np.full(E, capacity, np.int32)
+    offsets = (np.arange(E + 1) * capacity).astype(np.int32)
+    f, p, l_aux = stats(probs, counts, E, alpha)
+    mon = monitor(logits, probs, counts, kept, E)
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    experts = Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
+                              inp.get("b2"))
+    shared = None
+    if inp.get("ws1") is not None:
+        shared = (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+    y = expert_choice_rows(tokens, x, ec["gate"], experts, shared)
+    out = dict(logits=logits, probs=probs, counts=counts, kept=kept,
+               offsets=offsets, f=f, p=p, l_aux=l_aux, monitor=mon, y=y,
+               tokens=np.asarray(tokens, dtype=np.int32), capacity=capacity)
+    out.update(ec)
+    return out
 
 
 MONITOR_NAMES = ("z_loss", "entropy_bits", "load_imbalance", "utilization",

@@ -308,6 +308,110 @@ int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
     return status;
 }
 
+/* Expert-Choice routing: every expert picks its own C tokens.
+ * [SKILL] sec. 4.2: the expert scores are the router output transposed to
+ * (experts, tokens) and each expert takes the top capacity_per_expert
+ * tokens; this balances the load exactly.  Readings taken where the page
+ * is silent: the score is the router logit of (token, expert) (the page
+ * transposes the router output itself, before any softmax); ties go to
+ * the lower token index; the combine weight of a pick is the token's
+ * softmax gate probability for that expert ([DIVE] sec. 1.2 gate
+ * weights), not renormalised.  Slots are expert-major, C per expert, and
+ * within an expert in ascending token order.  Outputs:
+ *   slot_token[e*C + r]  the r-th picked token of expert e
+ *   slot_of[t*E + e]     slot of (t, e), or -1 if e did not pick t
+ *   gate[t*E + e]        probs[t,e] if e picked t, else 0
+ *   picks[t]             how many experts picked t
+ * Requires 0 <= C <= T. */
+int oracle_expert_choice(int T, int E, int C, const double *logits,
+                         const double *probs, int32_t *slot_token,
+                         int32_t *slot_of, double *gate, int32_t *picks)
+{
+    if (C < 0 || C > T)
+        return OR_ERR_ARG;
+    for (size_t i = 0; i < (size_t)T * E; ++i) {
+        gate[i] = 0.0;
+        slot_of[i] = -1;
+    }
+    for (int t = 0; t < T; ++t)
+        picks[t] = 0;
+    char *taken = (char *)malloc((size_t)(T > 0 ? T : 1));
+    for (int e = 0; e < E; ++e) {
+        memset(taken, 0, (size_t)(T > 0 ? T : 1));
+        for (int r = 0; r < C; ++r) {           /* C rounds of argmax */
+            int best = -1;
+            for (int t = 0; t < T; ++t)
+                if (!taken[t] && (best < 0 ||
+                                  logits[(size_t)t * E + e] >
+                                      logits[(size_t)best * E + e]))
+                    best = t;
+            taken[best] = 1;
+        }
+        int r = 0;
+        for (int t = 0; t < T; ++t)             /* ascending token order */
+            if (taken[t]) {
+                const int slot = e * C + r;
+                slot_token[slot] = t;
+                slot_of[(size_t)t * E + e] = slot;
+                gate[(size_t)t * E + e] = probs[(size_t)t * E + e];
+                picks[t] += 1;
+                ++r;
+            }
+    }
+    free(taken);
+    return OR_OK;
+}
+
+/* Expert-Choice layer output for listed tokens:
+ *   y_t = sum over experts e that picked t (ascending e) of
+ *         gate[t,e] * Expert_e(x_t)   (+ Shared(x_t))
+ * A token no expert picked gets 0 (plus the shared expert). */
+int oracle_expert_choice_rows(int n, const int32_t *tokens, int d, int E,
+                              int d_ff, int dtype, const void *x,
+                              const double *gate, const void *const *w1,
+                              const void *const *b1, const void *const *w2,
+                              const void *const *b2, const void *ws1,
+                              const void *bs1, const void *ws2,
+                              const void *bs2, double *y)
+{
+    int status = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n; ++r) {
+        int t = tokens[r];
+        double *xrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        double *yr = y + (size_t)r * d;
+        for (int c = 0; c < d; ++c) {
+            xrow[c] = ld(x, (size_t)t * d + c, dtype);
+            yr[c] = 0.0;
+        }
+        for (int e = 0; e < E; ++e) {
+            const double g = gate[(size_t)t * E + e];
+            if (g == 0.0)
+                continue;
+            if (!w1[e] || !w2[e]) {
+#pragma omp atomic write
+                status = OR_ERR_MISSING_EXPERT;
+                continue;
+            }
+            expert_apply(d, d_ff, dtype, xrow, w1[e], b1 ? b1[e] : NULL,
+                         w2[e], b2 ? b2[e] : NULL, h, o);
+            for (int c = 0; c < d; ++c)
+                yr[c] += g * o[c];
+        }
+        if (ws1) {
+            expert_apply(d, d_ff, dtype, xrow, ws1, bs1, ws2, bs2, h, o);
+            for (int c = 0; c < d; ++c)
+                yr[c] += o[c];
+        }
+        free(xrow);
+        free(h);
+        free(o);
+    }
+    return status;
+}
+
 /* Router and load monitors, six values:
  *   out[0] z-loss   = mean over tokens of (logsumexp_e logit[t,e])^2
  *                     ([SKILL] sec. 4.3, router z-loss)

@@ -477,3 +477,116 @@ def test_monitor_matches_direct_definitions():
                np.mean(entropy(out["probs"], base=2, axis=1))) < 1e-12
     c, kp = out["counts"], out["kept"]
     assert out["monitor"][4] == (60 - kp.sum()) / 60
+
+
+# ---------------------------------------------------------- expert choice
+def _ec_brute(logits, C):
+    """Per expert, the C-subset of tokens with the largest score sum; among
+    equal sums the lexicographically smallest token set (the lower-index
+    tie rule).  Exhaustive over all subsets: independent of any sort."""
+    T, E = logits.shape
+    out = []
+    for e in range(E):
+        best, best_set = None, None
+        for sub in itertools.combinations(range(T), C):
+            s = sum(logits[t, e] for t in sub)
+            if best is None or s > best:
+                best, best_set = s, sub
+        out.append(best_set)
+    return out
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(1, 7), st.integers(1, 4), st.data())
+def test_expert_choice_brute_force(T, E, data):
+    # integer scores make ties frequent; the tie rule is the lower token
+    C = data.draw(st.integers(0, T))
+    vals = data.draw(st.lists(st.integers(-2, 2), min_size=T * E,
+                              max_size=T * E))
+    logits = np.array(vals, np.float64).reshape(T, E)
+    probs = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    ec = oracle.expert_choice(logits, probs, C)
+    want = _ec_brute(logits, C)
+    for e in range(E):
+        got = ec["slot_token"][e * C:(e + 1) * C]
+        assert tuple(got.tolist()) == tuple(want[e])
+        for r, t in enumerate(got.tolist()):
+            assert ec["slot_of"][t, e] == e * C + r
+            assert ec["gate"][t, e] == probs[t, e]
+    assert ec["picks"].sum() == E * C
+    assert np.count_nonzero(ec["slot_of"] >= 0) == E * C
+    assert np.all((ec["gate"] == 0) == (ec["slot_of"] < 0)) or \
+        np.any(probs == 0)
+
+
+def test_expert_choice_perfect_balance():
+    # the pages' claim: every expert gets exactly its capacity
+    w, inp = tiny_inputs(E=6, T=48)
+    out = oracle.forward_expert_choice(inp, capacity=10)
+    assert np.all(out["kept"] == 10)
+    for e in range(6):
+        assert np.count_nonzero(out["slot_of"][:, e] >= 0) == 10
+    assert np.array_equal(out["offsets"], np.arange(7) * 10)
+    # Every token is a candidate of every expert: f = 1/E, L_aux = alpha.
+    assert np.allclose(out["f"], 1 / 6, rtol=1e-15)
+    assert abs(out["l_aux"] - 0.01) < 1e-15
+    # drop rate = assignments not kept = 1 - C/T
+    i = oracle.MONITOR_NAMES.index("drop_rate")
+    assert abs(out["monitor"][i] - (1 - 10 / 48)) < 1e-12
+
+
+def test_expert_choice_ranks_by_logit_not_probability():
+    # expert 1 scores token 0 with logit 0 (prob 0.119) and token 1 with
+    # logit 1 (prob 0.018): the transposed router output ranks by logit
+    logits = np.array([[2.0, 0.0], [5.0, 1.0]])
+    probs = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    ec = oracle.expert_choice(logits, probs, 1)
+    assert ec["slot_token"].tolist() == [1, 1]
+    assert ec["picks"].tolist() == [0, 2]
+    assert ec["gate"][1].tolist() == probs[1].tolist()
+
+
+def test_expert_choice_full_capacity_is_soft_mixture():
+    # C = T: every expert takes every token, y = sum_e p_e FFN_e(x) (+ the
+    # shared expert), the dense softmax mixture
+    w, inp = tiny_inputs(E=4, T=20)
+    out = oracle.forward_expert_choice(inp, capacity=20)
+    logits = torch.nn.functional.linear(inp["x"].double(),
+                                        inp["wr"].double(),
+                                        inp["br"].double())
+    p = torch.softmax(logits, -1).numpy()
+    ref = sum(p[:, e:e + 1] * dense_ffn_torch(
+        inp["x"], inp["w1"][e], inp["b1"][e], inp["w2"][e], inp["b2"][e])
+        for e in range(4))
+    assert np.allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+    assert np.all(out["picks"] == 4)
+
+
+def test_expert_choice_rows_partial_picks():
+    # C < T: each row sums only the experts that picked it, unrenormalised;
+    # a row nobody picked is zero
+    w, inp = tiny_inputs(E=4, T=24)
+    out = oracle.forward_expert_choice(inp, capacity=3)
+    ffn = [dense_ffn_torch(inp["x"], inp["w1"][e], inp["b1"][e],
+                           inp["w2"][e], inp["b2"][e]) for e in range(4)]
+    logits = torch.nn.functional.linear(inp["x"].double(),
+                                        inp["wr"].double(),
+                                        inp["br"].double()).numpy()
+    p = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    ref = np.zeros_like(out["y"])
+    for e in range(4):
+        top = np.argsort(-logits[:, e], kind="stable")[:3]
+        ref[top] += p[top, e:e + 1] * ffn[e][top]
+    assert np.allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+    assert np.any(out["picks"] == 0)
+    assert np.all(out["y"][out["picks"] == 0] == 0.0)
+
+
+def test_expert_choice_zero_capacity_and_bounds():
+    w, inp = tiny_inputs(E=3, T=10)
+    out = oracle.forward_expert_choice(inp, capacity=0)
+    assert out["slot_token"].size == 0 and np.all(out["slot_of"] == -1)
+    assert np.all(out["y"] == 0.0)
+    lg = np.zeros((4, 2))
+    with pytest.raises(ValueError):
+        oracle.expert_choice(lg, lg, 5)
