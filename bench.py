@@ -78,7 +78,7 @@ def algorithmic(wl, counts, kept):
     """FLOPs and bytes of one forward (kept rows only, touched experts)."""
     import numpy as np
     es = wl.elem_bytes
-    rows = int(np.sum(kept)) + wl.n_shared * wl.T
+    rows = int(np.sum(kept)) + wl.n_shared * wl.T     # expert GEMM rows
     touched = int(np.sum(kept > 0)) + wl.n_shared
     flops = 2.0 * wl.T * wl.d * wl.E + 4.0 * rows * wl.d * wl.d_ff
     expert_bytes = (2 * wl.d * wl.d_ff + (wl.d + wl.d_ff if wl.linear_biases
@@ -108,7 +108,11 @@ def cpu_baseline(wl, inp, budget_s):
         sub = dict(host)
         sub["x"] = host["x"][:n]
         t0 = time.perf_counter()
-        oracle.forward(sub, wl.k, wl.capacity_factor, wl.alpha)
+        if wl.routing == "expert_choice":
+            C = min(n, oracle.capacity(n, wl.E, wl.capacity_factor))
+            oracle.forward_expert_choice(sub, C, wl.alpha)
+        else:
+            oracle.forward(sub, wl.k, wl.capacity_factor, wl.alpha)
         return time.perf_counter() - t0
 
     n = min(wl.T, max(1, cores))
@@ -162,7 +166,8 @@ def main():
     n_x = wl.calls
     xs = [inp["x"]] + [workloads.make_x(wl, dev, c) for c in range(1, n_x)]
     weights = moe.Weights.from_dict(inp)
-    layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha)
+    layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha,
+                         routing=wl.routing)
     desc, r, ws, y = layer.buffers(wl.T)
     stream = torch.cuda.current_stream(dev)
 
@@ -210,7 +215,7 @@ def main():
     alg = algorithmic(wl, counts, kept)
     assert int(counts.sum()) == wl.T * wl.k
     tokens_per_s = wl.T * steps / (total_ms / 1e3)
-    if wl.T * wl.k / wl.E <= 48:
+    if float(np.sum(kept)) / wl.E <= 48:       # rows per routed expert
         roof = dict(bound="hbm", achieved=alg["up_bytes"] / (up_avg_ms * 1e6),
                     peak=HBM_PEAK_GBS, unit="GB/s")
     else:
@@ -244,7 +249,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E,
                    "k": wl.k, "d_ff": wl.d_ff, "n_shared": wl.n_shared,
                    "capacity_factor": wl.capacity_factor,
-                   "parallelism": "single-gpu"},
+                   "routing": wl.routing, "parallelism": "single-gpu"},
         "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
         "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),
         "wall_s": wall,

@@ -23,6 +23,25 @@
  *   7. balancing-bias step b_i += gamma * sign(count_i - target)
  *      ("MoE architecture deep dive", sec. 2.4).
  *
+ * Expert-Choice routing (desc->routing == MOE_ROUTE_EXPERT_CHOICE;
+ * "AI-Research-SKILLs MoE training guide", sec. 4.2, Expert Choice):
+ * instead of steps 2-3 every expert picks its own C = desc->capacity
+ * tokens, the C largest router logits l[t,e] in its column (ties to the
+ * lower token index), so each expert holds exactly C tokens.  A pick is
+ * weighted by the token's softmax probability p[t,e], not renormalised; a
+ * token no expert picked gets y = 0 (plus the shared expert).  The mode
+ * reuses the top-k data layout with k = E: each token is a candidate of
+ * every expert, in expert order, and the capacity rule becomes the
+ * per-expert top-C.  So for every t and e:
+ *   topk_idx[t][e] = e,  topk_w[t][e] = p[t,e],
+ *   slot_of[t][e]  = e*C + (rank of t among the picks of e in token
+ *                    order), or -1 if e did not pick t,
+ *   slot_token[e*C + r] = the r-th picked token of e (ascending),
+ *   counts[e] = T, kept[e] = C, offsets[e] = e*C,
+ * and f, p, L_aux and the monitors follow from those counts with k = E
+ * (f_i = 1/E, L_aux = alpha * sum_i p_i = alpha).  The expert FFN and
+ * combine steps are the same as for top-k.
+ *
  * Conventions for every entry point:
  *   - Pointers named in the structs and arguments are DEVICE pointers unless
  *     stated otherwise; arrays are row-major and contiguous.
@@ -63,24 +82,33 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+typedef enum {
+    MOE_ROUTE_TOPK = 0,          /* tokens choose k experts (default) */
+    MOE_ROUTE_EXPERT_CHOICE = 1  /* experts choose C tokens */
+} moe_routing_mode;
+
 /* Layer shape, host struct passed by pointer.
  *   T         tokens (>= 0)
  *   d         model width; multiple of 64
  *   E         routed experts, 1 <= E <= 256
- *   k         experts per token, 1 <= k <= E
+ *   k         experts per token, 1 <= k <= min(E, 64); must equal E for
+ *             expert choice
  *   d_ff      expert hidden width; multiple of 64
  *   n_shared  0 or 1 always-on shared expert (weight 1)
  *   dtype     MOE_F32 or MOE_BF16 for x, all weight matrices, the expert
  *             Linear biases and y (arithmetic accumulates in fp32)
- *   capacity  -1 = no limit, else C >= 0 assignments kept per expert
- *             (see moe_capacity)
- *   aux_alpha coefficient of L_aux (0.01 is the pages' usual value) */
+ *   capacity  top-k: -1 = no limit, else C >= 0 assignments kept per
+ *             expert (see moe_capacity); expert choice: tokens picked per
+ *             expert, 0 <= C <= T (required)
+ *   aux_alpha coefficient of L_aux (0.01 is the pages' usual value)
+ *   routing   a moe_routing_mode */
 typedef struct moe_desc {
     int32_t T, d, E, k, d_ff;
     int32_t n_shared;
     int32_t dtype;
     int32_t capacity;
     float aux_alpha;
+    int32_t routing;
 } moe_desc;
 
 /* Weights: caller-owned, read-only device buffers; NULL = absent.
@@ -111,7 +139,9 @@ typedef struct moe_weights {
  *   kept       [E]    int32  min(counts, C)
  *   offsets    [E+1]  int32  exclusive prefix sum of kept
  *   slot_token [T*k]  int32  token of each expert-sorted slot; slots at
- *                            and beyond offsets[E] hold -1
+ *                            and beyond offsets[E] hold -1 (expert
+ *                            choice: [E*C], every slot used; may be NULL
+ *                            when E*C == 0)
  *   slot_of    [T][k] int32  slot of each assignment, -1 if it overflowed
  *   f, p       [E]    fp32   f_i = counts_i/(T k), p_i = mean_t p[t,i]
  *   l_aux      [1]    fp32   alpha * E * sum_i f_i p_i
@@ -152,7 +182,10 @@ size_t moe_workspace_size(const moe_desc *desc);
 /* Router GEMM fused with bias, softmax, top-k and renormalisation
  * (layer steps 1-2).  Reads x [T][d] and the router weights; writes
  * r->topk_idx, r->topk_w and per-token-tile probability column sums into
- * the workspace (consumed by moe_permute for p_i). */
+ * the workspace (consumed by moe_permute for p_i).  Expert choice: writes
+ * topk_idx = e and topk_w = p[t,e] for all E experts, sets every entry of
+ * r->slot_of (required) to -1, and writes the logits, transposed to
+ * [E][T], into the workspace for moe_permute. */
 int moe_router_topk(const moe_desc *desc, const void *x,
                     const moe_weights *w, moe_routing *r, void *ws,
                     size_t ws_bytes, void *stream);
@@ -160,16 +193,20 @@ int moe_router_topk(const moe_desc *desc, const void *x,
 /* Counts, capacity, stable dispatch and statistics (layer steps 3 and 6).
  * Reads r->topk_idx and the router partial sums in the workspace; writes
  * counts, kept, offsets, slot_token, slot_of, f, p, l_aux and, if
- * r->monitor is not NULL, the six monitors. */
+ * r->monitor is not NULL, the six monitors.  Expert choice: each expert's
+ * top-C selection over the workspace logits replaces the capacity cut
+ * (r->topk_idx is not read), and only the picked entries of slot_of are
+ * written, over the -1 that moe_router_topk left there. */
 int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
                 size_t ws_bytes, void *stream);
 
 /* Grouped expert FFNs (layer step 4): for every kept slot s of expert e,
  *   Yp[s] = W2_e GELU(W1_e x[slot_token[s]] + b1_e) + b2_e,
- * and, with a shared expert, Yp[T*k + t] = Shared(x[t]) for every token.
- * Yp is written into the workspace (dtype, [T*k + n_shared*T][d]); the
- * hidden activations are rounded to dtype between the two GEMMs.
- * Equivalent to moe_ffn_up followed by moe_ffn_down. */
+ * and, with a shared expert, Yp[R + t] = Shared(x[t]) for every token,
+ * where R = T*k routed slots (expert choice: R = E*C).  Yp is written
+ * into the workspace (dtype, [R + n_shared*T][d]); the hidden activations
+ * are rounded to dtype between the two GEMMs.  Equivalent to moe_ffn_up
+ * followed by moe_ffn_down. */
 int moe_grouped_ffn(const moe_desc *desc, const void *x,
                     const moe_weights *w, const moe_routing *r, void *ws,
                     size_t ws_bytes, void *stream);
@@ -186,7 +223,7 @@ int moe_ffn_down(const moe_desc *desc, const moe_weights *w,
                  void *stream);
 
 /* Weighted combine (layer step 5): y[t] = sum over kept j, in j order, of
- * topk_w[t,j] * Yp[slot_of[t,j]], plus Yp[T*k + t] with a shared expert;
+ * topk_w[t,j] * Yp[slot_of[t,j]], plus Yp[R + t] with a shared expert;
  * fp32 accumulation, one rounding to dtype.  y is [T][d], dtype. */
 int moe_combine(const moe_desc *desc, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);

@@ -23,12 +23,15 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_ROUTE_TOPK = 0
+MOE_ROUTE_EXPERT_CHOICE = 1
 
 
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("k", c_i32),
                 ("d_ff", c_i32), ("n_shared", c_i32), ("dtype", c_i32),
-                ("capacity", c_i32), ("aux_alpha", ctypes.c_float)]
+                ("capacity", c_i32), ("aux_alpha", ctypes.c_float),
+                ("routing", c_i32)]
 
 
 class MoeWeights(ctypes.Structure):

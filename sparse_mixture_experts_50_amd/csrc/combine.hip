@@ -16,76 +16,99 @@
 
 namespace {
 
+constexpr int MAX_K = MOE_MAX_E;     // expert choice: k = E <= 256
+
+// 16 bytes of row `row_off` (elements) at vector index v: 8 bf16 or 4 fp32.
+template <bool BF16>
+__device__ __forceinline__ u32x4 load_vec(const void *yp, size_t row_off,
+                                          int v) {
+    if (BF16) return *((const u32x4 *)((const uint16_t *)yp + row_off) + v);
+    return *((const u32x4 *)((const float *)yp + row_off) + v);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void fma_vec(float *acc, float w, u32x4 q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+            acc[2 * i] = fmaf(w, bf16_lo(q[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, bf16_hi(q[i]), acc[2 * i + 1]);
+        } else {
+            acc[i] = fmaf(w, __uint_as_float(q[i]), acc[i]);
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void add_vec(float *acc, u32x4 q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+            acc[2 * i] += bf16_lo(q[i]);
+            acc[2 * i + 1] += bf16_hi(q[i]);
+        } else {
+            acc[i] += __uint_as_float(q[i]);
+        }
+    }
+}
+
+// One block per token.  Wave 0 first compacts the token's kept
+// assignments (slot >= 0) into LDS in j order, so every thread then walks
+// only the rows it adds, with no per-j global loads; the sum order is the
+// j order either way.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     constexpr int VW = BF16 ? 8 : 4;
+    __shared__ int s_slot[MAX_K];
+    __shared__ float s_w[MAX_K];
+    __shared__ int s_n;
     const int t = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        int n = 0;
+        for (int j0 = 0; j0 < p.k; j0 += 64) {
+            const int j = j0 + lane;
+            const int s = j < p.k ? p.slot_of[(size_t)t * p.k + j] : -1;
+            const float w = j < p.k ? p.topk_w[(size_t)t * p.k + j] : 0.0f;
+            const unsigned long long m = __ballot(s >= 0);
+            if (s >= 0) {
+                const int pos = n + __popcll(m & lt);
+                s_slot[pos] = s;
+                s_w[pos] = w;
+            }
+            n += __popcll(m);
+        }
+        if (lane == 0) s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n;
     const int nv = p.d / VW;
-    int slots[8];
-    float wts[8];
-    const int kk = p.k;
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
         float acc[VW];
 #pragma unroll
         for (int i = 0; i < VW; ++i) acc[i] = 0.0f;
-        for (int j0 = 0; j0 < kk; j0 += 8) {
-            const int nj = min(8, kk - j0);
-            for (int j = 0; j < nj; ++j) {
-                slots[j] = p.slot_of[(size_t)t * kk + j0 + j];
-                wts[j] = p.topk_w[(size_t)t * kk + j0 + j];
-            }
-            for (int j = 0; j < nj; ++j) {
-                const int s = slots[j];
-                if (s < 0) continue;
-                const float w = wts[j];
-                if (BF16) {
-                    const uint4 q = *((const uint4 *)((const uint16_t *)p.yp +
-                                                      (size_t)s * p.d) + v);
-                    acc[0] = fmaf(w, bf16_lo(q.x), acc[0]);
-                    acc[1] = fmaf(w, bf16_hi(q.x), acc[1]);
-                    acc[2] = fmaf(w, bf16_lo(q.y), acc[2]);
-                    acc[3] = fmaf(w, bf16_hi(q.y), acc[3]);
-                    acc[4] = fmaf(w, bf16_lo(q.z), acc[4]);
-                    acc[5] = fmaf(w, bf16_hi(q.z), acc[5]);
-                    acc[6] = fmaf(w, bf16_lo(q.w), acc[6]);
-                    acc[7] = fmaf(w, bf16_hi(q.w), acc[7]);
-                } else {
-                    const float4 q = *((const float4 *)((const float *)p.yp +
-                                                        (size_t)s * p.d) + v);
-                    acc[0] = fmaf(w, q.x, acc[0]);
-                    acc[1] = fmaf(w, q.y, acc[1]);
-                    acc[2] = fmaf(w, q.z, acc[2]);
-                    acc[3] = fmaf(w, q.w, acc[3]);
-                }
-            }
+        // four rows in flight, added in order
+        int i = 0;
+        for (; i + 4 <= n; i += 4) {
+            u32x4 q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                q[u] = load_vec<BF16>(p.yp, (size_t)s_slot[i + u] * p.d, v);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) fma_vec<BF16>(acc, s_w[i + u], q[u]);
         }
-        if (p.n_shared) {
-            const size_t srow = (size_t)(p.shared_base + t) * p.d;
-            if (BF16) {
-                const uint4 q = *((const uint4 *)((const uint16_t *)p.yp + srow) + v);
-                acc[0] += bf16_lo(q.x);
-                acc[1] += bf16_hi(q.x);
-                acc[2] += bf16_lo(q.y);
-                acc[3] += bf16_hi(q.y);
-                acc[4] += bf16_lo(q.z);
-                acc[5] += bf16_hi(q.z);
-                acc[6] += bf16_lo(q.w);
-                acc[7] += bf16_hi(q.w);
-            } else {
-                const float4 q = *((const float4 *)((const float *)p.yp + srow) + v);
-                acc[0] += q.x;
-                acc[1] += q.y;
-                acc[2] += q.z;
-                acc[3] += q.w;
-            }
-        }
+        for (; i < n; ++i)
+            fma_vec<BF16>(acc, s_w[i],
+                          load_vec<BF16>(p.yp, (size_t)s_slot[i] * p.d, v));
+        if (p.n_shared)
+            add_vec<BF16>(acc, load_vec<BF16>(
+                p.yp, (size_t)(p.shared_base + t) * p.d, v));
         if (BF16) {
-            uint4 o;
-            o.x = pack_bf16x2(acc[0], acc[1]);
-            o.y = pack_bf16x2(acc[2], acc[3]);
-            o.z = pack_bf16x2(acc[4], acc[5]);
-            o.w = pack_bf16x2(acc[6], acc[7]);
-            *((uint4 *)((uint16_t *)p.y + (size_t)t * p.d) + v) = o;
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+            *((u32x4 *)((uint16_t *)p.y + (size_t)t * p.d) + v) = o;
         } else {
             *((float4 *)((float *)p.y + (size_t)t * p.d) + v) =
                 make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -96,9 +119,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }  // namespace
 
 hipError_t launch_combine(const CombineParams &p, int dtype, hipStream_t s) {
+    // one 16-byte vector per thread where the row allows it
+    const int nv = p.d / (dtype == 1 ? 8 : 4);
+    const int threads = nv >= 256 ? 256 : (nv + 63) / 64 * 64;
     if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T), dim3(threads), 0, s, p);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T), dim3(threads), 0, s, p);
     return hipGetLastError();
 }

@@ -21,6 +21,8 @@ struct RouterParams {
     float *topk_w;        // [T][k]
     float *p_part;        // [ceil(T/32)][E]
     float *zh_part;       // [ceil(T/32)][2]: sum lse^2, sum entropy (nats)
+    float *scores;        // expert choice: logits [E][T]; null for top-k
+    int32_t *slot_of;     // expert choice: [T][E], set to -1 here
     int T, d, E, k;
 };
 
@@ -29,6 +31,7 @@ struct PermuteParams {
     const float *p_part;      // [n_rtiles][E]
     const float *zh_part;     // [n_rtiles][2]
     int32_t *blk;             // [n_chunks][E] scratch
+    const float *scores;      // expert choice: logits [E][T]; else null
     int32_t *counts, *kept, *offsets, *slot_token, *slot_of;
     float *f, *p, *l_aux;
     float *monitor;           // [6] or null
@@ -66,6 +69,7 @@ GemmVariantInfo gemm_variant_info(int variant);
 
 hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s);
 hipError_t launch_permute(const PermuteParams &p, hipStream_t s);
+hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
                        hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int dtype, hipStream_t s);

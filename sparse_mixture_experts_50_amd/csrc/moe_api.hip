@@ -15,24 +15,40 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t p_part, zh_part, blk, h, yp, total;
+    size_t p_part, zh_part, blk, scores, h, yp, total;
     int n_rtiles, n_chunks;
     size_t rows;
 };
 
 int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 
+bool expert_choice(const moe_desc *d) {
+    return d->routing == MOE_ROUTE_EXPERT_CHOICE;
+}
+
+// Routed expert rows: T*k assignments, or E*C picks for expert choice.
+long long routed_rows(const moe_desc *d) {
+    return expert_choice(d) ? (long long)d->E * d->capacity
+                            : (long long)d->T * d->k;
+}
+
 int check_desc(const moe_desc *d) {
     if (!d) return MOE_ERR_INVALID_ARG;
     if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->d < 1 ||
         d->d_ff < 1 || d->capacity < -1 ||
-        (d->n_shared != 0 && d->n_shared != 1))
+        (d->n_shared != 0 && d->n_shared != 1) ||
+        (d->routing != MOE_ROUTE_TOPK && !expert_choice(d)))
+        return MOE_ERR_INVALID_ARG;
+    if (expert_choice(d) &&
+        (d->k != d->E || d->capacity < 0 || d->capacity > d->T))
         return MOE_ERR_INVALID_ARG;
     if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (d->E > MOE_MAX_E || d->k > 64) return MOE_ERR_UNSUPPORTED;
+    if (d->E > MOE_MAX_E || (!expert_choice(d) && d->k > 64))
+        return MOE_ERR_UNSUPPORTED;
     if (d->d % 64 != 0 || d->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
     // 32-bit element offsets inside the kernels
-    const double rows = (double)d->T * d->k + (double)d->n_shared * d->T;
+    if ((double)d->T * d->k >= 2147483647.0) return MOE_ERR_UNSUPPORTED;
+    const double rows = (double)routed_rows(d) + (double)d->n_shared * d->T;
     if (rows * d->d_ff >= 2147483647.0 || rows * d->d >= 2147483647.0 ||
         (double)d->d * d->d_ff >= 2147483647.0)
         return MOE_ERR_UNSUPPORTED;
@@ -43,9 +59,12 @@ WsLayout layout(const moe_desc *d) {
     WsLayout L;
     const size_t es = elem_bytes(d->dtype);
     L.n_rtiles = (d->T + MOE_ROUTER_TOKENS - 1) / MOE_ROUTER_TOKENS;
-    L.n_chunks = (int)(((size_t)d->T * d->k + MOE_PERMUTE_CHUNK - 1) /
-                       MOE_PERMUTE_CHUNK);
-    L.rows = (size_t)d->T * d->k + (size_t)d->n_shared * d->T;
+    // expert choice dispatches by per-expert selection, not by chunks
+    L.n_chunks = expert_choice(d)
+                     ? 0
+                     : (int)(((size_t)d->T * d->k + MOE_PERMUTE_CHUNK - 1) /
+                             MOE_PERMUTE_CHUNK);
+    L.rows = (size_t)routed_rows(d) + (size_t)d->n_shared * d->T;
     size_t off = 0;
     L.p_part = off;
     off += align_up((size_t)L.n_rtiles * d->E * sizeof(float));
@@ -53,6 +72,8 @@ WsLayout layout(const moe_desc *d) {
     off += align_up((size_t)L.n_rtiles * 2 * sizeof(float));
     L.blk = off;
     off += align_up((size_t)L.n_chunks * d->E * sizeof(int32_t));
+    L.scores = off;       // expert choice: logits transposed, [E][T] fp32
+    if (expert_choice(d)) off += align_up((size_t)d->E * d->T * sizeof(float));
     L.h = off;
     off += align_up(L.rows * d->d_ff * es);
     L.yp = off;
@@ -105,7 +126,7 @@ int variant_override(bool up, const moe_desc *d, int N) {
 int pick_variant(const moe_desc *d, int N) {
     if (d->dtype == MOE_F32) return GEMM_F32_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
-    const double avg = (double)d->T * d->k / d->E;
+    const double avg = (double)routed_rows(d) / d->E;
     // the streaming kernel splits K in four quarters of whole 128-deep
     // load batches
     if (avg <= 32.0 && d->d % 512 == 0 && d->d_ff % 512 == 0)
@@ -122,7 +143,7 @@ int gemm_grid(const moe_desc *d, int variant, int N) {
         const long long slots = (long long)device_cus() * 2;
         return (int)(units < slots ? units : slots);
     }
-    const long long mtiles = ((long long)d->T * d->k + vi.bm - 1) / vi.bm +
+    const long long mtiles = (routed_rows(d) + vi.bm - 1) / vi.bm +
                              d->E +
                              (long long)d->n_shared * ((d->T + vi.bm - 1) / vi.bm);
     const long long ub = mtiles * (N / vi.bn);
@@ -146,20 +167,25 @@ int check_weights_ffn(const moe_desc *d, const moe_weights *w) {
     return MOE_OK;
 }
 
-int check_routing_router(const moe_routing *r) {
+int check_routing_router(const moe_desc *d, const moe_routing *r) {
     if (!r || !r->topk_idx || !r->topk_w) return MOE_ERR_INVALID_ARG;
+    if (expert_choice(d) && !r->slot_of) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
-int check_routing_permute(const moe_routing *r) {
-    if (!r || !r->topk_idx || !r->counts || !r->kept || !r->offsets ||
-        !r->slot_token || !r->slot_of || !r->f || !r->p || !r->l_aux)
+// slot_token holds routed_rows() entries, so with no routed rows (expert
+// choice with C = 0) it may be NULL.
+int check_routing_permute(const moe_desc *d, const moe_routing *r) {
+    if (!r || (!r->topk_idx && !expert_choice(d)) || !r->counts ||
+        !r->kept || !r->offsets || (!r->slot_token && routed_rows(d) > 0) ||
+        !r->slot_of || !r->f || !r->p || !r->l_aux)
         return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
-int check_routing_ffn(const moe_routing *r) {
-    if (!r || !r->offsets || !r->slot_token) return MOE_ERR_INVALID_ARG;
+int check_routing_ffn(const moe_desc *d, const moe_routing *r) {
+    if (!r || !r->offsets || (!r->slot_token && routed_rows(d) > 0))
+        return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -177,7 +203,7 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
     p.E = d->E;
     p.n_shared = d->n_shared;
     p.T = d->T;
-    p.shared_base = d->T * d->k;
+    p.shared_base = (int)routed_rows(d);
     if (up) {
         p.A = x;
         p.W = w->w1;
@@ -233,7 +259,7 @@ int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
     if (desc->T == 0) return MOE_OK;
     if (!x) return MOE_ERR_INVALID_ARG;
     if ((st = check_weights_router(w)) != MOE_OK) return st;
-    if ((st = check_routing_router(r)) != MOE_OK) return st;
+    if ((st = check_routing_router(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     const WsLayout L = layout(desc);
     RouterParams p;
@@ -245,6 +271,8 @@ int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
     p.topk_w = r->topk_w;
     p.p_part = (float *)at(ws, L.p_part);
     p.zh_part = (float *)at(ws, L.zh_part);
+    p.scores = expert_choice(desc) ? (float *)at(ws, L.scores) : nullptr;
+    p.slot_of = r->slot_of;
     p.T = desc->T;
     p.d = desc->d;
     p.E = desc->E;
@@ -257,7 +285,7 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     int st = check_desc(desc);
     if (st != MOE_OK) return st;
     if (desc->T == 0) return MOE_OK;
-    if ((st = check_routing_permute(r)) != MOE_OK) return st;
+    if ((st = check_routing_permute(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     const WsLayout L = layout(desc);
     PermuteParams p;
@@ -265,6 +293,7 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     p.p_part = (const float *)at(ws, L.p_part);
     p.zh_part = (const float *)at(ws, L.zh_part);
     p.blk = (int32_t *)at(ws, L.blk);
+    p.scores = expert_choice(desc) ? (const float *)at(ws, L.scores) : nullptr;
     p.counts = r->counts;
     p.kept = r->kept;
     p.offsets = r->offsets;
@@ -281,6 +310,8 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     p.n_rtiles = L.n_rtiles;
     p.n_chunks = L.n_chunks;
     p.alpha = desc->aux_alpha;
+    if (expert_choice(desc))
+        return to_status(launch_expert_choice(p, (hipStream_t)stream));
     return to_status(launch_permute(p, (hipStream_t)stream));
 }
 
@@ -292,7 +323,7 @@ int moe_ffn_up(const moe_desc *desc, const void *x, const moe_weights *w,
     if (desc->T == 0) return MOE_OK;
     if (!x) return MOE_ERR_INVALID_ARG;
     if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
-    if ((st = check_routing_ffn(r)) != MOE_OK) return st;
+    if ((st = check_routing_ffn(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     return run_gemm(desc, w, r, true, x, ws, (hipStream_t)stream);
 }
@@ -304,7 +335,7 @@ int moe_ffn_down(const moe_desc *desc, const moe_weights *w,
     if (st != MOE_OK) return st;
     if (desc->T == 0) return MOE_OK;
     if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
-    if ((st = check_routing_ffn(r)) != MOE_OK) return st;
+    if ((st = check_routing_ffn(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     return run_gemm(desc, w, r, false, nullptr, ws, (hipStream_t)stream);
 }
@@ -335,7 +366,7 @@ int moe_combine(const moe_desc *desc, const moe_routing *r, void *y, void *ws,
     p.d = desc->d;
     p.k = desc->k;
     p.n_shared = desc->n_shared;
-    p.shared_base = desc->T * desc->k;
+    p.shared_base = (int)routed_rows(desc);
     return to_status(launch_combine(p, desc->dtype, (hipStream_t)stream));
 }
 
@@ -348,8 +379,8 @@ int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
     if (!x || !y) return MOE_ERR_INVALID_ARG;
     if ((st = check_weights_router(w)) != MOE_OK) return st;
     if ((st = check_weights_ffn(desc, w)) != MOE_OK) return st;
-    if ((st = check_routing_router(r)) != MOE_OK) return st;
-    if ((st = check_routing_permute(r)) != MOE_OK) return st;
+    if ((st = check_routing_router(desc, r)) != MOE_OK) return st;
+    if ((st = check_routing_permute(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
     if ((st = moe_router_topk(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
         return st;
@@ -378,6 +409,6 @@ const char *moe_status_string(int status) {
     }
 }
 
-const char *moe_version(void) { return "moe-gfx950 0.1.0"; }
+const char *moe_version(void) { return "moe-gfx950 0.2.0"; }
 
 }  // extern "C"

@@ -16,21 +16,25 @@
 //           equal experts, slot = offset + rank, overflow -> -1
 // Assignments are numbered a = t*k + j, so chunk order is token-major and
 // the resulting permutation is stable in (t, j).
+//
+// Expert choice ("AI-Research-SKILLs MoE training guide", sec. 4.2): every
+// token is a candidate of every expert (counts = T, k = E) and expert e
+// keeps its C largest logits instead of its first C tokens.  Two launches:
+//   scan    as above, with counts = T
+//   select  one block per expert: exact radix select of the C-th largest
+//           logit (passes of 11, 11 and 10 bits over order-preserving
+//           keys), then the picks in token order; equal keys go to the
+//           lower token index
 #include "kernels.h"
 
 namespace {
 
 constexpr int CH = MOE_PERMUTE_CHUNK;
 
-// The six monitors from counts and kept (thread 0 of the block; the
-// per-router-block lse^2 and entropy sums are reduced in block order).
-__device__ void write_monitor(const PermuteParams &p, const int *cnt_s,
-                              const int *kept_s) {
-    float z = 0.0f, h = 0.0f;
-    for (int b = 0; b < p.n_rtiles; ++b) {
-        z += p.zh_part[(size_t)b * 2];
-        h += p.zh_part[(size_t)b * 2 + 1];
-    }
+// The six monitors from counts, kept and the reduced router sums z, h
+// (thread 0 of the block).
+__device__ void write_monitor(const PermuteParams &p, float z, float h,
+                              const int *cnt_s, const int *kept_s) {
     int cmax = cnt_s[0], cmin = cnt_s[0], used = 0, kept = 0;
     for (int e = 0; e < p.E; ++e) {
         cmax = max(cmax, cnt_s[e]);
@@ -45,6 +49,18 @@ __device__ void write_monitor(const PermuteParams &p, const int *cnt_s,
     p.monitor[3] = (float)used / (float)p.E;
     p.monitor[4] = (n - (float)kept) / n;
     p.monitor[5] = (float)cmax / (float)p.T;
+}
+
+// Sum of the per-router-block lse^2 and entropy partials in block order
+// (single-block callers only; thread 0 gets the result).
+__device__ void sum_zh_serial(const PermuteParams &p, float *z, float *h) {
+    float zs = 0.0f, hs = 0.0f;
+    for (int b = 0; b < p.n_rtiles; ++b) {
+        zs += p.zh_part[(size_t)b * 2];
+        hs += p.zh_part[(size_t)b * 2 + 1];
+    }
+    *z = zs;
+    *h = hs;
 }
 
 __global__ __launch_bounds__(256) void permute_hist(PermuteParams p) {
@@ -65,72 +81,132 @@ __global__ __launch_bounds__(256) void permute_hist(PermuteParams p) {
         p.blk[(size_t)blockIdx.x * p.E + e] = h[e];
 }
 
-__global__ __launch_bounds__(256) void permute_scan(PermuteParams p) {
+// One block of 1024 threads, thread = (segment, expert): S = 1024 / E
+// segments split the chunk list and the router-block list, so each thread
+// walks n/S entries instead of n; partial results meet in LDS and are
+// summed in segment order (deterministic).
+constexpr int SCAN_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
+    __shared__ int seg_i[SCAN_THREADS];
+    __shared__ float seg_f[SCAN_THREADS];
+    __shared__ float zh_w[SCAN_THREADS / 64][2];
     __shared__ int kept_s[MOE_MAX_E];
     __shared__ int cnt_s[MOE_MAX_E];
     __shared__ float fp_s[MOE_MAX_E];
     __shared__ int wsum[4];
-    const int e = threadIdx.x;
-    int cnt = 0, kept = 0;
-    if (e < p.E) {
-        // batches of 8 independent loads keep the serial scans short
-        int b = 0;
-        for (; b + 8 <= p.n_chunks; b += 8) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int S = SCAN_THREADS / p.E;              // E <= 256: S >= 4
+    const int e = tid % p.E, seg = tid / p.E;
+    const bool active = seg < S;
+
+    // 1. chunk counts of expert e over this segment's chunks
+    const int L = (p.n_chunks + S - 1) / S;
+    const int c0 = min(p.n_chunks, seg * L), c1 = min(p.n_chunks, c0 + L);
+    int part = 0;
+    if (active) {
+        int b = c0;
+        for (; b + 8 <= c1; b += 8) {
             int v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                p.blk[(size_t)(b + u) * p.E + e] = cnt;  // rank base
-                cnt += v[u];
-            }
+            for (int u = 0; u < 8; ++u) part += v[u];
         }
-        for (; b < p.n_chunks; ++b) {
-            const size_t i = (size_t)b * p.E + e;
-            const int v = p.blk[i];
-            p.blk[i] = cnt;           // rank base of expert e in chunk b
-            cnt += v;
-        }
-        kept = (p.capacity >= 0 && cnt > p.capacity) ? p.capacity : cnt;
-        p.counts[e] = cnt;
-        p.kept[e] = kept;
+        for (; b < c1; ++b) part += p.blk[(size_t)b * p.E + e];
+        seg_i[seg * p.E + e] = part;
+    }
+    // 2. probability column sums over this segment's router blocks
+    if (active) {
         float ps = 0.0f;
-        b = 0;
-        for (; b + 8 <= p.n_rtiles; b += 8) {
+        int b = seg;
+        for (; b + 7 * S < p.n_rtiles; b += 8 * S) {
             float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = p.p_part[(size_t)(b + u) * p.E + e];
+            for (int u = 0; u < 8; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
 #pragma unroll
             for (int u = 0; u < 8; ++u) ps += v[u];
         }
-        for (; b < p.n_rtiles; ++b) ps += p.p_part[(size_t)b * p.E + e];
+        for (; b < p.n_rtiles; b += S) ps += p.p_part[(size_t)b * p.E + e];
+        seg_f[seg * p.E + e] = ps;
+    }
+    // 3. router z / entropy partials: all threads, then waves in order
+    float zs = 0.0f, hs = 0.0f;
+    if (p.monitor) {
+        for (int b = tid; b < p.n_rtiles; b += SCAN_THREADS) {
+            zs += p.zh_part[(size_t)b * 2];
+            hs += p.zh_part[(size_t)b * 2 + 1];
+        }
+        zs = wave_sum(zs);
+        hs = wave_sum(hs);
+        if (lane == 0) {
+            zh_w[wave][0] = zs;
+            zh_w[wave][1] = hs;
+        }
+    }
+    __syncthreads();
+    // 4. rank bases: the segment's base plus a running count over its chunks
+    if (active && p.n_chunks > 0) {
+        int run = 0;
+        for (int q = 0; q < seg; ++q) run += seg_i[q * p.E + e];
+        for (int b = c0; b < c1; ++b) {
+            const size_t i = (size_t)b * p.E + e;
+            const int v = p.blk[i];
+            p.blk[i] = run;               // rank base of expert e in chunk b
+            run += v;
+        }
+    }
+    // 5. per expert (threads 0..E-1): counts, kept, f, p
+    int cnt = 0, kept = 0;
+    if (tid < p.E) {
+        if (p.scores) {
+            cnt = p.T;                    // expert choice: every token
+        } else {
+            for (int q = 0; q < S; ++q) cnt += seg_i[q * p.E + tid];
+        }
+        float ps = 0.0f;
+        for (int q = 0; q < S; ++q) ps += seg_f[q * p.E + tid];
+        kept = (p.capacity >= 0 && cnt > p.capacity) ? p.capacity : cnt;
+        p.counts[tid] = cnt;
+        p.kept[tid] = kept;
         const float pe = ps / (float)p.T;
         const float fe = (float)cnt / ((float)p.T * (float)p.k);
-        p.p[e] = pe;
-        p.f[e] = fe;
-        fp_s[e] = fe * pe;
+        p.p[tid] = pe;
+        p.f[tid] = fe;
+        fp_s[tid] = fe * pe;
+        kept_s[tid] = kept;
+        cnt_s[tid] = cnt;
     }
-    kept_s[e] = kept;
-    cnt_s[e] = cnt;
-    // exclusive scan of kept over experts (256 threads = 4 waves)
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // 6. offsets: exclusive scan of kept over experts (waves 0-3)
     int incl = kept;
+    if (tid < 256) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
     }
-    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (e < p.E) p.offsets[e] = before + incl - kept;
-    if (e == p.E - 1) p.offsets[p.E] = before + incl;
-    if (threadIdx.x == 0) {
-        float s = 0.0f;
-        for (int i = 0; i < p.E; ++i) s += fp_s[i];
-        p.l_aux[0] = p.alpha * (float)p.E * s;
-        if (p.monitor) write_monitor(p, cnt_s, kept_s);
+    if (tid < p.E) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        p.offsets[tid] = before + incl - kept;
+        if (tid == p.E - 1) p.offsets[p.E] = before + incl;
+    }
+    if (tid == 0) {
+        float sfp = 0.0f;
+        for (int i = 0; i < p.E; ++i) sfp += fp_s[i];
+        p.l_aux[0] = p.alpha * (float)p.E * sfp;
+        if (p.monitor) {
+            float z = 0.0f, h = 0.0f;
+            for (int w = 0; w < SCAN_THREADS / 64; ++w) {
+                z += zh_w[w][0];
+                h += zh_w[w][1];
+            }
+            write_monitor(p, z, h, cnt_s, kept_s);
+        }
     }
 }
 
@@ -237,7 +313,11 @@ __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
         float s = 0.0f;
         for (int i = 0; i < p.E; ++i) s += fp_s[i];
         p.l_aux[0] = p.alpha * (float)p.E * s;
-        if (p.monitor) write_monitor(p, cnt_s, kept_s);
+        if (p.monitor) {
+            float z, h;
+            sum_zh_serial(p, &z, &h);
+            write_monitor(p, z, h, cnt_s, kept_s);
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -275,6 +355,156 @@ __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
         if (sl >= off_s[p.E]) p.slot_token[sl] = -1;
 }
 
+// Float -> unsigned key with the same order (-0 is ranked with +0, as
+// the two compare equal).
+__device__ __forceinline__ unsigned order_key(float v) {
+    unsigned u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int EC_THREADS = 1024;
+constexpr int EC_WAVES = EC_THREADS / 64;
+constexpr int EC_KR = 8;          // keys per lane kept in registers
+constexpr int EC_BINS = 2048;     // 11-bit digits: passes of 11, 11, 10 bits
+
+// One 64-token step of a wave's in-order pick emission: keys above thr
+// are picked, equal keys while fewer than `need` equal ones came before.
+// sb / eb count the picks and the equal keys before this step.
+__device__ __forceinline__ void ec_pick_step(const PermuteParams &p, int e,
+                                             int C, unsigned thr, int need,
+                                             int t, bool in, unsigned u,
+                                             int &sb, int &eb) {
+    const int lane = threadIdx.x & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const bool gt = in && u > thr;
+    const bool eq = in && u == thr;
+    const unsigned long long em = __ballot(eq);
+    const bool sel = gt || (eq && eb + __popcll(em & lt) < need);
+    const unsigned long long sm = __ballot(sel);
+    if (sel) {
+        const int slot = e * C + sb + __popcll(sm & lt);
+        p.slot_token[slot] = t;
+        p.slot_of[(size_t)t * p.E + e] = slot;
+    }
+    sb += __popcll(sm);
+    eb += __popcll(em);
+}
+
+// Expert choice, block e: wave w owns the contiguous token segment
+// [w*L, (w+1)*L) (L a multiple of 64) and lane l its tokens w*L + 64i + l.
+// Keys of the first EC_KR*1024 tokens are staged in LDS; beyond that
+// (T > 8192) they are re-read.  The router has already set
+// slot_of[t][e] = -1 everywhere, so only the C picks are written here.
+__global__ __launch_bounds__(EC_THREADS) void ec_select(PermuteParams p) {
+    __shared__ unsigned keys[EC_KR * EC_THREADS];
+    __shared__ __attribute__((aligned(16))) int hist[EC_BINS];
+    __shared__ int w_gt[EC_WAVES], w_eq[EC_WAVES];
+    __shared__ unsigned s_digit;
+    __shared__ int s_need;
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = p.T, C = p.capacity;
+    if (C == 0) return;
+    const float *sc = p.scores + (size_t)e * T;
+    const int L = ((T + EC_WAVES - 1) / EC_WAVES + 63) / 64 * 64;
+    const int s0 = wave * L;
+    const int s1 = min(T, s0 + L);
+    const int n_i = L / 64;
+    const int n_r = min(n_i, EC_KR);      // 64-token steps staged in LDS
+    // LDS slot of step i of this lane (wave-private, so no barrier needed)
+    unsigned *kw = keys + wave * (EC_KR * 64) + lane;
+    for (int i = 0; i < n_r; ++i) {
+        const int t = s0 + 64 * i + lane;
+        kw[64 * i] = t < s1 ? order_key(sc[t]) : 0u;
+    }
+
+    // thr = the C-th largest key; need = how many keys equal to thr are
+    // picked (every key above thr is).  Invariant of each pass: at least
+    // `need` keys match `prefix` on the bits fixed so far.
+    unsigned prefix = 0, mask = 0;
+    int need = C;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+        const unsigned dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+        for (int i = tid; i < EC_BINS; i += EC_THREADS) hist[i] = 0;
+        __syncthreads();
+        for (int i = 0; i < n_i; ++i) {
+            const int t = s0 + 64 * i + lane;
+            if (t < s1) {
+                const unsigned u = i < n_r ? kw[64 * i] : order_key(sc[t]);
+                if ((u & mask) == prefix)
+                    atomicAdd(&hist[(u >> shift) & dmask], 1);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds bins [2016-32l, 2047-32l], scanned high to low
+            const int lo = EC_BINS - 32 - 32 * lane;
+            int sum = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int4 v = *(const int4 *)&hist[lo + 4 * q];
+                sum += v.x + v.y + v.z + v.w;
+            }
+            int incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            int before = incl - sum;
+            if (before < need && need <= incl) {   // exactly one lane
+                for (int j = 31; j >= 0; --j) {
+                    const int c = hist[lo + j];
+                    if (need <= before + c) {
+                        s_digit = (unsigned)(lo + j);
+                        s_need = need - before;
+                        break;
+                    }
+                    before += c;
+                }
+            }
+        }
+        __syncthreads();
+        // s_digit / s_need are rewritten only after the next pass's
+        // histogram barrier, which every thread reaches after this read
+        prefix |= s_digit << shift;
+        mask |= dmask << shift;
+        need = s_need;
+    }
+
+    // picks in token order: count per wave, one barrier, then every wave
+    // emits its own segment
+    int n_gt = 0, n_eq = 0;
+    for (int i = 0; i < n_i; ++i) {
+        const int t = s0 + 64 * i + lane;
+        const bool in = t < s1;
+        const unsigned u = !in ? 0u : i < n_r ? kw[64 * i] : order_key(sc[t]);
+        n_gt += __popcll(__ballot(in && u > prefix));
+        n_eq += __popcll(__ballot(in && u == prefix));
+    }
+    if (lane == 0) {
+        w_gt[wave] = n_gt;
+        w_eq[wave] = n_eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0;
+    for (int w = 0; w < wave; ++w) {
+        gt_before += w_gt[w];
+        eq_before += w_eq[w];
+    }
+    int sb = gt_before + min(eq_before, need);   // picks before this wave
+    int eb = eq_before;                          // equal keys before it
+    for (int i = 0; i < n_i; ++i) {
+        const int t = s0 + 64 * i + lane;
+        const bool in = t < s1;
+        const unsigned u = !in ? 0u : i < n_r ? kw[64 * i] : order_key(sc[t]);
+        ec_pick_step(p, e, C, prefix, need, t, in, u, sb, eb);
+    }
+}
+
 __global__ void bias_update_kernel(int E, const int32_t *counts, float target,
                                    float gamma, float *bias) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -295,10 +525,18 @@ hipError_t launch_permute(const PermuteParams &p, hipStream_t s) {
     hipLaunchKernelGGL(permute_hist, dim3(p.n_chunks), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_scatter, dim3(p.n_chunks), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s) {
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(ec_select, dim3(p.E), dim3(EC_THREADS), 0, s, p);
     return hipGetLastError();
 }
 

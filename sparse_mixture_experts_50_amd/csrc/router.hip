@@ -12,6 +12,12 @@
 // selection compares fp32 logits (softmax is monotonic), ties to the lower
 // expert index.  Each block also writes its column sums of the softmax
 // probabilities, reduced later in a fixed order for p_i.
+//
+// Expert choice ("AI-Research-SKILLs MoE training guide", sec. 4.2): no
+// top-k; every token writes the probabilities of all E experts and resets
+// its slot row to -1, and the block writes its logits transposed to [E][T]
+// (32 consecutive tokens per expert row), the layout in which each expert
+// later ranks its column.
 #include "kernels.h"
 
 namespace {
@@ -81,6 +87,19 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
         zsum += lse * lse;
         hsum += lnS - wave_sum(pl) / S;
 
+        if (p.scores) {          // expert choice: all experts, weight p
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int e = lane + 64 * i;
+                if (valid[i]) {
+                    p.topk_idx[(size_t)t * p.E + e] = e;
+                    p.topk_w[(size_t)t * p.E + e] = ex[i] / S;
+                    p.slot_of[(size_t)t * p.E + e] = -1;  // picks come later
+                }
+            }
+            continue;
+        }
+
         // top-k: k rounds of a wave-wide (max logit, min index) search
         bool taken[PER];
 #pragma unroll
@@ -145,6 +164,20 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
 #pragma unroll
         for (int w = 1; w < RW; ++w) s += pp[w][e];
         p.p_part[(size_t)blockIdx.x * p.E + e] = s;
+    }
+    if (p.scores) {
+        // the same additions in the same order as v[] above, so the
+        // scores equal the logits the softmax saw bit for bit
+        for (int i = threadIdx.x; i < p.E * RT; i += blockDim.x) {
+            const int e = i / RT, tl = i % RT, t = t0 + tl;
+            if (t >= p.T) continue;
+            float s = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s += lg[ks][tl][e];
+            s = s + (p.add ? p.add[e] : 0.0f);
+            s = s - (p.sub ? p.sub[e] : 0.0f);
+            p.scores[(size_t)e * p.T + t] = s;
+        }
     }
 }
 

@@ -18,6 +18,8 @@ from . import _lib
 from ._lib import MoeDesc, MoeRouting, MoeWeights, check
 
 _DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+_ROUTING = {"topk": _lib.MOE_ROUTE_TOPK,
+            "expert_choice": _lib.MOE_ROUTE_EXPERT_CHOICE}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -48,11 +50,15 @@ def _opt(t, name, shape, dtype, device):
 
 def make_desc(T: int, d: int, E: int, k: int, d_ff: int, dtype: torch.dtype,
               n_shared: int = 0, capacity: int = -1,
-              aux_alpha: float = 0.01) -> MoeDesc:
+              aux_alpha: float = 0.01, routing: str = "topk") -> MoeDesc:
+    """``routing`` is "topk" or "expert_choice" (then k must be E and
+    capacity the tokens each expert picks)."""
     if dtype not in _DT:
         raise ValueError(f"unsupported dtype {dtype}")
+    if routing not in _ROUTING:
+        raise ValueError(f"unknown routing {routing!r}")
     return MoeDesc(T, d, E, k, d_ff, n_shared, _DT[dtype], capacity,
-                   aux_alpha)
+                   aux_alpha, _ROUTING[routing])
 
 
 def moe_capacity(T: int, E: int, capacity_factor: Optional[float]) -> int:
@@ -119,9 +125,13 @@ class Weights:
 
 
 class Routing:
-    """Device buffers of the routing results and statistics."""
+    """Device buffers of the routing results and statistics (k = E for
+    expert choice)."""
 
-    def __init__(self, T: int, E: int, k: int, device):
+    def __init__(self, T: int, E: int, k: int, device,
+                 slots: Optional[int] = None):
+        """``slots``: length of slot_token, T*k by default (expert choice
+        uses E*C)."""
         i32, f32 = torch.int32, torch.float32
         z = lambda *s, dt: torch.empty(s, dtype=dt, device=device)
         self.topk_idx = z(T, k, dt=i32)
@@ -129,7 +139,7 @@ class Routing:
         self.counts = z(E, dt=i32)
         self.kept = z(E, dt=i32)
         self.offsets = z(E + 1, dt=i32)
-        self.slot_token = z(T * k, dt=i32)
+        self.slot_token = z(T * k if slots is None else slots, dt=i32)
         self.slot_of = z(T, k, dt=i32)
         self.f = z(E, dt=f32)
         self.p = z(E, dt=f32)
@@ -226,31 +236,48 @@ def moe_bias_update(counts, target: float, gamma: float,
 class MoeLayer:
     """One sparse MoE FFN layer on a GPU: weights plus reusable buffers.
 
+    ``routing="topk"``: each token picks ``k`` experts, with an optional
+    capacity floor(T/E * capacity_factor).  ``routing="expert_choice"``:
+    each expert picks floor(T/E * capacity_factor) tokens (``k`` is then E
+    and a capacity factor is required).
+
     ``forward(x)`` returns ``(y, routing)``; the routing buffers are reused
     by the next call with the same T (copy them to keep them)."""
 
     def __init__(self, weights: Weights, k: int,
                  capacity_factor: Optional[float] = None,
-                 aux_alpha: float = 0.01):
+                 aux_alpha: float = 0.01, routing: str = "topk"):
+        if routing not in _ROUTING:
+            raise ValueError(f"unknown routing {routing!r}")
+        if routing == "expert_choice":
+            if capacity_factor is None:
+                raise ValueError("expert choice needs a capacity factor")
+            k = weights.E
         self.w = weights
         self.k = k
         self.capacity_factor = capacity_factor
         self.aux_alpha = aux_alpha
+        self.routing = routing
         self._bufs = {}
 
     def desc(self, T: int) -> MoeDesc:
         w = self.w
         cap = moe_capacity(T, w.E, self.capacity_factor)
+        if self.routing == "expert_choice":
+            cap = min(cap, T)
         return make_desc(T, w.d, w.E, self.k, w.d_ff, w.dtype,
                          n_shared=w.n_shared, capacity=cap,
-                         aux_alpha=self.aux_alpha)
+                         aux_alpha=self.aux_alpha, routing=self.routing)
 
     def buffers(self, T: int):
         if T not in self._bufs:
             desc = self.desc(T)
             nbytes = moe_workspace_size(desc)
             ws = torch.empty(nbytes, dtype=torch.uint8, device=self.w.device)
-            r = Routing(T, self.w.E, self.k, self.w.device)
+            slots = None
+            if self.routing == "expert_choice":
+                slots = self.w.E * desc.capacity
+            r = Routing(T, self.w.E, self.k, self.w.device, slots=slots)
             y = torch.empty((T, self.w.d), dtype=self.w.dtype,
                             device=self.w.device)
             self._bufs[T] = (desc, r, ws, y)

@@ -40,7 +40,8 @@ def gpu_forward(w: workloads.Workload, inp: dict, steps: bool = False):
     """Run the layer through the C ABI.  ``steps`` calls the five entry
     points one by one instead of moe_forward."""
     weights = moe.Weights.from_dict(inp)
-    layer = moe.MoeLayer(weights, w.k, w.capacity_factor, w.alpha)
+    layer = moe.MoeLayer(weights, w.k, w.capacity_factor, w.alpha,
+                         routing=w.routing)
     x = inp["x"]
     if steps:
         desc, r, ws, y = layer.buffers(x.shape[0])
@@ -141,4 +142,83 @@ def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
                   rel=float(err / scale) if scale else 0.0,
                   rows=len(tokens))
     assert err <= tol, report
+    return report
+
+
+LOGIT_MARGIN = 1e-4
+
+
+def check_expert_choice(w: workloads.Workload, inp: dict, gpu: dict,
+                        tokens=None) -> dict:
+    """Expert-Choice rules, mirroring :func:`check_layer`:
+      * each expert's picks are C distinct tokens in ascending order;
+      * a token whose logit is more than 1e-4 above (below) the expert's
+        C-th largest oracle logit must (must not) be picked; tokens nearer
+        the threshold may go either way, and the GPU's picks are then
+        adopted by a conditioned oracle;
+      * slot_of, counts, kept, offsets equal the conditioned oracle's bit
+        for bit; topk_idx is the identity; topk_w the probabilities;
+      * statistics, monitors and outputs as for top-k routing."""
+    T = inp["x"].shape[0]
+    E = w.E
+    C = moe.moe_capacity(T, E, w.capacity_factor)
+    C = min(C, T)
+    ref = oracle.forward_expert_choice(inp, C, w.alpha,
+                                       tokens=np.arange(0, dtype=np.int32))
+    logits, probs = ref["logits"], ref["probs"]
+    st = gpu["slot_token"].reshape(-1)[:E * C]
+    undecided = 0
+    flips = 0
+    for e in range(E):
+        got = st[e * C:(e + 1) * C]
+        assert np.all(got >= 0) and np.all(got < T), e
+        assert np.all(np.diff(got) > 0), f"expert {e}: picks not ascending"
+        if C == 0:
+            continue
+        col = logits[:, e]
+        thr = np.sort(col)[::-1][C - 1]
+        picked = np.zeros(T, bool)
+        picked[got] = True
+        must = col > thr + LOGIT_MARGIN
+        never = col < thr - LOGIT_MARGIN
+        assert np.all(picked[must]), (e, np.nonzero(must & ~picked)[0][:5])
+        assert not np.any(picked[never]), (e, np.nonzero(never & picked)[0][:5])
+        undecided += int(np.count_nonzero(~must & ~never))
+        want = ref["slot_token"][e * C:(e + 1) * C]
+        flips += int(np.count_nonzero(np.setdiff1d(got, want)))
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    cond = oracle.forward_expert_choice(inp, C, w.alpha, tokens=tokens,
+                                        selection=st)
+    so = gpu["slot_of"].reshape(T, -1)
+    assert so.shape[1] == E
+    assert np.array_equal(so, cond["slot_of"]), "slot_of"
+    for key in ("counts", "kept", "offsets"):
+        assert np.array_equal(gpu[key].reshape(-1), cond[key]), key
+    assert np.array_equal(gpu["topk_idx"].reshape(T, E),
+                          np.tile(np.arange(E, dtype=np.int32), (T, 1)))
+    assert np.max(np.abs(gpu["topk_w"].reshape(T, E) - probs)) <= \
+        W_TOL[w.dtype]
+    assert np.allclose(gpu["f"], cond["f"], rtol=1e-6, atol=1e-9)
+    assert np.allclose(gpu["p"], cond["p"], rtol=1e-4, atol=2e-6)
+    assert abs(gpu["l_aux"][0] - cond["l_aux"]) <= \
+        1e-4 * abs(cond["l_aux"]) + 1e-7
+    g = gpu["monitor"].astype(np.float64)
+    mon = cond["monitor"]
+    assert abs(g[0] - mon[0]) <= 1e-4 * abs(mon[0]) + 1e-6, (g, mon)
+    assert abs(g[1] - mon[1]) <= 2e-4, (g, mon)
+    assert np.allclose(g[2:], mon[2:], rtol=1e-6, atol=1e-7), (g, mon)
+    y_ref = cond["y"]
+    y_gpu = gpu["y"][tokens]
+    scale = np.max(np.abs(y_ref)) if y_ref.size else 0.0
+    err = np.max(np.abs(y_gpu - y_ref)) if y_ref.size else 0.0
+    if w.n_shared == 0:
+        unpicked = cond["picks"][tokens] == 0
+        assert np.all(y_gpu[unpicked] == 0.0)
+    report = dict(T=T, C=C, undecided=undecided, flips=flips,
+                  max_err=float(err), scale=float(scale),
+                  rel=float(err / scale) if scale else 0.0,
+                  rows=len(tokens),
+                  unpicked=int(np.count_nonzero(cond["picks"] == 0)))
+    assert err <= TOL[w.dtype] * scale, report
     return report

@@ -74,6 +74,11 @@ def desc(**kw):
     (dict(d_ff=96), _lib.MOE_ERR_UNSUPPORTED),
     (dict(E=300, k=2), _lib.MOE_ERR_UNSUPPORTED),
     (dict(E=128, k=65), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(routing=2), _lib.MOE_ERR_INVALID_ARG),
+    # expert choice: k must be E, 0 <= capacity <= T
+    (dict(routing=1, k=2, capacity=16), _lib.MOE_ERR_INVALID_ARG),
+    (dict(routing=1, k=8, capacity=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(routing=1, k=8, capacity=65), _lib.MOE_ERR_INVALID_ARG),
 ])
 def test_descriptor_rejected_before_any_launch(kw, status):
     L = _lib.lib()
@@ -150,6 +155,25 @@ def test_workspace_grows_with_tokens():
     b = L.moe_workspace_size(ctypes.byref(desc(T=4096)))
     c = L.moe_workspace_size(ctypes.byref(desc(T=4096, n_shared=1)))
     assert 0 < a < b < c
+
+
+def test_expert_choice_descriptor_and_workspace():
+    L = _lib.lib()
+    # k = E = 128 > 64 is fine for expert choice
+    big = desc(routing=1, E=128, k=128, capacity=16)
+    assert L.moe_workspace_size(ctypes.byref(big)) > 0
+    # the routed rows are E*C, not T*k: fewer than top-k with k = E
+    a = L.moe_workspace_size(ctypes.byref(desc(routing=1, k=8, capacity=16)))
+    b = L.moe_workspace_size(ctypes.byref(desc(routing=1, k=8, capacity=32)))
+    assert 0 < a < b
+    assert L.moe_workspace_size(ctypes.byref(desc(k=8))) > b
+    # topk_idx is not needed by the expert-choice permute, but T = 0 is
+    # still a no-op and a missing slot map is still rejected
+    d = desc(routing=1, k=8, capacity=16)
+    ws = L.moe_workspace_size(ctypes.byref(d))
+    r = _lib.MoeRouting(*([FAKE] * 6 + [None] + [FAKE] * 3))
+    assert L.moe_permute(ctypes.byref(d), ctypes.byref(r), FAKE, ws,
+                         None) == -1
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

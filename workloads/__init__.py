@@ -51,6 +51,7 @@ class Workload:
     bias_var: float = 0.01       # variance of every Linear bias
     bias_update_gamma: Optional[float] = None  # one balancing-bias step
     calls: int = 1              # distinct x per timed run (decode)
+    routing: str = "topk"       # "topk" | "expert_choice" (then k == E)
     seed: int = 0
 
     @property
@@ -83,6 +84,12 @@ WORKLOADS: Dict[str, Workload] = {
     "deepseek_v3": Workload(
         name="deepseek_v3", T=8192, d=7168, E=256, k=8, d_ff=2048,
         dtype="bf16", n_shared=1, expert_bias="zipf", bias_update_gamma=0.001),
+    # Expert choice: each of 64 experts picks C = floor(T/E * 2) = 256
+    # tokens, the compute of top-2 routing on the Switch-sized layer.
+    "expert_choice_c2": Workload(
+        name="expert_choice_c2", T=8192, d=768, E=64, k=64, d_ff=3072,
+        dtype="bf16", capacity_factor=2.0, router_bias="skew", skew_var=1.0,
+        routing="expert_choice"),
 }
 
 
