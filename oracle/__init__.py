@@ -60,15 +60,20 @@ def lib():
             _f64p, _i32p, ctypes.c_double, _f64p, _f64p, _f64p]
         L.oracle_layer_rows.restype = ctypes.c_int
         L.oracle_layer_rows.argtypes = [ctypes.c_int, _i32p] + \
-            [ctypes.c_int] * 4 + [_vp, _i32p, _f64p, _i32p] + \
+            [ctypes.c_int] * 5 + [_vp, _i32p, _f64p, _i32p] + \
             [ctypes.POINTER(_vp)] * 4 + [_vp] * 4 + [_f64p]
         L.oracle_expert_choice.restype = ctypes.c_int
         L.oracle_expert_choice.argtypes = [ctypes.c_int] * 3 + [
             _f64p, _f64p, _i32p, _i32p, _f64p, _i32p]
         L.oracle_expert_choice_rows.restype = ctypes.c_int
         L.oracle_expert_choice_rows.argtypes = [ctypes.c_int, _i32p] + \
-            [ctypes.c_int] * 4 + [_vp, _f64p] + [ctypes.POINTER(_vp)] * 4 + \
+            [ctypes.c_int] * 5 + [_vp, _f64p] + [ctypes.POINTER(_vp)] * 4 + \
             [_vp] * 4 + [_f64p]
+        L.oracle_fp8_e4m3.restype = ctypes.c_double
+        L.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_dequant.restype = None
+        L.oracle_fp8_dequant.argtypes = [ctypes.c_int, ctypes.c_int, _vp,
+                                         _f32p, _f64p]
         L.oracle_monitor.restype = None
         L.oracle_monitor.argtypes = [ctypes.c_int] * 3 + [_f64p, _f64p, _i32p,
                                                           _i32p, _f64p]
@@ -81,8 +86,9 @@ def lib():
 
 # ---------------------------------------------------------------- marshal
 def _raw(a):
-    """(contiguous numpy array, dtype code) of a float32 / bfloat16 input.
-    dtype code 0 = float32 words, 1 = bfloat16 bit patterns."""
+    """(contiguous numpy array, dtype code) of a float32 / bfloat16 /
+    float64 input.  dtype code 0 = float32 words, 1 = bfloat16 bit
+    patterns, 3 = float64 (dequantised weights)."""
     if a is None:
         return None, None
     try:
@@ -96,6 +102,8 @@ def _raw(a):
                                             .view(np.uint16)), 1
             if a.dtype == torch.float32:
                 return np.ascontiguousarray(a.numpy()), 0
+            if a.dtype == torch.float64:
+                return np.ascontiguousarray(a.numpy()), 3
             raise TypeError(f"unsupported tensor dtype {a.dtype}")
     except ImportError:
         pass
@@ -104,6 +112,8 @@ def _raw(a):
         return np.ascontiguousarray(a), 1
     if a.dtype == np.float32:
         return np.ascontiguousarray(a), 0
+    if a.dtype == np.float64:
+        return np.ascontiguousarray(a), 3
     raise TypeError(f"unsupported array dtype {a.dtype}")
 
 
@@ -201,6 +211,35 @@ def stats(probs: np.ndarray, counts: np.ndarray, k: int, alpha: float):
     return f, p, float(l[0])
 
 
+def fp8_e4m3(codes) -> np.ndarray:
+    """float64 values of OCP E4M3 codes (uint8 array)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    f = np.vectorize(lambda b: lib().oracle_fp8_e4m3(int(b)), otypes=[float])
+    return f(c)
+
+
+def fp8_dequant(q, scale) -> np.ndarray:
+    """w[n][c] = e4m3(q[n][c]) * scale[n], float64 [N][K].  ``q`` is a
+    uint8 (or float8_e4m3fn) tensor or array [N][K], ``scale`` float32 [N]."""
+    try:
+        import torch
+        if isinstance(q, torch.Tensor):
+            q = q.detach().cpu()
+            if q.dtype != torch.uint8:
+                q = q.view(torch.uint8)
+            q = q.numpy()
+    except ImportError:
+        pass
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+    sc = _f32(scale)
+    N, K = q.shape
+    assert sc.shape == (N,)
+    w = np.empty((N, K), np.float64)
+    lib().oracle_fp8_dequant(N, K, q.ctypes.data, _p(sc, _f32p),
+                             _p(w, _f64p))
+    return w
+
+
 class Experts:
     """Per-expert weights for :func:`layer_rows`.
 
@@ -218,38 +257,76 @@ class Experts:
         return Experts(E, lambda e: (w1[e], None if b1 is None else b1[e],
                                      w2[e], None if b2 is None else b2[e]))
 
+    @staticmethod
+    def fp8(w1, s1, b1, w2, s2, b2):
+        """FP8 expert matrices with per-output-channel scales, dequantised
+        one expert at a time."""
+        E = w1.shape[0]
+        return Experts(E, lambda e: (
+            fp8_dequant(w1[e], s1[e]), None if b1 is None else b1[e],
+            fp8_dequant(w2[e], s2[e]), None if b2 is None else b2[e]))
+
+
+def experts_of(inp: dict) -> Experts:
+    """The routed experts of an input dict (FP8 when it carries scales)."""
+    if inp.get("w1_scale") is not None:
+        return Experts.fp8(inp["w1"], inp["w1_scale"], inp.get("b1"),
+                           inp["w2"], inp["w2_scale"], inp.get("b2"))
+    return Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
+                           inp.get("b2"))
+
+
+def shared_of(inp: dict):
+    """(Ws1, bs1, Ws2, bs2) of the shared expert, or None."""
+    if inp.get("ws1") is None:
+        return None
+    if inp.get("ws1_scale") is not None:
+        return (fp8_dequant(inp["ws1"], inp["ws1_scale"]), inp.get("bs1"),
+                fp8_dequant(inp["ws2"], inp["ws2_scale"]), inp.get("bs2"))
+    return (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+
 
 def _weight_tables(need, experts: Experts, dt: int, shared):
     """Pointer tables (w1, b1, w2, b2) over the experts in ``need`` (None
     for an absent bias family), the shared expert's four pointers, d_ff,
+    the weight matrices' dtype code (x's, or 3 for dequantised float64),
     and the converted arrays that must stay alive during the call."""
     E = experts.E
     keep = []
     tabs = [(_vp * E)() for _ in range(4)]
     d_ff = None
+    wdt = set()
+
+    def put(i, a):
+        ra, rdt = _raw(a)
+        if ra is None:
+            return None
+        if i in (0, 2):
+            assert rdt in (dt, 3), "weights must be x's dtype or float64"
+            wdt.add(rdt)
+        else:
+            assert rdt == dt, "biases and x must share a dtype"
+        keep.append(ra)
+        return ra.ctypes.data
+
     for e in sorted(need):
         parts = experts.get(e)
         for i, a in enumerate(parts):
-            ra, rdt = _raw(a)
-            if ra is None:
-                continue
-            assert rdt == dt, "weights and x must share a dtype"
-            keep.append(ra)
-            tabs[i][e] = ra.ctypes.data
+            ptr = put(i, a)
+            if ptr is not None:
+                tabs[i][e] = ptr
         d_ff = parts[0].shape[0]
     sh = [None] * 4
     if shared is not None:
         for i, a in enumerate(shared):
-            ra, rdt = _raw(a)
-            if ra is not None:
-                assert rdt == dt, "weights and x must share a dtype"
-                keep.append(ra)
-                sh[i] = ra.ctypes.data
+            sh[i] = put(i, a)
         d_ff = shared[0].shape[0]
     for i in (1, 3):
         if not any(tabs[i][e] for e in range(E)):
             tabs[i] = None
-    return tabs, sh, (1 if d_ff is None else d_ff), keep
+    assert len(wdt) <= 1, "all weight matrices must share a dtype"
+    wd = wdt.pop() if wdt else dt
+    return tabs, sh, (1 if d_ff is None else d_ff), wd, keep
 
 
 def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
@@ -270,10 +347,10 @@ def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
         for j in range(k):
             if so is None or so[t, j] >= 0:
                 need.add(int(idx[t, j]))
-    tabs, sh, d_ff, keep = _weight_tables(need, experts, dt, shared)
+    tabs, sh, d_ff, wd, keep = _weight_tables(need, experts, dt, shared)
     y = np.zeros((len(tokens), d), np.float64)
     rc = lib().oracle_layer_rows(
-        len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, xa.ctypes.data,
+        len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, wd, xa.ctypes.data,
         _p(idx, _i32p), _p(w, _f64p), _p(so, _i32p), *tabs, *sh,
         _p(y, _f64p))
     if rc != 0:
@@ -312,10 +389,10 @@ def expert_choice_rows(tokens, x, gate: np.ndarray, experts: "Experts",
     need = set()
     for t in tokens.tolist():
         need.update(int(e) for e in np.nonzero(gate[t])[0])
-    tabs, sh, d_ff, keep = _weight_tables(need, experts, dt, shared)
+    tabs, sh, d_ff, wd, keep = _weight_tables(need, experts, dt, shared)
     y = np.zeros((len(tokens), d), np.float64)
     rc = lib().oracle_expert_choice_rows(
-        len(tokens), _p(tokens, _i32p), d, E, d_ff, dt, xa.ctypes.data,
+        len(tokens), _p(tokens, _i32p), d, E, d_ff, dt, wd, xa.ctypes.data,
         _p(gate, _f64p), *tabs, *sh, _p(y, _f64p))
     if rc != 0:
         raise RuntimeError(f"oracle_expert_choice_rows failed ({rc})")
@@ -363,11 +440,8 @@ def forward_expert_choice(inp: dict, capacity: int, alpha: float = 0.01,
     mon = monitor(logits, probs, counts, kept, E)
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
-    experts = Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
-                              inp.get("b2"))
-    shared = None
-    if inp.get("ws1") is not None:
-        shared = (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+    experts = experts_of(inp)
+    shared = shared_of(inp)
     y = expert_choice_rows(tokens, x, ec["gate"], experts, shared)
     out = dict(logits=logits, probs=probs, counts=counts, kept=kept,
                offsets=offsets, f=f, p=p, l_aux=l_aux, monitor=mon, y=y,
@@ -432,11 +506,8 @@ def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
     f, p, l_aux = stats(probs, disp["counts"], k, alpha)
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
-    experts = Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
-                              inp.get("b2"))
-    shared = None
-    if inp.get("ws1") is not None:
-        shared = (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+    experts = experts_of(inp)
+    shared = shared_of(inp)
     y = layer_rows(tokens, x, idx, w, disp["slot_of"], experts, shared)
     out = dict(probs=probs, logits=logits, topk_idx=idx, topk_w=w,
                margin=margin, capacity=cap, f=f, p=p, l_aux=l_aux, y=y,

@@ -40,15 +40,50 @@
 #define OR_ERR_ARG -1
 #define OR_ERR_MISSING_EXPERT -2
 
-/* Exact widening of one stored element to double. */
+/* Exact widening of one stored element to double: dtype 0 = float32,
+ * 1 = bfloat16 bit patterns, 3 = double (dequantised weights). */
 static double ld(const void *p, size_t i, int dtype)
 {
     if (dtype == 0)
         return (double)((const float *)p)[i];
+    if (dtype == 3)
+        return ((const double *)p)[i];
     uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* One OCP 8-bit floating-point E4M3 code as a double (exact): sign bit,
+ * four exponent bits with bias 7, three mantissa bits.  Exponent field 0
+ * holds the subnormals m/8 * 2^-6; the all-ones exponent is still finite
+ * except for mantissa 7, the NaN code; there are no infinities, and the
+ * largest magnitude is 1.75 * 2^8 = 448.  The pages name FP8 weights
+ * ("MoE inference with vLLM"; "AI-Research-SKILLs MoE training guide",
+ * sec. 9) without a format; E4M3 is the OCP format the gfx950 matrix
+ * cores read. */
+double oracle_fp8_e4m3(uint8_t b)
+{
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Per-output-channel dequantisation of an [N][K] FP8 matrix:
+ * w[n][c] = e4m3(q[n][c]) * scale[n] (exact in double). */
+void oracle_fp8_dequant(int N, int K, const uint8_t *q, const float *scale,
+                        double *w)
+{
+    for (int n = 0; n < N; ++n)
+        for (int c = 0; c < K; ++c)
+            w[(size_t)n * K + c] =
+                oracle_fp8_e4m3(q[(size_t)n * K + c]) * (double)scale[n];
 }
 
 /* Expert capacity: floor((tokens / experts) * capacity_factor).
@@ -227,14 +262,15 @@ void oracle_stats(int T, int E, int k, const double *probs,
  * [GROUP] sec. 3.1 (FFN(x) = W2 GELU(W1 x + b1) + b2); [SKILL] sec. 3.1
  * (Linear(h, 4h), GELU, Linear(4h, h)).  W1 is [d_ff][d] and W2 is
  * [d][d_ff], the nn.Linear weight layout.  b1 and b2 may be NULL. */
-static void expert_apply(int d, int d_ff, int dtype, const double *xrow,
-                         const void *w1, const void *b1, const void *w2,
-                         const void *b2, double *h, double *out)
+static void expert_apply(int d, int d_ff, int dtype, int wdtype,
+                         const double *xrow, const void *w1, const void *b1,
+                         const void *w2, const void *b2, double *h,
+                         double *out)
 {
     for (int f = 0; f < d_ff; ++f) {
         double z = 0.0;
         for (int c = 0; c < d; ++c)
-            z += ld(w1, (size_t)f * d + c, dtype) * xrow[c];
+            z += ld(w1, (size_t)f * d + c, wdtype) * xrow[c];
         if (b1)
             z += ld(b1, (size_t)f, dtype);
         h[f] = 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
@@ -242,7 +278,7 @@ static void expert_apply(int d, int d_ff, int dtype, const double *xrow,
     for (int c = 0; c < d; ++c) {
         double o = 0.0;
         for (int f = 0; f < d_ff; ++f)
-            o += ld(w2, (size_t)c * d_ff + f, dtype) * h[f];
+            o += ld(w2, (size_t)c * d_ff + f, wdtype) * h[f];
         if (b2)
             o += ld(b2, (size_t)c, dtype);
         out[c] = o;
@@ -258,11 +294,13 @@ static void expert_apply(int d, int d_ff, int dtype, const double *xrow,
  * [SKILL] sec. 3.1 (weighted merge); [DIVE] sec. 2.3 (overflow skips the
  * experts).
  * Expert weights come as per-expert pointer tables; an entry may be NULL
- * for an expert that no listed token uses.  slot_of may be NULL (no
- * capacity limit: every assignment is kept).  ws1 == NULL means no shared
- * expert.  y is [n][d] double. */
+ * for an expert that no listed token uses.  The weight matrices are in
+ * wdtype (dtype, or 3 for dequantised double weights); x and the biases
+ * in dtype.  slot_of may be NULL (no capacity limit: every assignment is
+ * kept).  ws1 == NULL means no shared expert.  y is [n][d] double. */
 int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
-                      int dtype, const void *x, const int32_t *idx,
+                      int dtype, int wdtype, const void *x,
+                      const int32_t *idx,
                       const double *w, const int32_t *slot_of,
                       const void *const *w1, const void *const *b1,
                       const void *const *w2, const void *const *b2,
@@ -291,13 +329,14 @@ int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
                 status = OR_ERR_MISSING_EXPERT;
                 continue;
             }
-            expert_apply(d, d_ff, dtype, xrow, w1[e], b1 ? b1[e] : NULL,
-                         w2[e], b2 ? b2[e] : NULL, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, xrow, w1[e],
+                         b1 ? b1[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += w[a] * o[c];
         }
         if (ws1) {
-            expert_apply(d, d_ff, dtype, xrow, ws1, bs1, ws2, bs2, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, xrow, ws1, bs1, ws2, bs2, h,
+                         o);
             for (int c = 0; c < d; ++c)
                 yr[c] += o[c];
         }
@@ -367,7 +406,7 @@ int oracle_expert_choice(int T, int E, int C, const double *logits,
  *         gate[t,e] * Expert_e(x_t)   (+ Shared(x_t))
  * A token no expert picked gets 0 (plus the shared expert). */
 int oracle_expert_choice_rows(int n, const int32_t *tokens, int d, int E,
-                              int d_ff, int dtype, const void *x,
+                              int d_ff, int dtype, int wdtype, const void *x,
                               const double *gate, const void *const *w1,
                               const void *const *b1, const void *const *w2,
                               const void *const *b2, const void *ws1,
@@ -395,13 +434,14 @@ int oracle_expert_choice_rows(int n, const int32_t *tokens, int d, int E,
                 status = OR_ERR_MISSING_EXPERT;
                 continue;
             }
-            expert_apply(d, d_ff, dtype, xrow, w1[e], b1 ? b1[e] : NULL,
-                         w2[e], b2 ? b2[e] : NULL, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, xrow, w1[e],
+                         b1 ? b1[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += g * o[c];
         }
         if (ws1) {
-            expert_apply(d, d_ff, dtype, xrow, ws1, bs1, ws2, bs2, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, xrow, ws1, bs1, ws2, bs2, h,
+                         o);
             for (int c = 0; c < d; ++c)
                 yr[c] += o[c];
         }

@@ -590,3 +590,60 @@ def test_expert_choice_zero_capacity_and_bounds():
     lg = np.zeros((4, 2))
     with pytest.raises(ValueError):
         oracle.expert_choice(lg, lg, 5)
+
+
+# ------------------------------------------------------------ FP8 weights
+def test_fp8_e4m3_every_code_matches_torch():
+    # torch's float8_e4m3fn decoding is the library special case
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+    got = oracle.fp8_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_e4m3_format_values():
+    # values fixed by the format: largest finite, smallest normal and
+    # subnormal, one, a mantissa pattern, signed zero, the NaN codes
+    v = oracle.fp8_e4m3
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert v(0x08) == 2.0 ** -6 and v(0x01) == 2.0 ** -9
+    # 0x4D: exponent 9, mantissa 5 -> 1.625 * 2^2
+    assert v(0x38) == 1.0 and v(0x37) == 0.9375 and v(0x4D) == 6.5
+    assert v(0x00) == 0.0 and np.signbit(v(0x80))
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    assert v(0x77) == 240.0      # exponent 14 is finite (no infinities)
+
+
+def test_fp8_layer_equals_bf16_layer_on_representable_weights():
+    # per-output-channel scales 2^(n%5 - 2): decode(q) * s is exactly a
+    # bf16 value, so the FP8 layer must equal the bf16 layer bit for bit;
+    # a scale on the wrong axis or divided instead of multiplied fails
+    w, inp = tiny_inputs(E=3, T=24, d=16, d_ff=32, biases=False)
+    g = np.random.default_rng(5)
+    table = torch.arange(256, dtype=torch.uint8).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = np.nonzero(np.isfinite(table) & (np.abs(table) <= 64))[0]
+
+    def quant(E, N, K):
+        q = g.choice(finite, size=(E, N, K)).astype(np.uint8)
+        s = (2.0 ** (np.arange(N) % 5 - 2)).astype(np.float32)
+        s = np.tile(s, (E, 1))
+        deq = table[q] * s[:, :, None].astype(np.float64)
+        return q, s, torch.from_numpy(deq.astype(np.float32))
+    x16 = dict(inp)
+    x16["x"] = inp["x"].to(torch.bfloat16)
+    x16["wr"] = inp["wr"].to(torch.bfloat16)
+    q1, s1, d1 = quant(3, 32, 16)
+    q2, s2, d2 = quant(3, 16, 32)
+    bf = dict(x16, w1=d1.to(torch.bfloat16), w2=d2.to(torch.bfloat16))
+    assert torch.equal(bf["w1"].float(), d1) and torch.equal(bf["w2"].float(), d2)
+    f8 = dict(x16, w1=torch.from_numpy(q1), w1_scale=torch.from_numpy(s1),
+              w2=torch.from_numpy(q2), w2_scale=torch.from_numpy(s2))
+    a = oracle.forward(bf, k=2)
+    b = oracle.forward(f8, k=2)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.any(a["y"] != 0)
