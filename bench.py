@@ -78,15 +78,18 @@ def algorithmic(wl, counts, kept):
     """FLOPs and bytes of one forward (kept rows only, touched experts)."""
     import numpy as np
     es = wl.elem_bytes
+    ew = 1 if wl.expert_fp8 else es        # bytes per expert-matrix weight
+    sc = 4 if wl.expert_fp8 else 0         # fp32 scale per output channel
     rows = int(np.sum(kept)) + wl.n_shared * wl.T     # expert GEMM rows
     touched = int(np.sum(kept > 0)) + wl.n_shared
     flops = 2.0 * wl.T * wl.d * wl.E + 4.0 * rows * wl.d * wl.d_ff
-    expert_bytes = (2 * wl.d * wl.d_ff + (wl.d + wl.d_ff if wl.linear_biases
-                                          else 0)) * es
+    expert_bytes = (2 * wl.d * wl.d_ff * ew + (wl.d + wl.d_ff) * sc +
+                    (wl.d + wl.d_ff if wl.linear_biases else 0) * es)
     bytes_ = (wl.E * wl.d * es + touched * expert_bytes +
               2 * wl.T * wl.d * es)
     up_flops = 2.0 * rows * wl.d * wl.d_ff
-    up_bytes = touched * wl.d * wl.d_ff * es + rows * (wl.d + wl.d_ff) * es
+    up_bytes = (touched * wl.d_ff * (wl.d * ew + sc) +
+                rows * (wl.d + wl.d_ff) * es)
     return dict(flops=flops, bytes=bytes_, rows=rows, touched=touched,
                 up_flops=up_flops, up_bytes=up_bytes)
 
@@ -249,7 +252,9 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E,
                    "k": wl.k, "d_ff": wl.d_ff, "n_shared": wl.n_shared,
                    "capacity_factor": wl.capacity_factor,
-                   "routing": wl.routing, "parallelism": "single-gpu"},
+                   "routing": wl.routing,
+                   "expert_weights": "e4m3" if wl.expert_fp8 else wl.dtype,
+                   "parallelism": "single-gpu"},
         "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
         "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),
         "wall_s": wall,

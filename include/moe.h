@@ -101,7 +101,15 @@ typedef enum {
  *             expert (see moe_capacity); expert choice: tokens picked per
  *             expert, 0 <= C <= T (required)
  *   aux_alpha coefficient of L_aux (0.01 is the pages' usual value)
- *   routing   a moe_routing_mode */
+ *   routing   a moe_routing_mode
+ *   expert_fp8 0: w1, w2, ws1, ws2 are in dtype; 1: they are OCP FP8 E4M3
+ *             bytes with fp32 per-output-channel scales (moe_weights
+ *             *_scale), a weight being e4m3(byte) * scale[row].  Needs
+ *             dtype MOE_BF16 and d, d_ff multiples of 1024; activations,
+ *             biases and y stay bf16.  The pages quote FP8 serving of the
+ *             Mixtral layer ("MoE inference with vLLM"; "AI-Research-
+ *             SKILLs MoE training guide", sec. 9); its target is the
+ *             weight-streaming decode shape, whose bytes it halves. */
 typedef struct moe_desc {
     int32_t T, d, E, k, d_ff;
     int32_t n_shared;
@@ -109,6 +117,7 @@ typedef struct moe_desc {
     int32_t capacity;
     float aux_alpha;
     int32_t routing;
+    int32_t expert_fp8;
 } moe_desc;
 
 /* Weights: caller-owned, read-only device buffers; NULL = absent.
@@ -121,7 +130,10 @@ typedef struct moe_desc {
  *   w1, b1      [E][d_ff][d], [E][d_ff]   dtype (w1 required)
  *   w2, b2      [E][d][d_ff], [E][d]      dtype (w2 required)
  *   ws1..bs2    shared expert, same shapes without the E axis; ws1/ws2
- *               required iff n_shared == 1 */
+ *               required iff n_shared == 1
+ *   w1_scale    [E][d_ff] fp32, w2_scale [E][d], ws1_scale [d_ff],
+ *   ws2_scale   [d]: per-output-channel scales of FP8 expert matrices
+ *               (required iff expert_fp8, for the matrices present) */
 typedef struct moe_weights {
     const void *w_router;
     const float *b_router;
@@ -129,6 +141,7 @@ typedef struct moe_weights {
     const void *w1, *b1;
     const void *w2, *b2;
     const void *ws1, *bs1, *ws2, *bs2;
+    const float *w1_scale, *w2_scale, *ws1_scale, *ws2_scale;
 } moe_weights;
 
 /* Routing results and statistics: caller-owned device buffers.

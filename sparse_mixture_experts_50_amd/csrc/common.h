@@ -135,6 +135,8 @@ struct GemmParams {
     const void *Ws;           // shared [N][K] or null
     const void *bias_s;       // shared [N] or null
     void *out;                // [slots][N]
+    const float *scale;       // FP8 weights: per-output-channel [E][N]
+    const float *scale_s;     // FP8 shared expert [N]
     int E, n_shared, T, shared_base;
     int N, K;
 };

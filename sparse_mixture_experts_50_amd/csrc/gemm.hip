@@ -619,18 +619,18 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
 // more than 16 rows.  Two batches of SU sub-steps are kept in flight, and
 // the four partial accumulators are summed through LDS in a fixed order
 // before the epilogue.
-template <int MT, int SU>
-__device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][2],
-                                             const uint16_t *w0,
-                                             const uint16_t *w1,
+template <int MT, int TN, int SU>
+__device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][TN],
+                                             const uint16_t *w0, size_t wstep,
                                              const uint16_t *a0,
                                              const uint16_t *a1, int kq) {
-    u32x4 av[2][SU][MT], bv[2][SU][2];
+    u32x4 av[2][SU][MT], bv[2][SU][TN];
     auto load = [&](int buf, int k0) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < SU; ++s) {
-            bv[buf][s][0] = *(const u32x4 *)(w0 + k0 + s * 32);
-            bv[buf][s][1] = *(const u32x4 *)(w1 + k0 + s * 32);
+#pragma unroll
+            for (int n = 0; n < TN; ++n)
+                bv[buf][s][n] = *(const u32x4 *)(w0 + n * wstep + k0 + s * 32);
             av[buf][s][0] = *(const u32x4 *)(a0 + k0 + s * 32);
             if (MT == 2) av[buf][s][MT - 1] = *(const u32x4 *)(a1 + k0 + s * 32);
         }
@@ -641,7 +641,7 @@ __device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][2],
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < TN; ++n)
                     acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         as_bf16x8(bv[buf][s][n]), as_bf16x8(av[buf][s][m]),
                         acc[m][n], 0, 0, 0);
@@ -662,10 +662,96 @@ __device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][2],
     }
 }
 
-template <bool UP>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
-    constexpr int NB = 32;         // columns per unit (2 MFMA tiles)
-    constexpr int SU = 4;          // 32-deep sub-steps per load batch
+// FP8 (OCP E4M3) weight rows, bf16 activations.  Each lane loads 16
+// weight bytes, the run k = 16q .. 16q+15 of a 64-deep sub-step (q =
+// lane/16), and feeds two MFMAs with them (bytes 0-7, then 8-15), decoded
+// exactly to bf16 (every E4M3 value is a bf16 value: the fp32 decode's
+// upper half).  The token rows are read at the same k (two 16-byte loads),
+// so both operands agree on the k order inside each MFMA.  The
+// per-output-channel scale is applied in the epilogue.
+__device__ __forceinline__ uint32_t upper_halves(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+    const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    u32x4 r;
+    r[0] = upper_halves(a[0], a[1]);
+    r[1] = upper_halves(b[0], b[1]);
+    r[2] = upper_halves(c[0], c[1]);
+    r[3] = upper_halves(d[0], d[1]);
+    return r;
+}
+
+template <int MT, int TN, int SU>
+__device__ __forceinline__ void stream_chunk_fp8(floatx4 (&acc)[2][TN],
+                                                 const uint8_t *w0,
+                                                 size_t wstep,
+                                                 const uint16_t *a0,
+                                                 const uint16_t *a1, int kq) {
+    u32x4 av[2][SU][MT][2], bv[2][SU][TN];
+    auto load = [&](int buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SU; ++s) {
+#pragma unroll
+            for (int n = 0; n < TN; ++n)
+                bv[buf][s][n] = *(const u32x4 *)(w0 + n * wstep + k0 + s * 64);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                av[buf][s][0][h] = *(const u32x4 *)(a0 + k0 + s * 64 + 8 * h);
+                if (MT == 2)
+                    av[buf][s][MT - 1][h] =
+                        *(const u32x4 *)(a1 + k0 + s * 64 + 8 * h);
+            }
+        }
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SU; ++s)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const u32x4 q = bv[buf][s][n];
+                const u32x4 lo = e4m3x8_to_bf16x8(q[0], q[1]);
+                const u32x4 hi = e4m3x8_to_bf16x8(q[2], q[3]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(lo), as_bf16x8(av[buf][s][m][0]), acc[m][n],
+                        0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(hi), as_bf16x8(av[buf][s][m][1]), acc[m][n],
+                        0, 0, 0);
+                }
+            }
+    };
+    constexpr int STEP = 64 * SU;
+    load(0, 0);
+    for (int k0 = 0; k0 < kq; k0 += 2 * STEP) {
+        if (k0 + STEP < kq) load(1, k0 + STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k0 + STEP < kq) {
+            if (k0 + 2 * STEP < kq) load(0, k0 + 2 * STEP);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// FP8 = false: bf16 weights; true: E4M3 weights with per-channel scales.
+// NB = columns per unit (NB/16 MFMA tiles): wider units re-read the token
+// rows fewer times per weight byte.
+template <bool UP, bool FP8, int NB>
+__global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
+    constexpr int TN = NB / 16;
+    // sub-steps per load batch: 32-deep (bf16) or 64-deep (FP8) ones
+    constexpr int SU = NB == 32 ? 4 : 2;
     __shared__ float part[4][32][NB + 1];
     __shared__ TileTable tt;
     const int tid = threadIdx.x;
@@ -678,7 +764,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
     const uint16_t *A = (const uint16_t *)p.A;
     const int kq = K / 4;                     // this wave's K range
     const int kbeg = wave * kq;
-    const int kg = (lane >> 4) * 8;           // k group of this lane
+    // k offset of this lane inside a sub-step: 8 bf16 of a 32-deep one, or
+    // 16 of a 64-deep one for FP8 weights
+    const int kg = FP8 ? (lane >> 4) * 16 : (lane >> 4) * 8;
     const int r16 = lane & 15;
     uint16_t *out = (uint16_t *)p.out;
 
@@ -686,14 +774,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
         const int g = u / NTN, n_tile = u - g * NTN;
         if (tt.rows[g] == 0) continue;
         const bool routed = g < p.E;
-        const uint16_t *Wg = routed ? (const uint16_t *)p.W + (size_t)g * N * K
-                                    : (const uint16_t *)p.Ws;
+        const int esz = FP8 ? 1 : 2;         // bytes per weight
+        const char *Wg = routed
+            ? (const char *)p.W + (size_t)g * N * K * esz
+            : (const char *)p.Ws;
         const uint16_t *bg = routed
             ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
             : (const uint16_t *)p.bias_s;
+        const float *sg = FP8 ? (routed ? p.scale + (size_t)g * N : p.scale_s)
+                              : nullptr;
         const int n0 = n_tile * NB;
-        const uint16_t *w0 = Wg + (size_t)(n0 + r16) * K + kbeg + kg;
-        const uint16_t *w1 = w0 + (size_t)16 * K;
+        const char *w0 = Wg + ((size_t)(n0 + r16) * K + kbeg + kg) * esz;
+        const size_t wstep = (size_t)16 * K;     // elements between tiles
 
         for (int mc = 0; mc < tt.mt[g]; ++mc) {
             const int row0 = tt.start[g] + mc * 32;
@@ -713,23 +805,33 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
             }
             const uint16_t *a0 = A + (size_t)src[0] * K + kbeg + kg;
             const uint16_t *a1 = A + (size_t)src[1] * K + kbeg + kg;
-            floatx4 acc[2][2];
+            floatx4 acc[2][TN];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < TN; ++n)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[m][n][v] = 0.0f;
-            if (nrows > 16)
-                stream_chunk<2, SU>(acc, w0, w1, a0, a1, kq);
-            else
-                stream_chunk<1, SU>(acc, w0, w1, a0, a1, kq);
+            if (FP8) {
+                const uint8_t *q0 = (const uint8_t *)w0;
+                if (nrows > 16)
+                    stream_chunk_fp8<2, TN, NB == 32 ? 2 : 1>(acc, q0, wstep,
+                                                              a0, a1, kq);
+                else
+                    stream_chunk_fp8<1, TN, SU>(acc, q0, wstep, a0, a1, kq);
+            } else {
+                const uint16_t *b0 = (const uint16_t *)w0;
+                if (nrows > 16)
+                    stream_chunk<2, TN, SU>(acc, b0, wstep, a0, a1, kq);
+                else
+                    stream_chunk<1, TN, SU>(acc, b0, wstep, a0, a1, kq);
+            }
             // lane holds row m = 16*mt + lane%16, features
             // 16*nt + 4*(lane/16) + 0..3
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < TN; ++n)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         part[wave][16 * m + r16][16 * n + 4 * (lane >> 4) + v] =
@@ -745,6 +847,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_stream(GemmParams p) {
                     float v1 = part[0][m][c + 1] + part[1][m][c + 1];
                     v1 += part[2][m][c + 1];
                     v1 += part[3][m][c + 1];
+                    if (FP8) {
+                        v0 *= sg[n0 + c];
+                        v1 *= sg[n0 + c + 1];
+                    }
                     if (bg) {
                         v0 += bf16_to_f32(bg[n0 + c]);
                         v1 += bf16_to_f32(bg[n0 + c + 1]);
@@ -899,6 +1005,9 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA_256x256: return {256, 256, 512, 4 * 512 * 64};
     case GEMM_BF16_DMA_128x256: return {128, 256, 256, 4 * 384 * 64};
     case GEMM_BF16_STREAM_32x64: return {32, 32, 256, 0};
+    case GEMM_FP8_STREAM_32x64: return {32, 32, 256, 0};
+    case GEMM_BF16_STREAM_64x64: return {32, 64, 256, 0};
+    case GEMM_FP8_STREAM_64x64: return {32, 64, 256, 0};
     case GEMM_BF16_DMA64_256x256: return {256, 256, 512, 2 * 512 * 128};
     case GEMM_BF16_DMA64_128x256: return {128, 256, 256, 2 * 384 * 128};
     default: return {64, 64, 256, 0};
@@ -934,11 +1043,35 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
                   : launch_dma64<128, 256, 2, 2, false>(p, grid, s);
     case GEMM_BF16_STREAM_32x64:
         if (up)
-            hipLaunchKernelGGL(gemm_bf16_stream<true>, dim3(grid), dim3(256), 0,
-                               s, p);
+            hipLaunchKernelGGL((gemm_stream<true, false, 32>), dim3(grid),
+                               dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL(gemm_bf16_stream<false>, dim3(grid), dim3(256),
-                               0, s, p);
+            hipLaunchKernelGGL((gemm_stream<false, false, 32>), dim3(grid),
+                               dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_BF16_STREAM_64x64:
+        if (up)
+            hipLaunchKernelGGL((gemm_stream<true, false, 64>), dim3(grid),
+                               dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_stream<false, false, 64>), dim3(grid),
+                               dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_FP8_STREAM_64x64:
+        if (up)
+            hipLaunchKernelGGL((gemm_stream<true, true, 64>), dim3(grid),
+                               dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_stream<false, true, 64>), dim3(grid),
+                               dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_FP8_STREAM_32x64:
+        if (up)
+            hipLaunchKernelGGL((gemm_stream<true, true, 32>), dim3(grid),
+                               dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_stream<false, true, 32>), dim3(grid),
+                               dim3(256), 0, s, p);
         return hipGetLastError();
     default:
         if (up)

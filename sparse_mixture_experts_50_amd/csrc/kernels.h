@@ -59,7 +59,16 @@ enum GemmVariant {
     GEMM_BF16_STREAM_32x64 = 7,
     GEMM_BF16_DMA64_256x256 = 8,
     GEMM_BF16_DMA64_128x256 = 9,
+    GEMM_FP8_STREAM_32x64 = 10,   // FP8 (E4M3) weights, bf16 activations
+    GEMM_BF16_STREAM_64x64 = 11,  // streaming with 64-column units
+    GEMM_FP8_STREAM_64x64 = 12,
 };
+
+// Variants that stream weights over persistent (group, column-slab) units.
+inline bool stream_variant(int v) {
+    return v == GEMM_BF16_STREAM_32x64 || v == GEMM_FP8_STREAM_32x64 ||
+           v == GEMM_BF16_STREAM_64x64 || v == GEMM_FP8_STREAM_64x64;
+}
 
 struct GemmVariantInfo {
     int bm, bn, threads, lds_bytes;

@@ -42,7 +42,13 @@ int check_desc(const moe_desc *d) {
     if (expert_choice(d) &&
         (d->k != d->E || d->capacity < 0 || d->capacity > d->T))
         return MOE_ERR_INVALID_ARG;
+    if (d->expert_fp8 != 0 && d->expert_fp8 != 1) return MOE_ERR_INVALID_ARG;
     if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    // FP8 weights run on the weight-streaming kernel: its four K quarters
+    // hold whole 256-deep load batches
+    if (d->expert_fp8 && (d->dtype != MOE_BF16 || d->d % 1024 != 0 ||
+                          d->d_ff % 1024 != 0))
+        return MOE_ERR_UNSUPPORTED;
     if (d->E > MOE_MAX_E || (!expert_choice(d) && d->k > 64))
         return MOE_ERR_UNSUPPORTED;
     if (d->d % 64 != 0 || d->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -114,23 +120,32 @@ int variant_override(bool up, const moe_desc *d, int N) {
     if (!v || !*v) return -1;
     const int id = atoi(v);
     if (d->dtype == MOE_F32) return -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_DMA64_128x256 ||
-        id == GEMM_F32_64x64)
+    const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
+                        id == GEMM_FP8_STREAM_64x64;
+    if (d->expert_fp8) return fp8_id ? id : -1;
+    if (id < GEMM_BF16_256x256 || id > GEMM_FP8_STREAM_64x64 ||
+        id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
+    // the streaming kernels split K in four quarters of whole load batches
+    // (4 x 32 deep for 32-column units, 2 x 32 for 64-column ones)
     if (id == GEMM_BF16_STREAM_32x64 && (d->d % 512 != 0 || d->d_ff % 512 != 0))
+        return -1;
+    if (id == GEMM_BF16_STREAM_64x64 && (d->d % 256 != 0 || d->d_ff % 256 != 0))
         return -1;
     return id;
 }
 
 int pick_variant(const moe_desc *d, int N) {
     if (d->dtype == MOE_F32) return GEMM_F32_64x64;
+    if (d->expert_fp8) return GEMM_FP8_STREAM_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
     const double avg = (double)routed_rows(d) / d->E;
-    // the streaming kernel splits K in four quarters of whole 128-deep
-    // load batches
-    if (avg <= 32.0 && d->d % 512 == 0 && d->d_ff % 512 == 0)
-        return GEMM_BF16_STREAM_32x64;
+    // the streaming kernel splits K in four quarters of whole 64-deep
+    // load batches; 64-column units re-read the token rows half as often
+    // as 32-column ones
+    if (avg <= 32.0 && d->d % 256 == 0 && d->d_ff % 256 == 0)
+        return GEMM_BF16_STREAM_64x64;
     if (avg <= 48.0) return GEMM_BF16_32x256;
     if (avg <= 192.0) return GEMM_BF16_DMA64_128x256;
     return GEMM_BF16_DMA64_256x256;
@@ -138,7 +153,7 @@ int pick_variant(const moe_desc *d, int N) {
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
     const GemmVariantInfo vi = gemm_variant_info(variant);
-    if (variant == GEMM_BF16_STREAM_32x64) {    // persistent over units
+    if (stream_variant(variant)) {              // persistent over units
         const long long units = (long long)(d->E + d->n_shared) * (N / vi.bn);
         const long long slots = (long long)device_cus() * 2;
         return (int)(units < slots ? units : slots);
@@ -164,6 +179,9 @@ int check_weights_router(const moe_weights *w) {
 int check_weights_ffn(const moe_desc *d, const moe_weights *w) {
     if (!w || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
     if (d->n_shared && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+    if (d->expert_fp8 && (!w->w1_scale || !w->w2_scale ||
+                          (d->n_shared && (!w->ws1_scale || !w->ws2_scale))))
+        return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -211,6 +229,8 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
         p.Ws = w->ws1;
         p.bias_s = w->bs1;
         p.out = at(ws, L.h);
+        p.scale = w->w1_scale;
+        p.scale_s = w->ws1_scale;
         p.N = d->d_ff;
         p.K = d->d;
     } else {
@@ -220,6 +240,8 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
         p.Ws = w->ws2;
         p.bias_s = w->bs2;
         p.out = at(ws, L.yp);
+        p.scale = w->w2_scale;
+        p.scale_s = w->ws2_scale;
         p.N = d->d;
         p.K = d->d_ff;
     }

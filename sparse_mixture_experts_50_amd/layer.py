@@ -6,6 +6,9 @@ layouts are those of include/moe.h:
   x [T][d]; w_router [E][d]; w1 [E][d_ff][d]; w2 [E][d][d_ff];
   b1 [E][d_ff]; b2 [E][d]; shared expert ws1 [d_ff][d], ws2 [d][d_ff];
   b_router / expert_bias float32 [E].
+FP8 expert matrices: uint8 (or float8_e4m3fn) tensors of the same shapes
+holding OCP E4M3 codes, with float32 per-output-channel scales
+w1_scale [E][d_ff], w2_scale [E][d], ws1_scale [d_ff], ws2_scale [d].
 """
 from __future__ import annotations
 
@@ -50,15 +53,17 @@ def _opt(t, name, shape, dtype, device):
 
 def make_desc(T: int, d: int, E: int, k: int, d_ff: int, dtype: torch.dtype,
               n_shared: int = 0, capacity: int = -1,
-              aux_alpha: float = 0.01, routing: str = "topk") -> MoeDesc:
+              aux_alpha: float = 0.01, routing: str = "topk",
+              expert_fp8: bool = False) -> MoeDesc:
     """``routing`` is "topk" or "expert_choice" (then k must be E and
-    capacity the tokens each expert picks)."""
+    capacity the tokens each expert picks); ``expert_fp8`` marks E4M3
+    expert matrices."""
     if dtype not in _DT:
         raise ValueError(f"unsupported dtype {dtype}")
     if routing not in _ROUTING:
         raise ValueError(f"unknown routing {routing!r}")
     return MoeDesc(T, d, E, k, d_ff, n_shared, _DT[dtype], capacity,
-                   aux_alpha, _ROUTING[routing])
+                   aux_alpha, _ROUTING[routing], int(bool(expert_fp8)))
 
 
 def moe_capacity(T: int, E: int, capacity_factor: Optional[float]) -> int:
@@ -78,33 +83,56 @@ def moe_workspace_size(desc: MoeDesc) -> int:
     return n
 
 
+def _codes(t):
+    """float8_e4m3fn tensors are passed as their uint8 codes."""
+    if t is not None and t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
 class Weights:
-    """Device weight tensors of one layer (see module docstring)."""
+    """Device weight tensors of one layer (see module docstring).  The
+    expert matrices are FP8 when given as uint8 / float8_e4m3fn codes, and
+    then need their scales."""
 
     def __init__(self, w_router, w1, w2, b_router=None, expert_bias=None,
-                 b1=None, b2=None, ws1=None, bs1=None, ws2=None, bs2=None):
+                 b1=None, b2=None, ws1=None, bs1=None, ws2=None, bs2=None,
+                 w1_scale=None, w2_scale=None, ws1_scale=None,
+                 ws2_scale=None):
+        w1, w2, ws1, ws2 = _codes(w1), _codes(w2), _codes(ws1), _codes(ws2)
         self.w_router, self.w1, self.w2 = w_router, w1, w2
         self.b_router, self.expert_bias = b_router, expert_bias
         self.b1, self.b2 = b1, b2
         self.ws1, self.bs1, self.ws2, self.bs2 = ws1, bs1, ws2, bs2
+        self.w1_scale, self.w2_scale = w1_scale, w2_scale
+        self.ws1_scale, self.ws2_scale = ws1_scale, ws2_scale
         E, d_ff, d = w1.shape
         self.E, self.d, self.d_ff = E, d, d_ff
-        self.dtype = w1.dtype
+        self.dtype = w_router.dtype
         self.device = w1.device
         self.n_shared = 0 if ws1 is None else 1
+        self.expert_fp8 = w1.dtype == torch.uint8
         dt, dev = self.dtype, self.device
+        wdt = torch.uint8 if self.expert_fp8 else dt
+        f32 = torch.float32
         _need(w_router, "w_router", (E, d), dt, dev)
-        _need(w1, "w1", (E, d_ff, d), dt, dev)
-        _need(w2, "w2", (E, d, d_ff), dt, dev)
-        _opt(b_router, "b_router", (E,), torch.float32, dev)
-        _opt(expert_bias, "expert_bias", (E,), torch.float32, dev)
+        _need(w1, "w1", (E, d_ff, d), wdt, dev)
+        _need(w2, "w2", (E, d, d_ff), wdt, dev)
+        _opt(b_router, "b_router", (E,), f32, dev)
+        _opt(expert_bias, "expert_bias", (E,), f32, dev)
         _opt(b1, "b1", (E, d_ff), dt, dev)
         _opt(b2, "b2", (E, d), dt, dev)
+        if self.expert_fp8:
+            _need(w1_scale, "w1_scale", (E, d_ff), f32, dev)
+            _need(w2_scale, "w2_scale", (E, d), f32, dev)
         if self.n_shared:
-            _need(ws1, "ws1", (d_ff, d), dt, dev)
-            _need(ws2, "ws2", (d, d_ff), dt, dev)
+            _need(ws1, "ws1", (d_ff, d), wdt, dev)
+            _need(ws2, "ws2", (d, d_ff), wdt, dev)
             _opt(bs1, "bs1", (d_ff,), dt, dev)
             _opt(bs2, "bs2", (d,), dt, dev)
+            if self.expert_fp8:
+                _need(ws1_scale, "ws1_scale", (d_ff,), f32, dev)
+                _need(ws2_scale, "ws2_scale", (d,), f32, dev)
 
     @staticmethod
     def from_dict(inp: dict, device=None) -> "Weights":
@@ -116,12 +144,15 @@ class Weights:
         return Weights(g("wr"), g("w1"), g("w2"), b_router=g("br"),
                        expert_bias=g("ebias"), b1=g("b1"), b2=g("b2"),
                        ws1=g("ws1"), bs1=g("bs1"), ws2=g("ws2"),
-                       bs2=g("bs2"))
+                       bs2=g("bs2"), w1_scale=g("w1_scale"),
+                       w2_scale=g("w2_scale"), ws1_scale=g("ws1_scale"),
+                       ws2_scale=g("ws2_scale"))
 
     def struct(self) -> MoeWeights:
         return MoeWeights(*[_ptr(t) for t in (
             self.w_router, self.b_router, self.expert_bias, self.w1, self.b1,
-            self.w2, self.b2, self.ws1, self.bs1, self.ws2, self.bs2)])
+            self.w2, self.b2, self.ws1, self.bs1, self.ws2, self.bs2,
+            self.w1_scale, self.w2_scale, self.ws1_scale, self.ws2_scale)])
 
 
 class Routing:
@@ -267,7 +298,8 @@ class MoeLayer:
             cap = min(cap, T)
         return make_desc(T, w.d, w.E, self.k, w.d_ff, w.dtype,
                          n_shared=w.n_shared, capacity=cap,
-                         aux_alpha=self.aux_alpha, routing=self.routing)
+                         aux_alpha=self.aux_alpha, routing=self.routing,
+                         expert_fp8=w.expert_fp8)
 
     def buffers(self, T: int):
         if T not in self._bufs:

@@ -79,6 +79,11 @@ def desc(**kw):
     (dict(routing=1, k=2, capacity=16), _lib.MOE_ERR_INVALID_ARG),
     (dict(routing=1, k=8, capacity=-1), _lib.MOE_ERR_INVALID_ARG),
     (dict(routing=1, k=8, capacity=65), _lib.MOE_ERR_INVALID_ARG),
+    # FP8 expert weights: bf16 layers with d, d_ff multiples of 1024
+    (dict(expert_fp8=2), _lib.MOE_ERR_INVALID_ARG),
+    (dict(expert_fp8=1, d=1024, d_ff=1024, dtype=0), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(expert_fp8=1, d=512, d_ff=1024), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(expert_fp8=1, d=1024, d_ff=1536), _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_descriptor_rejected_before_any_launch(kw, status):
     L = _lib.lib()
@@ -174,6 +179,22 @@ def test_expert_choice_descriptor_and_workspace():
     r = _lib.MoeRouting(*([FAKE] * 6 + [None] + [FAKE] * 3))
     assert L.moe_permute(ctypes.byref(d), ctypes.byref(r), FAKE, ws,
                          None) == -1
+
+
+def test_fp8_needs_scales():
+    L = _lib.lib()
+    d = desc(expert_fp8=1, d=1024, d_ff=1024)
+    ws = L.moe_workspace_size(ctypes.byref(d))
+    assert ws > 0
+    r = _lib.MoeRouting(*([FAKE] * 10))
+    no_scale = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                               None, None, None, None)
+    assert L.moe_forward(ctypes.byref(d), FAKE, ctypes.byref(no_scale),
+                         ctypes.byref(r), FAKE, FAKE, ws, None) == -1
+    one_scale = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                                None, None, None, None, FAKE, None)
+    assert L.moe_grouped_ffn(ctypes.byref(d), FAKE, ctypes.byref(one_scale),
+                             ctypes.byref(r), FAKE, ws, None) == -1
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -52,6 +52,7 @@ class Workload:
     bias_update_gamma: Optional[float] = None  # one balancing-bias step
     calls: int = 1              # distinct x per timed run (decode)
     routing: str = "topk"       # "topk" | "expert_choice" (then k == E)
+    expert_fp8: bool = False    # expert matrices stored as E4M3 + scales
     seed: int = 0
 
     @property
@@ -84,6 +85,11 @@ WORKLOADS: Dict[str, Workload] = {
     "deepseek_v3": Workload(
         name="deepseek_v3", T=8192, d=7168, E=256, k=8, d_ff=2048,
         dtype="bf16", n_shared=1, expert_bias="zipf", bias_update_gamma=0.001),
+    # Mixtral-8x7B-shaped decode with E4M3 expert weights (per-channel
+    # scales): half the weight bytes of the bf16 layer.
+    "mixtral_decode_fp8": Workload(
+        name="mixtral_decode_fp8", T=32, d=4096, E=8, k=2, d_ff=14336,
+        dtype="bf16", router_var=0.02, calls=200, expert_fp8=True),
     # Expert choice: each of 64 experts picks C = floor(T/E * 2) = 256
     # tokens, the compute of top-2 routing on the Switch-sized layer.
     "expert_choice_c2": Workload(
@@ -151,6 +157,18 @@ def make_expert(w: Workload, e: int, device="cpu", shared: bool = False):
     return w1, b1, w2, b2
 
 
+def quantize_e4m3(wt: torch.Tensor):
+    """Checkpoint conversion of one [N, K] matrix to FP8: per-row scale
+    amax / 448 (1 for an all-zero row) and E4M3 codes of w / scale by
+    torch's float8_e4m3fn cast (round to nearest even).  Returns (uint8
+    codes, float32 scales)."""
+    wf = wt.to(torch.float32)
+    amax = wf.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (wf / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q, scale
+
+
 def make_router(w: Workload, device="cpu"):
     """Router weight Wr[E, d] plus the float32 additive logit term (the
     router Linear bias, or a fixed per-expert skew) and the float32
@@ -185,6 +203,8 @@ def make_inputs(w: Workload, device="cpu", call: int = 0) -> dict:
     dt = w.torch_dtype
     out = {"x": make_x(w, device, call)}
     out["wr"], out["br"], out["ebias"] = make_router(w, device)
+    if w.expert_fp8:
+        return _fp8_experts(w, device, out)
     w1 = torch.empty((w.E, w.d_ff, w.d), device=device, dtype=dt)
     w2 = torch.empty((w.E, w.d, w.d_ff), device=device, dtype=dt)
     b1 = torch.empty((w.E, w.d_ff), device=device, dtype=dt) \
@@ -203,6 +223,44 @@ def make_inputs(w: Workload, device="cpu", call: int = 0) -> dict:
     if w.n_shared:
         s1, sb1, s2, sb2 = make_expert(w, 0, device, shared=True)
         out.update(ws1=s1, bs1=sb1, ws2=s2, bs2=sb2)
+    else:
+        out.update(ws1=None, bs1=None, ws2=None, bs2=None)
+    return out
+
+
+def _fp8_experts(w: Workload, device, out: dict) -> dict:
+    """The expert part of make_inputs for FP8 workloads: the layer-dtype
+    weights of make_expert, converted by quantize_e4m3 (adds w1_scale,
+    w2_scale and, with a shared expert, ws1_scale, ws2_scale)."""
+    dt = w.torch_dtype
+    u8, f32 = torch.uint8, torch.float32
+    w1 = torch.empty((w.E, w.d_ff, w.d), device=device, dtype=u8)
+    w2 = torch.empty((w.E, w.d, w.d_ff), device=device, dtype=u8)
+    s1 = torch.empty((w.E, w.d_ff), device=device, dtype=f32)
+    s2 = torch.empty((w.E, w.d), device=device, dtype=f32)
+    b1 = torch.empty((w.E, w.d_ff), device=device, dtype=dt) \
+        if w.linear_biases else None
+    b2 = torch.empty((w.E, w.d), device=device, dtype=dt) \
+        if w.linear_biases else None
+    for e in range(w.E):
+        e1, eb1, e2, eb2 = make_expert(w, e, device)
+        q, s = quantize_e4m3(e1)
+        w1[e].copy_(q)
+        s1[e].copy_(s)
+        q, s = quantize_e4m3(e2)
+        w2[e].copy_(q)
+        s2[e].copy_(s)
+        if b1 is not None:
+            b1[e].copy_(eb1)
+            b2[e].copy_(eb2)
+        del e1, e2, q
+    out.update(w1=w1, b1=b1, w2=w2, b2=b2, w1_scale=s1, w2_scale=s2)
+    if w.n_shared:
+        e1, sb1, e2, sb2 = make_expert(w, 0, device, shared=True)
+        q1, t1 = quantize_e4m3(e1)
+        q2, t2 = quantize_e4m3(e2)
+        out.update(ws1=q1, bs1=sb1, ws2=q2, bs2=sb2, ws1_scale=t1,
+                   ws2_scale=t2)
     else:
         out.update(ws1=None, bs1=None, ws2=None, bs2=None)
     return out
