@@ -60,15 +60,15 @@ def lib():
             _f64p, _i32p, ctypes.c_double, _f64p, _f64p, _f64p]
         L.oracle_layer_rows.restype = ctypes.c_int
         L.oracle_layer_rows.argtypes = [ctypes.c_int, _i32p] + \
-            [ctypes.c_int] * 5 + [_vp, _i32p, _f64p, _i32p] + \
-            [ctypes.POINTER(_vp)] * 4 + [_vp] * 4 + [_f64p]
+            [ctypes.c_int] * 6 + [_vp, _i32p, _f64p, _i32p] + \
+            [ctypes.POINTER(_vp)] * 6 + [_vp] * 6 + [_f64p]
         L.oracle_expert_choice.restype = ctypes.c_int
         L.oracle_expert_choice.argtypes = [ctypes.c_int] * 3 + [
             _f64p, _f64p, _i32p, _i32p, _f64p, _i32p]
         L.oracle_expert_choice_rows.restype = ctypes.c_int
         L.oracle_expert_choice_rows.argtypes = [ctypes.c_int, _i32p] + \
-            [ctypes.c_int] * 5 + [_vp, _f64p] + [ctypes.POINTER(_vp)] * 4 + \
-            [_vp] * 4 + [_f64p]
+            [ctypes.c_int] * 6 + [_vp, _f64p] + [ctypes.POINTER(_vp)] * 6 + \
+            [_vp] * 6 + [_f64p]
         L.oracle_fp8_e4m3.restype = ctypes.c_double
         L.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
         L.oracle_fp8_dequant.restype = None
@@ -211,6 +211,9 @@ def stats(probs: np.ndarray, counts: np.ndarray, k: int, alpha: float):
     return f, p, float(l[0])
 
 
+ACTIVATIONS = {"gelu": 0, "silu": 1, "swiglu": 2}
+
+
 def fp8_e4m3(codes) -> np.ndarray:
     """float64 values of OCP E4M3 codes (uint8 array)."""
     c = np.asarray(codes, dtype=np.uint8)
@@ -243,47 +246,67 @@ def fp8_dequant(q, scale) -> np.ndarray:
 class Experts:
     """Per-expert weights for :func:`layer_rows`.
 
-    ``get(e)`` returns ``(W1[d_ff,d], b1|None, W2[d,d_ff], b2|None)`` as
-    torch CPU tensors or numpy arrays; it is only called for experts that a
-    listed token actually uses, so large layers can be fetched lazily."""
+    ``get(e)`` returns ``(W1[d_ff,d], b1|None, W2[d,d_ff], b2|None)``, plus
+    ``W3[d_ff,d], b3|None`` (the SwiGLU up projection) for gated experts,
+    as torch CPU tensors or numpy arrays; it is only called for experts
+    that a listed token actually uses, so large layers can be fetched
+    lazily."""
 
     def __init__(self, E: int, get):
         self.E = E
         self.get = get
 
     @staticmethod
-    def stacked(w1, b1, w2, b2):
+    def stacked(w1, b1, w2, b2, w3=None, b3=None):
         E = w1.shape[0]
-        return Experts(E, lambda e: (w1[e], None if b1 is None else b1[e],
-                                     w2[e], None if b2 is None else b2[e]))
+        pick = lambda t, e: None if t is None else t[e]
+
+        def get(e):
+            parts = (w1[e], pick(b1, e), w2[e], pick(b2, e))
+            if w3 is not None:
+                parts += (w3[e], pick(b3, e))
+            return parts
+        return Experts(E, get)
 
     @staticmethod
-    def fp8(w1, s1, b1, w2, s2, b2):
+    def fp8(w1, s1, b1, w2, s2, b2, w3=None, s3=None, b3=None):
         """FP8 expert matrices with per-output-channel scales, dequantised
         one expert at a time."""
         E = w1.shape[0]
-        return Experts(E, lambda e: (
-            fp8_dequant(w1[e], s1[e]), None if b1 is None else b1[e],
-            fp8_dequant(w2[e], s2[e]), None if b2 is None else b2[e]))
+        pick = lambda t, e: None if t is None else t[e]
+
+        def get(e):
+            parts = (fp8_dequant(w1[e], s1[e]), pick(b1, e),
+                     fp8_dequant(w2[e], s2[e]), pick(b2, e))
+            if w3 is not None:
+                parts += (fp8_dequant(w3[e], s3[e]), pick(b3, e))
+            return parts
+        return Experts(E, get)
 
 
 def experts_of(inp: dict) -> Experts:
-    """The routed experts of an input dict (FP8 when it carries scales)."""
+    """The routed experts of an input dict (FP8 when it carries scales,
+    gated when it carries w3)."""
     if inp.get("w1_scale") is not None:
         return Experts.fp8(inp["w1"], inp["w1_scale"], inp.get("b1"),
-                           inp["w2"], inp["w2_scale"], inp.get("b2"))
+                           inp["w2"], inp["w2_scale"], inp.get("b2"),
+                           inp.get("w3"), inp.get("w3_scale"), inp.get("b3"))
     return Experts.stacked(inp["w1"], inp.get("b1"), inp["w2"],
-                           inp.get("b2"))
+                           inp.get("b2"), inp.get("w3"), inp.get("b3"))
 
 
 def shared_of(inp: dict):
-    """(Ws1, bs1, Ws2, bs2) of the shared expert, or None."""
+    """(Ws1, bs1, Ws2, bs2[, Ws3, bs3]) of the shared expert, or None."""
     if inp.get("ws1") is None:
         return None
-    if inp.get("ws1_scale") is not None:
-        return (fp8_dequant(inp["ws1"], inp["ws1_scale"]), inp.get("bs1"),
-                fp8_dequant(inp["ws2"], inp["ws2_scale"]), inp.get("bs2"))
-    return (inp["ws1"], inp.get("bs1"), inp["ws2"], inp.get("bs2"))
+    f8 = inp.get("ws1_scale") is not None
+    deq = (lambda q, key: fp8_dequant(q, inp[key])) if f8 else \
+        (lambda q, key: q)
+    parts = (deq(inp["ws1"], "ws1_scale"), inp.get("bs1"),
+             deq(inp["ws2"], "ws2_scale"), inp.get("bs2"))
+    if inp.get("ws3") is not None:
+        parts += (deq(inp["ws3"], "ws3_scale"), inp.get("bs3"))
+    return parts
 
 
 def _weight_tables(need, experts: Experts, dt: int, shared):
@@ -293,7 +316,7 @@ def _weight_tables(need, experts: Experts, dt: int, shared):
     and the converted arrays that must stay alive during the call."""
     E = experts.E
     keep = []
-    tabs = [(_vp * E)() for _ in range(4)]
+    tabs = [(_vp * E)() for _ in range(6)]     # w1, b1, w2, b2, w3, b3
     d_ff = None
     wdt = set()
 
@@ -301,7 +324,7 @@ def _weight_tables(need, experts: Experts, dt: int, shared):
         ra, rdt = _raw(a)
         if ra is None:
             return None
-        if i in (0, 2):
+        if i in (0, 2, 4):
             assert rdt in (dt, 3), "weights must be x's dtype or float64"
             wdt.add(rdt)
         else:
@@ -316,24 +339,33 @@ def _weight_tables(need, experts: Experts, dt: int, shared):
             if ptr is not None:
                 tabs[i][e] = ptr
         d_ff = parts[0].shape[0]
-    sh = [None] * 4
+    sh = [None] * 6
     if shared is not None:
         for i, a in enumerate(shared):
             sh[i] = put(i, a)
         d_ff = shared[0].shape[0]
-    for i in (1, 3):
+    for i in (1, 3, 4, 5):
         if not any(tabs[i][e] for e in range(E)):
             tabs[i] = None
     assert len(wdt) <= 1, "all weight matrices must share a dtype"
     wd = wdt.pop() if wdt else dt
-    return tabs, sh, (1 if d_ff is None else d_ff), wd, keep
+    # C order: w1, b1, w3, b3, w2, b2
+    order = (0, 1, 4, 5, 2, 3)
+    return ([tabs[i] for i in order], [sh[i] for i in order],
+            (1 if d_ff is None else d_ff), wd, keep)
+
+
+def _act(activation: str) -> int:
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"unknown activation {activation!r}")
+    return ACTIVATIONS[activation]
 
 
 def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
-               shared=None) -> np.ndarray:
+               shared=None, activation: str = "gelu") -> np.ndarray:
     """Layer output rows y[tokens] (float64 [n, d]) for the given routing.
     ``slot_of`` None means every assignment is kept.  ``shared`` is
-    ``(Ws1, bs1, Ws2, bs2)`` or None."""
+    ``(Ws1, bs1, Ws2, bs2[, Ws3, bs3])`` or None."""
     tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
     xa, dt = _raw(x)
     T, d = xa.shape
@@ -350,7 +382,8 @@ def layer_rows(tokens: Sequence[int], x, idx, w, slot_of, experts: Experts,
     tabs, sh, d_ff, wd, keep = _weight_tables(need, experts, dt, shared)
     y = np.zeros((len(tokens), d), np.float64)
     rc = lib().oracle_layer_rows(
-        len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, wd, xa.ctypes.data,
+        len(tokens), _p(tokens, _i32p), d, k, d_ff, dt, wd, _act(activation),
+        xa.ctypes.data,
         _p(idx, _i32p), _p(w, _f64p), _p(so, _i32p), *tabs, *sh,
         _p(y, _f64p))
     if rc != 0:
@@ -379,7 +412,7 @@ def expert_choice(logits: np.ndarray, probs: np.ndarray, C: int) -> dict:
 
 
 def expert_choice_rows(tokens, x, gate: np.ndarray, experts: "Experts",
-                       shared=None) -> np.ndarray:
+                       shared=None, activation: str = "gelu") -> np.ndarray:
     """Expert-Choice layer output rows y[tokens] (float64 [n, d])."""
     tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
     xa, dt = _raw(x)
@@ -392,7 +425,8 @@ def expert_choice_rows(tokens, x, gate: np.ndarray, experts: "Experts",
     tabs, sh, d_ff, wd, keep = _weight_tables(need, experts, dt, shared)
     y = np.zeros((len(tokens), d), np.float64)
     rc = lib().oracle_expert_choice_rows(
-        len(tokens), _p(tokens, _i32p), d, E, d_ff, dt, wd, xa.ctypes.data,
+        len(tokens), _p(tokens, _i32p), d, E, d_ff, dt, wd, _act(activation),
+        xa.ctypes.data,
         _p(gate, _f64p), *tabs, *sh, _p(y, _f64p))
     if rc != 0:
         raise RuntimeError(f"oracle_expert_choice_rows failed ({rc})")
@@ -417,7 +451,8 @@ def _selection_from_slots(slot_token: np.ndarray, probs: np.ndarray,
 
 def forward_expert_choice(inp: dict, capacity: int, alpha: float = 0.01,
                           tokens: Optional[Sequence[int]] = None,
-                          selection: Optional[np.ndarray] = None) -> dict:
+                          selection: Optional[np.ndarray] = None,
+                          activation: str = "gelu") -> dict:
     """The Expert-Choice layer step by step.
 
     Every token is a candidate of every expert, so the routing statistics
@@ -442,7 +477,8 @@ def forward_expert_choice(inp: dict, capacity: int, alpha: float = 0.01,
         tokens = np.arange(T, dtype=np.int32)
     experts = experts_of(inp)
     shared = shared_of(inp)
-    y = expert_choice_rows(tokens, x, ec["gate"], experts, shared)
+    y = expert_choice_rows(tokens, x, ec["gate"], experts, shared,
+                           activation)
     out = dict(logits=logits, probs=probs, counts=counts, kept=kept,
                offsets=offsets, f=f, p=p, l_aux=l_aux, monitor=mon, y=y,
                tokens=np.asarray(tokens, dtype=np.int32), capacity=capacity)
@@ -480,11 +516,14 @@ def bias_update(counts, target: float, gamma: float, bias) -> np.ndarray:
 def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
             alpha: float = 0.01, tokens: Optional[Sequence[int]] = None,
             selection: Optional[np.ndarray] = None,
-            probs: Optional[np.ndarray] = None) -> dict:
+            probs: Optional[np.ndarray] = None,
+            activation: str = "gelu") -> dict:
     """The whole layer, step by step, as the pages define it.
 
     ``inp`` holds x, wr, br, ebias, w1, b1, w2, b2, ws1, bs1, ws2, bs2 (the
-    dict the workload generator returns).  ``tokens`` restricts the costly
+    dict the workload generator returns; w3/b3 and ws3/bs3 for SwiGLU, the
+    *_scale arrays for FP8 experts).  ``activation`` is "gelu", "silu" or
+    "swiglu".  ``tokens`` restricts the costly
     expert evaluation to some rows (routing, counts and statistics always
     cover every token).  ``selection`` replaces the oracle's own top-k
     choice (a checker adopting equally valid picks at near-ties); the
@@ -508,7 +547,8 @@ def forward(inp: dict, k: int, capacity_factor: Optional[float] = None,
         tokens = np.arange(T, dtype=np.int32)
     experts = experts_of(inp)
     shared = shared_of(inp)
-    y = layer_rows(tokens, x, idx, w, disp["slot_of"], experts, shared)
+    y = layer_rows(tokens, x, idx, w, disp["slot_of"], experts, shared,
+                   activation)
     out = dict(probs=probs, logits=logits, topk_idx=idx, topk_w=w,
                margin=margin, capacity=cap, f=f, p=p, l_aux=l_aux, y=y,
                tokens=np.asarray(tokens, dtype=np.int32))

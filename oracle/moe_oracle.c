@@ -257,15 +257,24 @@ void oracle_stats(int T, int E, int k, const double *probs,
     *l_aux = alpha * (double)E * acc;
 }
 
+/* Activation of the expert's hidden units.
+ *   act 0  GELU(z) = z/2 (1 + erf(z/sqrt 2))  ([GROUP] sec. 3.1; [SKILL]
+ *          sec. 3.1 Linear, GELU, Linear)
+ *   act 1  SiLU(z) = z / (1 + e^-z)           ([SKILL] sec. 6.1 Mixtral
+ *          block code: Linear, SiLU, Linear)
+ *   act 2  SwiGLU: SiLU(gate) * up, gate = W1 x + b1, up = W3 x + b3
+ *          ([SKILL] sec. 6.1 text: the Mixtral expert uses SwiGLU) */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
 /* One expert applied to one token:
- *   h = GELU(W1 x + b1),  out = W2 h + b2,  GELU(z) = z/2 (1 + erf(z/sqrt 2))
- * [GROUP] sec. 3.1 (FFN(x) = W2 GELU(W1 x + b1) + b2); [SKILL] sec. 3.1
- * (Linear(h, 4h), GELU, Linear(4h, h)).  W1 is [d_ff][d] and W2 is
- * [d][d_ff], the nn.Linear weight layout.  b1 and b2 may be NULL. */
-static void expert_apply(int d, int d_ff, int dtype, int wdtype,
+ *   z = W1 x + b1;  h = GELU(z) | SiLU(z) | SiLU(z) * (W3 x + b3)
+ *   out = W2 h + b2
+ * W1 and W3 are [d_ff][d], W2 is [d][d_ff] (nn.Linear layout); biases
+ * may be NULL; w3 is used only by act 2. */
+static void expert_apply(int d, int d_ff, int dtype, int wdtype, int act,
                          const double *xrow, const void *w1, const void *b1,
-                         const void *w2, const void *b2, double *h,
-                         double *out)
+                         const void *w3, const void *b3, const void *w2,
+                         const void *b2, double *h, double *out)
 {
     for (int f = 0; f < d_ff; ++f) {
         double z = 0.0;
@@ -273,7 +282,18 @@ static void expert_apply(int d, int d_ff, int dtype, int wdtype,
             z += ld(w1, (size_t)f * d + c, wdtype) * xrow[c];
         if (b1)
             z += ld(b1, (size_t)f, dtype);
-        h[f] = 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+        if (act == 0) {
+            h[f] = 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+        } else if (act == 1) {
+            h[f] = silu(z);
+        } else {
+            double u = 0.0;
+            for (int c = 0; c < d; ++c)
+                u += ld(w3, (size_t)f * d + c, wdtype) * xrow[c];
+            if (b3)
+                u += ld(b3, (size_t)f, dtype);
+            h[f] = silu(z) * u;
+        }
     }
     for (int c = 0; c < d; ++c) {
         double o = 0.0;
@@ -299,13 +319,15 @@ static void expert_apply(int d, int d_ff, int dtype, int wdtype,
  * in dtype.  slot_of may be NULL (no capacity limit: every assignment is
  * kept).  ws1 == NULL means no shared expert.  y is [n][d] double. */
 int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
-                      int dtype, int wdtype, const void *x,
+                      int dtype, int wdtype, int act, const void *x,
                       const int32_t *idx,
                       const double *w, const int32_t *slot_of,
                       const void *const *w1, const void *const *b1,
+                      const void *const *w3, const void *const *b3,
                       const void *const *w2, const void *const *b2,
-                      const void *ws1, const void *bs1, const void *ws2,
-                      const void *bs2, double *y)
+                      const void *ws1, const void *bs1, const void *ws3,
+                      const void *bs3, const void *ws2, const void *bs2,
+                      double *y)
 {
     int status = OR_OK;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -324,19 +346,20 @@ int oracle_layer_rows(int n, const int32_t *tokens, int d, int k, int d_ff,
             if (slot_of && slot_of[a] < 0)
                 continue;
             int e = idx[a];
-            if (!w1[e] || !w2[e]) {
+            if (!w1[e] || !w2[e] || (act == 2 && !w3[e])) {
 #pragma omp atomic write
                 status = OR_ERR_MISSING_EXPERT;
                 continue;
             }
-            expert_apply(d, d_ff, dtype, wdtype, xrow, w1[e],
-                         b1 ? b1[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, act, xrow, w1[e],
+                         b1 ? b1[e] : NULL, w3 ? w3[e] : NULL,
+                         b3 ? b3[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += w[a] * o[c];
         }
         if (ws1) {
-            expert_apply(d, d_ff, dtype, wdtype, xrow, ws1, bs1, ws2, bs2, h,
-                         o);
+            expert_apply(d, d_ff, dtype, wdtype, act, xrow, ws1, bs1, ws3,
+                         bs3, ws2, bs2, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += o[c];
         }
@@ -406,12 +429,14 @@ int oracle_expert_choice(int T, int E, int C, const double *logits,
  *         gate[t,e] * Expert_e(x_t)   (+ Shared(x_t))
  * A token no expert picked gets 0 (plus the shared expert). */
 int oracle_expert_choice_rows(int n, const int32_t *tokens, int d, int E,
-                              int d_ff, int dtype, int wdtype, const void *x,
-                              const double *gate, const void *const *w1,
-                              const void *const *b1, const void *const *w2,
-                              const void *const *b2, const void *ws1,
-                              const void *bs1, const void *ws2,
-                              const void *bs2, double *y)
+                              int d_ff, int dtype, int wdtype, int act,
+                              const void *x, const double *gate,
+                              const void *const *w1, const void *const *b1,
+                              const void *const *w3, const void *const *b3,
+                              const void *const *w2, const void *const *b2,
+                              const void *ws1, const void *bs1,
+                              const void *ws3, const void *bs3,
+                              const void *ws2, const void *bs2, double *y)
 {
     int status = OR_OK;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -429,19 +454,20 @@ int oracle_expert_choice_rows(int n, const int32_t *tokens, int d, int E,
             const double g = gate[(size_t)t * E + e];
             if (g == 0.0)
                 continue;
-            if (!w1[e] || !w2[e]) {
+            if (!w1[e] || !w2[e] || (act == 2 && !w3[e])) {
 #pragma omp atomic write
                 status = OR_ERR_MISSING_EXPERT;
                 continue;
             }
-            expert_apply(d, d_ff, dtype, wdtype, xrow, w1[e],
-                         b1 ? b1[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
+            expert_apply(d, d_ff, dtype, wdtype, act, xrow, w1[e],
+                         b1 ? b1[e] : NULL, w3 ? w3[e] : NULL,
+                         b3 ? b3[e] : NULL, w2[e], b2 ? b2[e] : NULL, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += g * o[c];
         }
         if (ws1) {
-            expert_apply(d, d_ff, dtype, wdtype, xrow, ws1, bs1, ws2, bs2, h,
-                         o);
+            expert_apply(d, d_ff, dtype, wdtype, act, xrow, ws1, bs1, ws3,
+                         bs3, ws2, bs2, h, o);
             for (int c = 0; c < d; ++c)
                 yr[c] += o[c];
         }

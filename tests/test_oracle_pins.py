@@ -647,3 +647,80 @@ def test_fp8_layer_equals_bf16_layer_on_representable_weights():
     b = oracle.forward(f8, k=2)
     assert np.array_equal(a["y"], b["y"])
     assert np.any(a["y"] != 0)
+
+
+# ------------------------------------------------- SiLU / SwiGLU experts
+def test_silu_textbook_values():
+    # one hidden unit, identity read-out: y = SiLU(z) = z * sigma(z)
+    zs = np.array([-3.0, -1.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    x = zs[:, None]
+    one = np.ones((1, 1), np.float32)
+    ex = oracle.Experts(1, lambda e: (one, None, one, None))
+    y = oracle.layer_rows(range(len(zs)), x, np.zeros((6, 1), np.int32),
+                          np.ones((6, 1)), None, ex, activation="silu")
+    sigma = np.array([0.04742587317756678, 0.2689414213699951, 0.5,
+                      0.6224593312018546, 0.7310585786300049,
+                      0.8807970779778823])          # logistic function
+    assert np.allclose(y[:, 0], zs * sigma, rtol=1e-13, atol=1e-15)
+
+
+def _dense(x, w1, b1, w2, b2, w3=None, b3=None, act="gelu"):
+    f = lambda a: None if a is None else torch.as_tensor(a).double()
+    z = torch.nn.functional.linear(f(x), f(w1), f(b1))
+    if act == "silu":
+        h = torch.nn.functional.silu(z)
+    else:
+        h = torch.nn.functional.silu(z) * torch.nn.functional.linear(
+            f(x), f(w3), f(b3))
+    return torch.nn.functional.linear(h, f(w2), f(b2)).numpy()
+
+
+def test_single_expert_silu_and_swiglu_are_torch_ffns():
+    for act in ("silu", "swiglu"):
+        w = workloads.Workload(name="t", T=16, d=8, E=1, k=1, d_ff=12,
+                               dtype="f32", linear_biases=True,
+                               activation=act, seed=4)
+        inp = workloads.make_inputs(w)
+        out = oracle.forward(inp, k=1, activation=act)
+        ref = _dense(inp["x"], inp["w1"][0], inp["b1"][0], inp["w2"][0],
+                     inp["b2"][0], None if act == "silu" else inp["w3"][0],
+                     None if act == "silu" else inp["b3"][0], act)
+        assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13), act
+
+
+def test_swiglu_with_unit_up_projection_is_silu():
+    # W3 = 0, b3 = 1: the up branch is 1, so SwiGLU reduces to SiLU
+    # exactly; a swapped gate/up (SiLU on the up branch) gives SiLU(1)*z
+    w = workloads.Workload(name="t", T=20, d=8, E=3, k=2, d_ff=12,
+                           dtype="f32", linear_biases=True,
+                           activation="swiglu", seed=6)
+    inp = workloads.make_inputs(w)
+    inp["w3"] = torch.zeros_like(inp["w3"])
+    inp["b3"] = torch.ones_like(inp["b3"])
+    a = oracle.forward(inp, k=2, activation="swiglu")
+    b = oracle.forward(inp, k=2, activation="silu")
+    assert np.array_equal(a["y"], b["y"])
+    c = oracle.forward(inp, k=2, activation="gelu")
+    assert not np.allclose(a["y"], c["y"])
+
+
+def test_swiglu_shared_expert_and_fp8_up_projection():
+    # the shared expert is gated too; FP8 W3 dequantises like W1
+    w = workloads.Workload(name="t", T=12, d=1024, E=2, k=1, d_ff=1024,
+                           dtype="bf16", n_shared=1, activation="swiglu",
+                           expert_fp8=True, seed=7)
+    inp = workloads.make_inputs(w)
+    out = oracle.forward(inp, k=1, activation="swiglu",
+                         tokens=np.array([0, 5], np.int32))
+    x = inp["x"][[0, 5]].float()
+    deq = lambda q, s: oracle.fp8_dequant(q, s)
+    e = out["topk_idx"][[0, 5], 0]
+    ref = np.stack([
+        _dense(x[i:i + 1], deq(inp["w1"][e[i]], inp["w1_scale"][e[i]]), None,
+               deq(inp["w2"][e[i]], inp["w2_scale"][e[i]]), None,
+               deq(inp["w3"][e[i]], inp["w3_scale"][e[i]]), None,
+               "swiglu")[0] for i in range(2)])
+    ref += _dense(x, deq(inp["ws1"], inp["ws1_scale"]), None,
+                  deq(inp["ws2"], inp["ws2_scale"]), None,
+                  deq(inp["ws3"], inp["ws3_scale"]), None, "swiglu")
+    assert np.allclose(out["y"], ref, rtol=1e-10, atol=1e-10)

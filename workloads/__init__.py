@@ -53,6 +53,7 @@ class Workload:
     calls: int = 1              # distinct x per timed run (decode)
     routing: str = "topk"       # "topk" | "expert_choice" (then k == E)
     expert_fp8: bool = False    # expert matrices stored as E4M3 + scales
+    activation: str = "gelu"    # "gelu" | "silu" | "swiglu" (adds W3, b3)
     seed: int = 0
 
     @property
@@ -157,6 +158,19 @@ def make_expert(w: Workload, e: int, device="cpu", shared: bool = False):
     return w1, b1, w2, b2
 
 
+def make_expert_up3(w: Workload, e: int, device="cpu", shared: bool = False):
+    """The SwiGLU up projection of one expert: (W3[d_ff,d], b3[d_ff] | None),
+    from streams of its own."""
+    tag = "s" if shared else "r"
+    w3 = _normal((w.d_ff, w.d), 1.0 / w.d, w.seed, tag + "w3", e, device,
+                 w.torch_dtype)
+    b3 = None
+    if w.linear_biases:
+        b3 = _normal((w.d_ff,), w.bias_var, w.seed, tag + "b3", e, device,
+                     w.torch_dtype)
+    return w3, b3
+
+
 def quantize_e4m3(wt: torch.Tensor):
     """Checkpoint conversion of one [N, K] matrix to FP8: per-row scale
     amax / 448 (1 for an all-zero row) and E4M3 codes of w / scale by
@@ -220,9 +234,22 @@ def make_inputs(w: Workload, device="cpu", call: int = 0) -> dict:
             b2[e].copy_(eb2)
         del e1, e2
     out.update(w1=w1, b1=b1, w2=w2, b2=b2)
+    if w.activation == "swiglu":
+        w3 = torch.empty((w.E, w.d_ff, w.d), device=device, dtype=dt)
+        b3 = torch.empty((w.E, w.d_ff), device=device, dtype=dt) \
+            if w.linear_biases else None
+        for e in range(w.E):
+            e3, eb3 = make_expert_up3(w, e, device)
+            w3[e].copy_(e3)
+            if b3 is not None:
+                b3[e].copy_(eb3)
+        out.update(w3=w3, b3=b3)
     if w.n_shared:
         s1, sb1, s2, sb2 = make_expert(w, 0, device, shared=True)
         out.update(ws1=s1, bs1=sb1, ws2=s2, bs2=sb2)
+        if w.activation == "swiglu":
+            s3, sb3 = make_expert_up3(w, 0, device, shared=True)
+            out.update(ws3=s3, bs3=sb3)
     else:
         out.update(ws1=None, bs1=None, ws2=None, bs2=None)
     return out
@@ -255,12 +282,29 @@ def _fp8_experts(w: Workload, device, out: dict) -> dict:
             b2[e].copy_(eb2)
         del e1, e2, q
     out.update(w1=w1, b1=b1, w2=w2, b2=b2, w1_scale=s1, w2_scale=s2)
+    if w.activation == "swiglu":
+        w3 = torch.empty((w.E, w.d_ff, w.d), device=device, dtype=u8)
+        s3 = torch.empty((w.E, w.d_ff), device=device, dtype=f32)
+        b3 = torch.empty((w.E, w.d_ff), device=device, dtype=dt) \
+            if w.linear_biases else None
+        for e in range(w.E):
+            e3, eb3 = make_expert_up3(w, e, device)
+            q, sc = quantize_e4m3(e3)
+            w3[e].copy_(q)
+            s3[e].copy_(sc)
+            if b3 is not None:
+                b3[e].copy_(eb3)
+        out.update(w3=w3, b3=b3, w3_scale=s3)
     if w.n_shared:
         e1, sb1, e2, sb2 = make_expert(w, 0, device, shared=True)
         q1, t1 = quantize_e4m3(e1)
         q2, t2 = quantize_e4m3(e2)
         out.update(ws1=q1, bs1=sb1, ws2=q2, bs2=sb2, ws1_scale=t1,
                    ws2_scale=t2)
+        if w.activation == "swiglu":
+            e3, sb3 = make_expert_up3(w, 0, device, shared=True)
+            q3, t3 = quantize_e4m3(e3)
+            out.update(ws3=q3, bs3=sb3, ws3_scale=t3)
     else:
         out.update(ws1=None, bs1=None, ws2=None, bs2=None)
     return out
