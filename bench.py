@@ -80,15 +80,16 @@ def algorithmic(wl, counts, kept):
     es = wl.elem_bytes
     ew = 1 if wl.expert_fp8 else es        # bytes per expert-matrix weight
     sc = 4 if wl.expert_fp8 else 0         # fp32 scale per output channel
+    nu = 2 if wl.activation == "swiglu" else 1   # up matrices (W1[, W3])
     rows = int(np.sum(kept)) + wl.n_shared * wl.T     # expert GEMM rows
     touched = int(np.sum(kept > 0)) + wl.n_shared
-    flops = 2.0 * wl.T * wl.d * wl.E + 4.0 * rows * wl.d * wl.d_ff
-    expert_bytes = (2 * wl.d * wl.d_ff * ew + (wl.d + wl.d_ff) * sc +
-                    (wl.d + wl.d_ff if wl.linear_biases else 0) * es)
+    flops = 2.0 * wl.T * wl.d * wl.E + 2.0 * (nu + 1) * rows * wl.d * wl.d_ff
+    expert_bytes = ((nu + 1) * wl.d * wl.d_ff * ew + (wl.d + nu * wl.d_ff) * sc
+                    + (wl.d + nu * wl.d_ff if wl.linear_biases else 0) * es)
     bytes_ = (wl.E * wl.d * es + touched * expert_bytes +
               2 * wl.T * wl.d * es)
-    up_flops = 2.0 * rows * wl.d * wl.d_ff
-    up_bytes = (touched * wl.d_ff * (wl.d * ew + sc) +
+    up_flops = 2.0 * nu * rows * wl.d * wl.d_ff
+    up_bytes = (nu * touched * wl.d_ff * (wl.d * ew + sc) +
                 rows * (wl.d + wl.d_ff) * es)
     return dict(flops=flops, bytes=bytes_, rows=rows, touched=touched,
                 up_flops=up_flops, up_bytes=up_bytes)
@@ -113,9 +114,11 @@ def cpu_baseline(wl, inp, budget_s):
         t0 = time.perf_counter()
         if wl.routing == "expert_choice":
             C = min(n, oracle.capacity(n, wl.E, wl.capacity_factor))
-            oracle.forward_expert_choice(sub, C, wl.alpha)
+            oracle.forward_expert_choice(sub, C, wl.alpha,
+                                         activation=wl.activation)
         else:
-            oracle.forward(sub, wl.k, wl.capacity_factor, wl.alpha)
+            oracle.forward(sub, wl.k, wl.capacity_factor, wl.alpha,
+                           activation=wl.activation)
         return time.perf_counter() - t0
 
     n = min(wl.T, max(1, cores))
@@ -170,7 +173,7 @@ def main():
     xs = [inp["x"]] + [workloads.make_x(wl, dev, c) for c in range(1, n_x)]
     weights = moe.Weights.from_dict(inp)
     layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha,
-                         routing=wl.routing)
+                         routing=wl.routing, activation=wl.activation)
     desc, r, ws, y = layer.buffers(wl.T)
     stream = torch.cuda.current_stream(dev)
 
@@ -254,6 +257,7 @@ def main():
                    "capacity_factor": wl.capacity_factor,
                    "routing": wl.routing,
                    "expert_weights": "e4m3" if wl.expert_fp8 else wl.dtype,
+                   "activation": wl.activation,
                    "parallelism": "single-gpu"},
         "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
         "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),

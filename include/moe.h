@@ -12,7 +12,10 @@
  *      token-order dispatch; overflow assignments skip the expert
  *      ("MoE architecture deep dive", sec. 2.3);
  *   4. each expert: W2 GELU(W1 x + b1) + b2 with exact erf GELU
- *      ("The expert group activated per token", sec. 3.1 FFN formula);
+ *      ("The expert group activated per token", sec. 3.1 FFN formula), or
+ *      with SiLU, or gated: W2 (SiLU(W1 x + b1) * (W3 x + b3)) + b2
+ *      (SwiGLU) ("AI-Research-SKILLs MoE training guide", sec. 6.1
+ *      Mixtral block: its code uses Linear, SiLU, Linear, its text SwiGLU);
  *      optional always-on shared expert ("MoE architecture deep dive",
  *      sec. 3, DeepSeek-V3 shared expert);
  *   5. y[t] = sum_j w[t,j] Expert_{idx[t,j]}(x[t]) (+ Shared(x[t]))
@@ -87,6 +90,12 @@ typedef enum {
     MOE_ROUTE_EXPERT_CHOICE = 1  /* experts choose C tokens */
 } moe_routing_mode;
 
+typedef enum {
+    MOE_ACT_GELU = 0,    /* h = GELU(W1 x + b1), exact erf form */
+    MOE_ACT_SILU = 1,    /* h = SiLU(W1 x + b1), SiLU(z) = z / (1 + e^-z) */
+    MOE_ACT_SWIGLU = 2   /* h = SiLU(W1 x + b1) * (W3 x + b3) */
+} moe_activation;
+
 /* Layer shape, host struct passed by pointer.
  *   T         tokens (>= 0)
  *   d         model width; multiple of 64
@@ -109,7 +118,9 @@ typedef enum {
  *             biases and y stay bf16.  The pages quote FP8 serving of the
  *             Mixtral layer ("MoE inference with vLLM"; "AI-Research-
  *             SKILLs MoE training guide", sec. 9); its target is the
- *             weight-streaming decode shape, whose bytes it halves. */
+ *             weight-streaming decode shape, whose bytes it halves.
+ *   activation a moe_activation (applies to routed and shared experts);
+ *             MOE_ACT_SWIGLU needs d_ff a multiple of 128 for bf16 */
 typedef struct moe_desc {
     int32_t T, d, E, k, d_ff;
     int32_t n_shared;
@@ -118,6 +129,7 @@ typedef struct moe_desc {
     float aux_alpha;
     int32_t routing;
     int32_t expert_fp8;
+    int32_t activation;
 } moe_desc;
 
 /* Weights: caller-owned, read-only device buffers; NULL = absent.
@@ -133,7 +145,11 @@ typedef struct moe_desc {
  *               required iff n_shared == 1
  *   w1_scale    [E][d_ff] fp32, w2_scale [E][d], ws1_scale [d_ff],
  *   ws2_scale   [d]: per-output-channel scales of FP8 expert matrices
- *               (required iff expert_fp8, for the matrices present) */
+ *               (required iff expert_fp8, for the matrices present)
+ *   w3, b3      [E][d_ff][d], [E][d_ff]  SwiGLU up projection (w3
+ *               required iff activation == MOE_ACT_SWIGLU); ws3, bs3 the
+ *               shared expert's; w3_scale [E][d_ff], ws3_scale [d_ff] for
+ *               FP8.  W1 is then the gate projection. */
 typedef struct moe_weights {
     const void *w_router;
     const float *b_router;
@@ -142,6 +158,8 @@ typedef struct moe_weights {
     const void *w2, *b2;
     const void *ws1, *bs1, *ws2, *bs2;
     const float *w1_scale, *w2_scale, *ws1_scale, *ws2_scale;
+    const void *w3, *b3, *ws3, *bs3;
+    const float *w3_scale, *ws3_scale;
 } moe_weights;
 
 /* Routing results and statistics: caller-owned device buffers.
@@ -225,7 +243,8 @@ int moe_grouped_ffn(const moe_desc *desc, const void *x,
                     size_t ws_bytes, void *stream);
 
 /* First half of moe_grouped_ffn: H[s] = GELU(W1_e x[token(s)] + b1_e)
- * into the workspace (one kernel launch). */
+ * (or the SiLU / SwiGLU form of desc->activation) into the workspace (one
+ * kernel launch). */
 int moe_ffn_up(const moe_desc *desc, const void *x, const moe_weights *w,
                const moe_routing *r, void *ws, size_t ws_bytes,
                void *stream);

@@ -25,13 +25,17 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_ROUTE_TOPK = 0
 MOE_ROUTE_EXPERT_CHOICE = 1
+MOE_ACT_GELU = 0
+MOE_ACT_SILU = 1
+MOE_ACT_SWIGLU = 2
 
 
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("k", c_i32),
                 ("d_ff", c_i32), ("n_shared", c_i32), ("dtype", c_i32),
                 ("capacity", c_i32), ("aux_alpha", ctypes.c_float),
-                ("routing", c_i32), ("expert_fp8", c_i32)]
+                ("routing", c_i32), ("expert_fp8", c_i32),
+                ("activation", c_i32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -39,7 +43,9 @@ class MoeWeights(ctypes.Structure):
                 ("expert_bias", c_vp), ("w1", c_vp), ("b1", c_vp),
                 ("w2", c_vp), ("b2", c_vp), ("ws1", c_vp), ("bs1", c_vp),
                 ("ws2", c_vp), ("bs2", c_vp), ("w1_scale", c_vp),
-                ("w2_scale", c_vp), ("ws1_scale", c_vp), ("ws2_scale", c_vp)]
+                ("w2_scale", c_vp), ("ws1_scale", c_vp), ("ws2_scale", c_vp),
+                ("w3", c_vp), ("b3", c_vp), ("ws3", c_vp), ("bs3", c_vp),
+                ("w3_scale", c_vp), ("ws3_scale", c_vp)]
 
 
 class MoeRouting(ctypes.Structure):

@@ -137,6 +137,45 @@ struct GemmParams {
     void *out;                // [slots][N]
     const float *scale;       // FP8 weights: per-output-channel [E][N]
     const float *scale_s;     // FP8 shared expert [N]
+    // SwiGLU up GEMM (gated != 0): W is the gate matrix W1 and W3 the up
+    // matrix, both [E][N/2][K]; the N = 2*d_ff columns are a virtual panel
+    // of 64-row chunks (32 rows of W1, then the same 32 rows of W3), and
+    // the output holds N/2 features per row
+    const void *W3, *bias3, *Ws3, *bias_s3;
+    const float *scale3, *scale_s3;
     int E, n_shared, T, shared_base;
     int N, K;
+    int act;                  // up epilogue: ACT_GELU, ACT_SILU, ACT_SWIGLU
+    int gated;                // 1 for the SwiGLU up GEMM
+    int ldo;                  // output row stride (elements)
 };
+
+enum { ACT_GELU = 0, ACT_SILU = 1, ACT_SWIGLU = 2 };
+
+__device__ __forceinline__ float silu_f(float z) {
+    return z / (1.0f + expf(-z));
+}
+
+// Activation of an ungated up GEMM output.
+__device__ __forceinline__ float act_up(int act, float z) {
+    return act == ACT_SILU ? silu_f(z) : gelu_erf(z);
+}
+
+// Start of weight row v (elements of esz bytes) of group g's panel; for a
+// gated up GEMM v indexes the interleaved W1 / W3 panel.
+__device__ __forceinline__ const char *weight_row(const GemmParams &p,
+                                                  bool routed, int g, int v,
+                                                  int esz) {
+    if (!p.gated) {
+        const char *W = routed ? (const char *)p.W + (size_t)g * p.N * p.K * esz
+                               : (const char *)p.Ws;
+        return W + (size_t)v * p.K * esz;
+    }
+    const int F = p.N >> 1;
+    const int c = v >> 6, r = v & 63;
+    const size_t row = (size_t)(32 * c + (r & 31));
+    const char *base = r < 32 ? (const char *)(routed ? p.W : p.Ws)
+                              : (const char *)(routed ? p.W3 : p.Ws3);
+    if (routed) base += (size_t)g * F * p.K * esz;
+    return base + row * p.K * esz;
+}

@@ -34,13 +34,13 @@ constexpr int BK = 64;
 template <int AC, int BC>
 __device__ __forceinline__ void tile_gload(u32x4 (&ra)[AC], u32x4 (&rb)[BC],
                                            const uint16_t *A,
-                                           const uint16_t *Wg,
                                            const int (&aoff)[AC],
-                                           const int (&boff)[BC], int ko) {
+                                           const uint16_t *const (&bp)[BC],
+                                           int ko) {
 #pragma unroll
     for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4 *)(A + aoff[i] + ko);
 #pragma unroll
-    for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4 *)(Wg + boff[i] + ko);
+    for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4 *)(bp[i] + ko);
 }
 
 // Registers -> one LDS stage; chunk c of row r lands at r*8 + (c ^ (r/2 % 8)).
@@ -96,6 +96,96 @@ __device__ __forceinline__ void mfma_block(floatx16 (&acc)[TM][TN],
                                                                acc[i][j], 0, 0, 0);
 }
 
+// Epilogue of the 32x32-MFMA tile kernels.  The lane holds row
+// m = lane%32 of each 32x32 block and features 8*q + 4*(lane/32) + 0..3
+// (q = 0..3).  Ungated: bias, then GELU or SiLU on the up pass, one 8-byte
+// store per q.  Gated (SwiGLU up pass): blocks j and j+1 of a wave are the
+// gate and up halves of one 64-column chunk c of the virtual panel, so the
+// lane forms SiLU(gate + b1) * (up + b3) for features 32*c + 8*q +
+// 4*(lane/32) + 0..3 itself (the host only picks tiles whose waves cover
+// whole 64-column chunks).
+template <int BM, int BN, int WM, int WN, int TM, int TN, bool UP>
+__device__ __forceinline__ void store_tile(const GemmParams &p,
+                                           const floatx16 (&acc)[TM][TN],
+                                           bool routed, int g, int row0,
+                                           int nrows, int n0, int wm, int wn,
+                                           int lane) {
+    uint16_t *out = (uint16_t *)p.out;
+    if (UP && p.gated) {
+        const int F = p.N >> 1;
+        const uint16_t *b1 = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const uint16_t *b3 = routed
+            ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s3;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+            if (m >= nrows) continue;
+            uint16_t *orow = out + (size_t)(row0 + m) * p.ldo;
+#pragma unroll
+            for (int j = 0; j + 1 < TN; j += 2) {
+                const int f0 = (n0 + wn * (BN / WN) + j * 32) >> 1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int f = f0 + 8 * q + 4 * (lane >> 5);
+                    float h[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float gv = acc[i][j][4 * q + r];
+                        float uv = acc[i][j + 1][4 * q + r];
+                        if (b1) gv += bf16_to_f32(b1[f + r]);
+                        if (b3) uv += bf16_to_f32(b3[f + r]);
+                        h[r] = silu_f(gv) * uv;
+                    }
+                    u32x2 o;
+                    o.x = pack_bf16x2(h[0], h[1]);
+                    o.y = pack_bf16x2(h[2], h[3]);
+                    *(u32x2 *)(orow + f) = o;
+                }
+            }
+        }
+        return;
+    }
+    const uint16_t *bg = routed
+        ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * p.N : nullptr)
+        : (const uint16_t *)p.bias_s;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+        if (m >= nrows) continue;
+        uint16_t *orow = out + (size_t)(row0 + m) * p.ldo;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
+                              4 * (lane >> 5);
+                float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                if (bg) {
+                    const u32x2 bb = *(const u32x2 *)(bg + n);
+                    v0 += bf16_lo(bb.x);
+                    v1 += bf16_hi(bb.x);
+                    v2 += bf16_lo(bb.y);
+                    v3 += bf16_hi(bb.y);
+                }
+                if (UP) {
+                    v0 = act_up(p.act, v0);
+                    v1 = act_up(p.act, v1);
+                    v2 = act_up(p.act, v2);
+                    v3 = act_up(p.act, v3);
+                }
+                u32x2 o;
+                o.x = pack_bf16x2(v0, v1);
+                o.y = pack_bf16x2(v2, v3);
+                *(u32x2 *)(orow + n) = o;
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, bool UP>
 __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
     constexpr int NT = WM * WN * 64;
@@ -135,12 +225,6 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
         const int nrows = min(BM, tt.rows[g] - m_tile * BM);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        const uint16_t *Wg = routed
-            ? (const uint16_t *)p.W + (size_t)g * N * K
-            : (const uint16_t *)p.Ws;
-        const uint16_t *bg = routed
-            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
-            : (const uint16_t *)p.bias_s;
 
         int aoff[AC];
 #pragma unroll
@@ -154,9 +238,12 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
                 aoff[i] = src * K + lc * 8;
             }
         }
-        int boff[BC];
+        const uint16_t *bp[BC];
 #pragma unroll
-        for (int i = 0; i < BC; ++i) boff[i] = (n0 + lrow + i * RPP) * K + lc * 8;
+        for (int i = 0; i < BC; ++i)
+            bp[i] = (const uint16_t *)weight_row(p, routed, g,
+                                                 n0 + lrow + i * RPP, 2) +
+                    lc * 8;
 
         floatx16 acc[TM][TN];
 #pragma unroll
@@ -172,7 +259,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
         // fragments of the next step are read right after the barrier,
         // under the last sub-step's MFMAs.
         u32x4 ra[AC], rb[BC];
-        tile_gload<AC, BC>(ra, rb, A, Wg, aoff, boff, 0);
+        tile_gload<AC, BC>(ra, rb, A, aoff, bp, 0);
         tile_sstore<AC, BC, BM, RPP>(ra, rb, smem, lrow, lc);
         __syncthreads();
         bf16x8 fa[2][TM], fb[2][TN];
@@ -181,7 +268,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
             const int cur = kt & 1;
             const bool more = kt + 1 < KT;
             if (more)
-                tile_gload<AC, BC>(ra, rb, A, Wg, aoff, boff, (kt + 1) * BK);
+                tile_gload<AC, BC>(ra, rb, A, aoff, bp, (kt + 1) * BK);
             const u32x4 *stage = smem + cur * STAGE;
 #pragma unroll
             for (int kk = 0; kk < BK / 16 - 1; ++kk) {
@@ -202,43 +289,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_lds(GemmParams p) {
             mfma_block<TM, TN>(acc, fa[LAST], fb[LAST]);
         }
         __syncthreads();   // LDS is reused by the next tile's prologue
-
-        // Epilogue.  Lane holds row m = lane%32 of each 32x32 tile and
-        // features 8*q + 4*(lane/32) + 0..3 for q = 0..3.
-        uint16_t *out = (uint16_t *)p.out;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
-            if (m >= nrows) continue;
-            uint16_t *orow = out + (size_t)(row0 + m) * N;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
-                                  4 * (lane >> 5);
-                    float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                    float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                    if (bg) {
-                        const u32x2 bb = *(const u32x2 *)(bg + n);
-                        v0 += bf16_lo(bb.x);
-                        v1 += bf16_hi(bb.x);
-                        v2 += bf16_lo(bb.y);
-                        v3 += bf16_hi(bb.y);
-                    }
-                    if (UP) {
-                        v0 = gelu_erf(v0);
-                        v1 = gelu_erf(v1);
-                        v2 = gelu_erf(v2);
-                        v3 = gelu_erf(v3);
-                    }
-                    u32x2 o;
-                    o.x = pack_bf16x2(v0, v1);
-                    o.y = pack_bf16x2(v2, v3);
-                    *(u32x2 *)(orow + n) = o;
-                }
-            }
-        }
+        store_tile<BM, BN, WM, WN, TM, TN, UP>(p, acc, routed, g, row0, nrows,
+                                               n0, wm, wn, lane);
     }
 }
 
@@ -332,16 +384,11 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
         const int nrows = min(BM, tt.rows[g] - m_tile * BM);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        const uint16_t *Wg = routed
-            ? (const uint16_t *)p.W + (size_t)g * N * K
-            : (const uint16_t *)p.Ws;
-        const uint16_t *bg = routed
-            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
-            : (const uint16_t *)p.bias_s;
 
-        // per-lane source offsets (elements) of each load instruction;
-        // tile rows past the group's end read row 0 and are never stored
-        int aoff[IA], boff[IB];
+        // per-lane sources of each load instruction; tile rows past the
+        // group's end read row 0 and are never stored
+        int aoff[IA];
+        const uint16_t *bp[IB];
 #pragma unroll
         for (int j = 0; j < IA; ++j) {
             const int rr = (wave + j * NW) * 16 + lr;
@@ -358,7 +405,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
         for (int j = 0; j < IB; ++j) {
             const int rr = (wave + j * NW) * 16 + lr;
             const int ch = lp ^ ((rr >> 2) & 3);
-            boff[j] = (n0 + rr) * K + ch * 8;
+            bp[j] = (const uint16_t *)weight_row(p, routed, g, n0 + rr, 2) +
+                    ch * 8;
         }
         auto issue = [&](int ks) __attribute__((always_inline)) {
             u32x4 *st = smem + (ks % NS) * STAGE;
@@ -368,7 +416,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
                 dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
 #pragma unroll
             for (int j = 0; j < IB; ++j)
-                dma16(Wg + boff[j] + ko, st + BM * 4 + (wave + j * NW) * 64);
+                dma16(bp[j] + ko, st + BM * 4 + (wave + j * NW) * 64);
         };
 
         floatx16 acc[TM][TN];
@@ -415,41 +463,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma(GemmParams p) {
             if (kt + 1 < KT) step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
         }
         __syncthreads();   // the ring is reused by the next tile
-
-        uint16_t *out = (uint16_t *)p.out;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
-            if (m >= nrows) continue;
-            uint16_t *orow = out + (size_t)(row0 + m) * N;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
-                                  4 * (lane >> 5);
-                    float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                    float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                    if (bg) {
-                        const u32x2 bb = *(const u32x2 *)(bg + n);
-                        v0 += bf16_lo(bb.x);
-                        v1 += bf16_hi(bb.x);
-                        v2 += bf16_lo(bb.y);
-                        v3 += bf16_hi(bb.y);
-                    }
-                    if (UP) {
-                        v0 = gelu_erf(v0);
-                        v1 = gelu_erf(v1);
-                        v2 = gelu_erf(v2);
-                        v3 = gelu_erf(v3);
-                    }
-                    u32x2 o;
-                    o.x = pack_bf16x2(v0, v1);
-                    o.y = pack_bf16x2(v2, v3);
-                    *(u32x2 *)(orow + n) = o;
-                }
-            }
-        }
+        store_tile<BM, BN, WM, WN, TM, TN, UP>(p, acc, routed, g, row0, nrows,
+                                               n0, wm, wn, lane);
     }
 }
 
@@ -501,14 +516,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
         const int nrows = min(BM, tt.rows[g] - m_tile * BM);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        const uint16_t *Wg = routed
-            ? (const uint16_t *)p.W + (size_t)g * N * K
-            : (const uint16_t *)p.Ws;
-        const uint16_t *bg = routed
-            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
-            : (const uint16_t *)p.bias_s;
 
-        int aoff[IA], boff[IB];
+        int aoff[IA];
+        const uint16_t *bp[IB];
 #pragma unroll
         for (int j = 0; j < IA; ++j) {
             const int rr = (wave + j * NW) * 8 + lr;
@@ -525,7 +535,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
         for (int j = 0; j < IB; ++j) {
             const int rr = (wave + j * NW) * 8 + lr;
             const int ch = lp ^ ((rr >> 1) & 7);
-            boff[j] = (n0 + rr) * K + ch * 8;
+            bp[j] = (const uint16_t *)weight_row(p, routed, g, n0 + rr, 2) +
+                    ch * 8;
         }
         auto issue = [&](int ks) __attribute__((always_inline)) {
             u32x4 *st = smem + (ks & 1) * STAGE;
@@ -535,7 +546,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
                 dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
 #pragma unroll
             for (int j = 0; j < IB; ++j)
-                dma16(Wg + boff[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+                dma16(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
         };
 
         floatx16 acc[TM][TN];
@@ -568,41 +579,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
             wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
         }
-
-        uint16_t *out = (uint16_t *)p.out;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = wm * (BM / WM) + i * 32 + (lane & 31);
-            if (m >= nrows) continue;
-            uint16_t *orow = out + (size_t)(row0 + m) * N;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * (BN / WN) + j * 32 + 8 * q +
-                                  4 * (lane >> 5);
-                    float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                    float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                    if (bg) {
-                        const u32x2 bb = *(const u32x2 *)(bg + n);
-                        v0 += bf16_lo(bb.x);
-                        v1 += bf16_hi(bb.x);
-                        v2 += bf16_lo(bb.y);
-                        v3 += bf16_hi(bb.y);
-                    }
-                    if (UP) {
-                        v0 = gelu_erf(v0);
-                        v1 = gelu_erf(v1);
-                        v2 = gelu_erf(v2);
-                        v3 = gelu_erf(v3);
-                    }
-                    u32x2 o;
-                    o.x = pack_bf16x2(v0, v1);
-                    o.y = pack_bf16x2(v2, v3);
-                    *(u32x2 *)(orow + n) = o;
-                }
-            }
-        }
+        store_tile<BM, BN, WM, WN, TM, TN, UP>(p, acc, routed, g, row0, nrows,
+                                               n0, wm, wn, lane);
     }
 }
 
@@ -621,7 +599,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
 // before the epilogue.
 template <int MT, int TN, int SU>
 __device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][TN],
-                                             const uint16_t *w0, size_t wstep,
+                                             const uint16_t *const (&wt)[TN],
                                              const uint16_t *a0,
                                              const uint16_t *a1, int kq) {
     u32x4 av[2][SU][MT], bv[2][SU][TN];
@@ -630,7 +608,7 @@ __device__ __forceinline__ void stream_chunk(floatx4 (&acc)[2][TN],
         for (int s = 0; s < SU; ++s) {
 #pragma unroll
             for (int n = 0; n < TN; ++n)
-                bv[buf][s][n] = *(const u32x4 *)(w0 + n * wstep + k0 + s * 32);
+                bv[buf][s][n] = *(const u32x4 *)(wt[n] + k0 + s * 32);
             av[buf][s][0] = *(const u32x4 *)(a0 + k0 + s * 32);
             if (MT == 2) av[buf][s][MT - 1] = *(const u32x4 *)(a1 + k0 + s * 32);
         }
@@ -689,8 +667,7 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 
 template <int MT, int TN, int SU>
 __device__ __forceinline__ void stream_chunk_fp8(floatx4 (&acc)[2][TN],
-                                                 const uint8_t *w0,
-                                                 size_t wstep,
+                                                 const uint8_t *const (&wt)[TN],
                                                  const uint16_t *a0,
                                                  const uint16_t *a1, int kq) {
     u32x4 av[2][SU][MT][2], bv[2][SU][TN];
@@ -699,7 +676,7 @@ __device__ __forceinline__ void stream_chunk_fp8(floatx4 (&acc)[2][TN],
         for (int s = 0; s < SU; ++s) {
 #pragma unroll
             for (int n = 0; n < TN; ++n)
-                bv[buf][s][n] = *(const u32x4 *)(w0 + n * wstep + k0 + s * 64);
+                bv[buf][s][n] = *(const u32x4 *)(wt[n] + k0 + s * 64);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 av[buf][s][0][h] = *(const u32x4 *)(a0 + k0 + s * 64 + 8 * h);
@@ -775,17 +752,13 @@ __global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
         if (tt.rows[g] == 0) continue;
         const bool routed = g < p.E;
         const int esz = FP8 ? 1 : 2;         // bytes per weight
-        const char *Wg = routed
-            ? (const char *)p.W + (size_t)g * N * K * esz
-            : (const char *)p.Ws;
-        const uint16_t *bg = routed
-            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
-            : (const uint16_t *)p.bias_s;
-        const float *sg = FP8 ? (routed ? p.scale + (size_t)g * N : p.scale_s)
-                              : nullptr;
         const int n0 = n_tile * NB;
-        const char *w0 = Wg + ((size_t)(n0 + r16) * K + kbeg + kg) * esz;
-        const size_t wstep = (size_t)16 * K;     // elements between tiles
+        // this lane's weight row of every 16-row MFMA tile of the unit
+        const char *wt[TN];
+#pragma unroll
+        for (int n = 0; n < TN; ++n)
+            wt[n] = weight_row(p, routed, g, n0 + 16 * n + r16, esz) +
+                    (size_t)(kbeg + kg) * esz;
 
         for (int mc = 0; mc < tt.mt[g]; ++mc) {
             const int row0 = tt.start[g] + mc * 32;
@@ -813,18 +786,22 @@ __global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[m][n][v] = 0.0f;
             if (FP8) {
-                const uint8_t *q0 = (const uint8_t *)w0;
+                const uint8_t *q[TN];
+#pragma unroll
+                for (int n = 0; n < TN; ++n) q[n] = (const uint8_t *)wt[n];
                 if (nrows > 16)
-                    stream_chunk_fp8<2, TN, NB == 32 ? 2 : 1>(acc, q0, wstep,
-                                                              a0, a1, kq);
+                    stream_chunk_fp8<2, TN, NB == 32 ? 2 : 1>(acc, q, a0, a1,
+                                                              kq);
                 else
-                    stream_chunk_fp8<1, TN, SU>(acc, q0, wstep, a0, a1, kq);
+                    stream_chunk_fp8<1, TN, SU>(acc, q, a0, a1, kq);
             } else {
-                const uint16_t *b0 = (const uint16_t *)w0;
+                const uint16_t *b[TN];
+#pragma unroll
+                for (int n = 0; n < TN; ++n) b[n] = (const uint16_t *)wt[n];
                 if (nrows > 16)
-                    stream_chunk<2, TN, SU>(acc, b0, wstep, a0, a1, kq);
+                    stream_chunk<2, TN, SU>(acc, b, a0, a1, kq);
                 else
-                    stream_chunk<1, TN, SU>(acc, b0, wstep, a0, a1, kq);
+                    stream_chunk<1, TN, SU>(acc, b, a0, a1, kq);
             }
             // lane holds row m = 16*mt + lane%16, features
             // 16*nt + 4*(lane/16) + 0..3
@@ -837,30 +814,77 @@ __global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
                         part[wave][16 * m + r16][16 * n + 4 * (lane >> 4) + v] =
                             acc[m][n][v];
             __syncthreads();
-            for (int e = tid; e < 32 * NB / 2; e += 256) {
-                const int m = e / (NB / 2);
-                const int c = (e - m * (NB / 2)) * 2;
-                if (m < nrows) {
-                    float v0 = part[0][m][c] + part[1][m][c];
-                    v0 += part[2][m][c];
-                    v0 += part[3][m][c];
-                    float v1 = part[0][m][c + 1] + part[1][m][c + 1];
-                    v1 += part[2][m][c + 1];
-                    v1 += part[3][m][c + 1];
-                    if (FP8) {
-                        v0 *= sg[n0 + c];
-                        v1 *= sg[n0 + c + 1];
+            if (UP && p.gated) {
+                // a 64-column unit of the virtual panel: columns 0-31 are
+                // the gate rows and 32-63 the up rows of features
+                // 32*n_tile + 0..31
+                const int F = N >> 1, f0 = n0 >> 1;
+                const uint16_t *b1 = routed
+                    ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+                    : (const uint16_t *)p.bias_s;
+                const uint16_t *b3 = routed
+                    ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+                    : (const uint16_t *)p.bias_s3;
+                const float *s1 = FP8 ? (routed ? p.scale + (size_t)g * F : p.scale_s)
+                                      : nullptr;
+                const float *s3 = FP8 ? (routed ? p.scale3 + (size_t)g * F : p.scale_s3)
+                                      : nullptr;
+                for (int e = tid; e < 32 * 16; e += 256) {
+                    const int m = e >> 4;
+                    const int c = (e & 15) * 2;
+                    if (m < nrows) {
+                        float h[2];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            float gv = part[0][m][c + i] + part[1][m][c + i];
+                            gv += part[2][m][c + i];
+                            gv += part[3][m][c + i];
+                            float uv = part[0][m][32 + c + i] + part[1][m][32 + c + i];
+                            uv += part[2][m][32 + c + i];
+                            uv += part[3][m][32 + c + i];
+                            if (FP8) {
+                                gv *= s1[f0 + c + i];
+                                uv *= s3[f0 + c + i];
+                            }
+                            if (b1) gv += bf16_to_f32(b1[f0 + c + i]);
+                            if (b3) uv += bf16_to_f32(b3[f0 + c + i]);
+                            h[i] = silu_f(gv) * uv;
+                        }
+                        *(uint32_t *)(out + (size_t)(row0 + m) * p.ldo + f0 + c) =
+                            pack_bf16x2(h[0], h[1]);
                     }
-                    if (bg) {
-                        v0 += bf16_to_f32(bg[n0 + c]);
-                        v1 += bf16_to_f32(bg[n0 + c + 1]);
+                }
+            } else {
+                const uint16_t *bg = routed
+                    ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+                    : (const uint16_t *)p.bias_s;
+                const float *sg = FP8 ? (routed ? p.scale + (size_t)g * N : p.scale_s)
+                                      : nullptr;
+                for (int e = tid; e < 32 * NB / 2; e += 256) {
+                    const int m = e / (NB / 2);
+                    const int c = (e - m * (NB / 2)) * 2;
+                    if (m < nrows) {
+                        float v0 = part[0][m][c] + part[1][m][c];
+                        v0 += part[2][m][c];
+                        v0 += part[3][m][c];
+                        float v1 = part[0][m][c + 1] + part[1][m][c + 1];
+                        v1 += part[2][m][c + 1];
+                        v1 += part[3][m][c + 1];
+                        if (FP8) {
+                            v0 *= sg[n0 + c];
+                            v1 *= sg[n0 + c + 1];
+                        }
+                        if (bg) {
+                            v0 += bf16_to_f32(bg[n0 + c]);
+                            v1 += bf16_to_f32(bg[n0 + c + 1]);
+                        }
+                        if (UP) {
+                            v0 = act_up(p.act, v0);
+                            v1 = act_up(p.act, v1);
+                        }
+                        *(uint32_t *)(out + (size_t)(row0 + m) * p.ldo + n0 + c) =
+                            pack_bf16x2(v0, v1);
                     }
-                    if (UP) {
-                        v0 = gelu_erf(v0);
-                        v1 = gelu_erf(v1);
-                    }
-                    *(uint32_t *)(out + (size_t)(row0 + m) * N + n0 + c) =
-                        pack_bf16x2(v0, v1);
                 }
             }
             __syncthreads();
@@ -894,11 +918,7 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
         const int nrows = min(BM, tt.rows[g] - m_tile * BM);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        const float *Wg = routed ? (const float *)p.W + (size_t)g * N * K
-                                 : (const float *)p.Ws;
-        const float *bg = routed
-            ? (p.bias ? (const float *)p.bias + (size_t)g * N : nullptr)
-            : (const float *)p.bias_s;
+        const bool gated = UP && p.gated;
         const float *arow = nullptr;
         if (lr < nrows) {
             const int slot = row0 + lr;
@@ -906,7 +926,11 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
             if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
             arow = A + (size_t)src * K;
         }
-        const float *brow = Wg + (size_t)(n0 + lr) * K;
+        const float *brow = (const float *)weight_row(p, routed, g, n0 + lr, 4);
+        // this thread's 4 tile columns: 4*tx .. 4*tx+3, or (gated) the
+        // gate columns 2*tx, 2*tx+1 and their up columns 32 + 2*tx, +1
+        const int cb0 = gated ? 2 * tx : 4 * tx;
+        const int cb1 = gated ? 32 + 2 * tx : 4 * tx + 2;
         float acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -928,9 +952,10 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
 #pragma unroll
             for (int kk = 0; kk < BKF; ++kk) {
                 const float4 a4 = *(const float4 *)&As[kk][ty * 4];
-                const float4 b4 = *(const float4 *)&Bs[kk][tx * 4];
+                const float2 b01 = *(const float2 *)&Bs[kk][cb0];
+                const float2 b23 = *(const float2 *)&Bs[kk][cb1];
                 const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-                const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float b[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -939,21 +964,48 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
             __syncthreads();
         }
         float *out = (float *)p.out;
+        if (gated) {
+            const int F = N >> 1, f = (n0 >> 1) + 2 * tx;
+            const float *b1 = routed
+                ? (p.bias ? (const float *)p.bias + (size_t)g * F : nullptr)
+                : (const float *)p.bias_s;
+            const float *b3 = routed
+                ? (p.bias3 ? (const float *)p.bias3 + (size_t)g * F : nullptr)
+                : (const float *)p.bias_s3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = ty * 4 + i;
+                if (m >= nrows) continue;
+                float h[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float gv = acc[i][j], uv = acc[i][2 + j];
+                    if (b1) gv += b1[f + j];
+                    if (b3) uv += b3[f + j];
+                    h[j] = silu_f(gv) * uv;
+                }
+                *(float2 *)(out + (size_t)(row0 + m) * p.ldo + f) =
+                    make_float2(h[0], h[1]);
+            }
+            continue;
+        }
+        const float *bg = routed
+            ? (p.bias ? (const float *)p.bias + (size_t)g * N : nullptr)
+            : (const float *)p.bias_s;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = ty * 4 + i;
             if (m >= nrows) continue;
-            float4 o;
             float v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n0 + tx * 4 + j;
                 float z = acc[i][j];
                 if (bg) z += bg[n];
-                v[j] = UP ? gelu_erf(z) : z;
+                v[j] = UP ? act_up(p.act, z) : z;
             }
-            o = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4 *)(out + (size_t)(row0 + m) * N + n0 + tx * 4) = o;
+            *(float4 *)(out + (size_t)(row0 + m) * p.ldo + n0 + tx * 4) =
+                make_float4(v[0], v[1], v[2], v[3]);
         }
     }
 }

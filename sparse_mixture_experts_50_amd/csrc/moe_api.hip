@@ -43,6 +43,14 @@ int check_desc(const moe_desc *d) {
         (d->k != d->E || d->capacity < 0 || d->capacity > d->T))
         return MOE_ERR_INVALID_ARG;
     if (d->expert_fp8 != 0 && d->expert_fp8 != 1) return MOE_ERR_INVALID_ARG;
+    if (d->activation < MOE_ACT_GELU || d->activation > MOE_ACT_SWIGLU)
+        return MOE_ERR_INVALID_ARG;
+    // the gated bf16 up GEMM runs on tiles whose waves cover whole 64-column
+    // chunks of the 2*d_ff virtual panel (256-column tiles, 64-column
+    // streaming units)
+    if (d->activation == MOE_ACT_SWIGLU && d->dtype == MOE_BF16 &&
+        d->d_ff % 128 != 0)
+        return MOE_ERR_UNSUPPORTED;
     if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     // FP8 weights run on the weight-streaming kernel: its four K quarters
     // hold whole 256-deep load batches
@@ -56,7 +64,7 @@ int check_desc(const moe_desc *d) {
     if ((double)d->T * d->k >= 2147483647.0) return MOE_ERR_UNSUPPORTED;
     const double rows = (double)routed_rows(d) + (double)d->n_shared * d->T;
     if (rows * d->d_ff >= 2147483647.0 || rows * d->d >= 2147483647.0 ||
-        (double)d->d * d->d_ff >= 2147483647.0)
+        2.0 * d->d * d->d_ff >= 2147483647.0)
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -115,11 +123,22 @@ int device_cus() {
 
 // Tuning override: MOE_GEMM_VARIANT_UP / MOE_GEMM_VARIANT_DOWN name a
 // GemmVariant; it is used only if valid for this dtype and width.
+bool gated_up(const moe_desc *d, bool up) {
+    return up && d->activation == MOE_ACT_SWIGLU;
+}
+
+// Variants whose waves hold whole 64-column chunks of the gated panel.
+bool gate_capable(int v) {
+    return v != GEMM_BF16_64x64 && v != GEMM_BF16_STREAM_32x64 &&
+           v != GEMM_FP8_STREAM_32x64;
+}
+
 int variant_override(bool up, const moe_desc *d, int N) {
     const char *v = getenv(up ? "MOE_GEMM_VARIANT_UP" : "MOE_GEMM_VARIANT_DOWN");
     if (!v || !*v) return -1;
     const int id = atoi(v);
     if (d->dtype == MOE_F32) return -1;
+    if (gated_up(d, up) && !gate_capable(id)) return -1;
     const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
                         id == GEMM_FP8_STREAM_64x64;
     if (d->expert_fp8) return fp8_id ? id : -1;
@@ -182,6 +201,12 @@ int check_weights_ffn(const moe_desc *d, const moe_weights *w) {
     if (d->expert_fp8 && (!w->w1_scale || !w->w2_scale ||
                           (d->n_shared && (!w->ws1_scale || !w->ws2_scale))))
         return MOE_ERR_INVALID_ARG;
+    if (d->activation == MOE_ACT_SWIGLU) {
+        if (!w->w3 || (d->n_shared && !w->ws3)) return MOE_ERR_INVALID_ARG;
+        if (d->expert_fp8 &&
+            (!w->w3_scale || (d->n_shared && !w->ws3_scale)))
+            return MOE_ERR_INVALID_ARG;
+    }
     return MOE_OK;
 }
 
@@ -215,7 +240,7 @@ int check_routing_combine(const moe_routing *r) {
 GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
                        const moe_routing *r, bool up, const void *x, void *ws) {
     const WsLayout L = layout(d);
-    GemmParams p;
+    GemmParams p = {};
     p.slot_token = r->slot_token;
     p.offsets = r->offsets;
     p.E = d->E;
@@ -231,7 +256,19 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
         p.out = at(ws, L.h);
         p.scale = w->w1_scale;
         p.scale_s = w->ws1_scale;
-        p.N = d->d_ff;
+        p.act = d->activation;
+        p.gated = d->activation == MOE_ACT_SWIGLU;
+        if (p.gated) {
+            p.W3 = w->w3;
+            p.bias3 = w->b3;
+            p.Ws3 = w->ws3;
+            p.bias_s3 = w->bs3;
+            p.scale3 = w->w3_scale;
+            p.scale_s3 = w->ws3_scale;
+        }
+        // a gated up GEMM has 2*d_ff (virtual) columns and d_ff outputs
+        p.N = p.gated ? 2 * d->d_ff : d->d_ff;
+        p.ldo = d->d_ff;
         p.K = d->d;
     } else {
         p.A = at(ws, L.h);
@@ -243,6 +280,7 @@ GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
         p.scale = w->w2_scale;
         p.scale_s = w->ws2_scale;
         p.N = d->d;
+        p.ldo = d->d;
         p.K = d->d_ff;
     }
     return p;
@@ -253,6 +291,9 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
     const GemmParams p = gemm_params(d, w, r, up, x, ws);
     int variant = variant_override(up, d, p.N);
     if (variant < 0) variant = pick_variant(d, p.N);
+    // check_desc keeps a gated N = 2*d_ff a multiple of 256, so pick_variant
+    // never lands on a variant that cannot pair gate and up columns
+    if (gated_up(d, up) && !gate_capable(variant)) return MOE_ERR_UNSUPPORTED;
     const int grid = gemm_grid(d, variant, p.N);
     return to_status(launch_gemm(p, variant, up, grid, s));
 }

@@ -9,6 +9,8 @@ layouts are those of include/moe.h:
 FP8 expert matrices: uint8 (or float8_e4m3fn) tensors of the same shapes
 holding OCP E4M3 codes, with float32 per-output-channel scales
 w1_scale [E][d_ff], w2_scale [E][d], ws1_scale [d_ff], ws2_scale [d].
+SwiGLU experts add the up projection w3 [E][d_ff][d], b3 [E][d_ff] (ws3,
+bs3 for the shared expert; w3_scale, ws3_scale for FP8); W1 is the gate.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ from ._lib import MoeDesc, MoeRouting, MoeWeights, check
 _DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
 _ROUTING = {"topk": _lib.MOE_ROUTE_TOPK,
             "expert_choice": _lib.MOE_ROUTE_EXPERT_CHOICE}
+_ACT = {"gelu": _lib.MOE_ACT_GELU, "silu": _lib.MOE_ACT_SILU,
+        "swiglu": _lib.MOE_ACT_SWIGLU}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -54,16 +58,19 @@ def _opt(t, name, shape, dtype, device):
 def make_desc(T: int, d: int, E: int, k: int, d_ff: int, dtype: torch.dtype,
               n_shared: int = 0, capacity: int = -1,
               aux_alpha: float = 0.01, routing: str = "topk",
-              expert_fp8: bool = False) -> MoeDesc:
+              expert_fp8: bool = False, activation: str = "gelu") -> MoeDesc:
     """``routing`` is "topk" or "expert_choice" (then k must be E and
     capacity the tokens each expert picks); ``expert_fp8`` marks E4M3
-    expert matrices."""
+    expert matrices; ``activation`` is "gelu", "silu" or "swiglu"."""
     if dtype not in _DT:
         raise ValueError(f"unsupported dtype {dtype}")
     if routing not in _ROUTING:
         raise ValueError(f"unknown routing {routing!r}")
+    if activation not in _ACT:
+        raise ValueError(f"unknown activation {activation!r}")
     return MoeDesc(T, d, E, k, d_ff, n_shared, _DT[dtype], capacity,
-                   aux_alpha, _ROUTING[routing], int(bool(expert_fp8)))
+                   aux_alpha, _ROUTING[routing], int(bool(expert_fp8)),
+                   _ACT[activation])
 
 
 def moe_capacity(T: int, E: int, capacity_factor: Optional[float]) -> int:
@@ -98,8 +105,13 @@ class Weights:
     def __init__(self, w_router, w1, w2, b_router=None, expert_bias=None,
                  b1=None, b2=None, ws1=None, bs1=None, ws2=None, bs2=None,
                  w1_scale=None, w2_scale=None, ws1_scale=None,
-                 ws2_scale=None):
+                 ws2_scale=None, w3=None, b3=None, ws3=None, bs3=None,
+                 w3_scale=None, ws3_scale=None):
         w1, w2, ws1, ws2 = _codes(w1), _codes(w2), _codes(ws1), _codes(ws2)
+        w3, ws3 = _codes(w3), _codes(ws3)
+        self.w3, self.b3, self.ws3, self.bs3 = w3, b3, ws3, bs3
+        self.w3_scale, self.ws3_scale = w3_scale, ws3_scale
+        self.gated = w3 is not None
         self.w_router, self.w1, self.w2 = w_router, w1, w2
         self.b_router, self.expert_bias = b_router, expert_bias
         self.b1, self.b2 = b1, b2
@@ -125,6 +137,11 @@ class Weights:
         if self.expert_fp8:
             _need(w1_scale, "w1_scale", (E, d_ff), f32, dev)
             _need(w2_scale, "w2_scale", (E, d), f32, dev)
+        if self.gated:
+            _need(w3, "w3", (E, d_ff, d), wdt, dev)
+            _opt(b3, "b3", (E, d_ff), dt, dev)
+            if self.expert_fp8:
+                _need(w3_scale, "w3_scale", (E, d_ff), f32, dev)
         if self.n_shared:
             _need(ws1, "ws1", (d_ff, d), wdt, dev)
             _need(ws2, "ws2", (d, d_ff), wdt, dev)
@@ -133,6 +150,11 @@ class Weights:
             if self.expert_fp8:
                 _need(ws1_scale, "ws1_scale", (d_ff,), f32, dev)
                 _need(ws2_scale, "ws2_scale", (d,), f32, dev)
+            if self.gated:
+                _need(ws3, "ws3", (d_ff, d), wdt, dev)
+                _opt(bs3, "bs3", (d_ff,), dt, dev)
+                if self.expert_fp8:
+                    _need(ws3_scale, "ws3_scale", (d_ff,), f32, dev)
 
     @staticmethod
     def from_dict(inp: dict, device=None) -> "Weights":
@@ -146,13 +168,17 @@ class Weights:
                        ws1=g("ws1"), bs1=g("bs1"), ws2=g("ws2"),
                        bs2=g("bs2"), w1_scale=g("w1_scale"),
                        w2_scale=g("w2_scale"), ws1_scale=g("ws1_scale"),
-                       ws2_scale=g("ws2_scale"))
+                       ws2_scale=g("ws2_scale"), w3=g("w3"), b3=g("b3"),
+                       ws3=g("ws3"), bs3=g("bs3"), w3_scale=g("w3_scale"),
+                       ws3_scale=g("ws3_scale"))
 
     def struct(self) -> MoeWeights:
         return MoeWeights(*[_ptr(t) for t in (
             self.w_router, self.b_router, self.expert_bias, self.w1, self.b1,
             self.w2, self.b2, self.ws1, self.bs1, self.ws2, self.bs2,
-            self.w1_scale, self.w2_scale, self.ws1_scale, self.ws2_scale)])
+            self.w1_scale, self.w2_scale, self.ws1_scale, self.ws2_scale,
+            self.w3, self.b3, self.ws3, self.bs3, self.w3_scale,
+            self.ws3_scale)])
 
 
 class Routing:
@@ -270,16 +296,23 @@ class MoeLayer:
     ``routing="topk"``: each token picks ``k`` experts, with an optional
     capacity floor(T/E * capacity_factor).  ``routing="expert_choice"``:
     each expert picks floor(T/E * capacity_factor) tokens (``k`` is then E
-    and a capacity factor is required).
+    and a capacity factor is required).  ``activation``: "gelu", "silu",
+    or "swiglu" (the default when the weights carry w3).
 
     ``forward(x)`` returns ``(y, routing)``; the routing buffers are reused
     by the next call with the same T (copy them to keep them)."""
 
     def __init__(self, weights: Weights, k: int,
                  capacity_factor: Optional[float] = None,
-                 aux_alpha: float = 0.01, routing: str = "topk"):
+                 aux_alpha: float = 0.01, routing: str = "topk",
+                 activation: Optional[str] = None):
         if routing not in _ROUTING:
             raise ValueError(f"unknown routing {routing!r}")
+        if activation is None:
+            activation = "swiglu" if weights.gated else "gelu"
+        if (activation == "swiglu") != weights.gated:
+            raise ValueError("swiglu needs w3, and w3 needs swiglu")
+        self.activation = activation
         if routing == "expert_choice":
             if capacity_factor is None:
                 raise ValueError("expert choice needs a capacity factor")
@@ -299,7 +332,7 @@ class MoeLayer:
         return make_desc(T, w.d, w.E, self.k, w.d_ff, w.dtype,
                          n_shared=w.n_shared, capacity=cap,
                          aux_alpha=self.aux_alpha, routing=self.routing,
-                         expert_fp8=w.expert_fp8)
+                         expert_fp8=w.expert_fp8, activation=self.activation)
 
     def buffers(self, T: int):
         if T not in self._bufs:

@@ -41,7 +41,7 @@ def gpu_forward(w: workloads.Workload, inp: dict, steps: bool = False):
     points one by one instead of moe_forward."""
     weights = moe.Weights.from_dict(inp)
     layer = moe.MoeLayer(weights, w.k, w.capacity_factor, w.alpha,
-                         routing=w.routing)
+                         routing=w.routing, activation=w.activation)
     x = inp["x"]
     if steps:
         desc, r, ws, y = layer.buffers(x.shape[0])
@@ -74,7 +74,8 @@ def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
                 tokens=None) -> dict:
     """Oracle on the same inputs; assert every rule; return a report."""
     ref = oracle.forward(inp, w.k, w.capacity_factor, w.alpha,
-                         tokens=np.arange(0, dtype=np.int32))
+                         tokens=np.arange(0, dtype=np.int32),
+                         activation=w.activation)
     T = inp["x"].shape[0]
     margin = ref["margin"]
     undecided = margin <= MARGIN
@@ -102,7 +103,8 @@ def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
     cond = oracle.forward(inp, w.k, w.capacity_factor, w.alpha,
-                          tokens=tokens, selection=sel, probs=probs)
+                          tokens=tokens, selection=sel, probs=probs,
+                          activation=w.activation)
     for key in ("counts", "kept", "offsets", "slot_token", "slot_of"):
         assert np.array_equal(gpu[key].reshape(-1),
                               cond[key].reshape(-1)), key
@@ -164,7 +166,8 @@ def check_expert_choice(w: workloads.Workload, inp: dict, gpu: dict,
     C = moe.moe_capacity(T, E, w.capacity_factor)
     C = min(C, T)
     ref = oracle.forward_expert_choice(inp, C, w.alpha,
-                                       tokens=np.arange(0, dtype=np.int32))
+                                       tokens=np.arange(0, dtype=np.int32),
+                                       activation=w.activation)
     logits, probs = ref["logits"], ref["probs"]
     st = gpu["slot_token"].reshape(-1)[:E * C]
     undecided = 0
@@ -189,7 +192,7 @@ def check_expert_choice(w: workloads.Workload, inp: dict, gpu: dict,
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
     cond = oracle.forward_expert_choice(inp, C, w.alpha, tokens=tokens,
-                                        selection=st)
+                                        selection=st, activation=w.activation)
     so = gpu["slot_of"].reshape(T, -1)
     assert so.shape[1] == E
     assert np.array_equal(so, cond["slot_of"]), "slot_of"

@@ -84,6 +84,9 @@ def desc(**kw):
     (dict(expert_fp8=1, d=1024, d_ff=1024, dtype=0), _lib.MOE_ERR_UNSUPPORTED),
     (dict(expert_fp8=1, d=512, d_ff=1024), _lib.MOE_ERR_UNSUPPORTED),
     (dict(expert_fp8=1, d=1024, d_ff=1536), _lib.MOE_ERR_UNSUPPORTED),
+    # activations: gelu, silu, swiglu; gated bf16 needs d_ff % 128 == 0
+    (dict(activation=3), _lib.MOE_ERR_INVALID_ARG),
+    (dict(activation=2, d_ff=192), _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_descriptor_rejected_before_any_launch(kw, status):
     L = _lib.lib()
@@ -195,6 +198,21 @@ def test_fp8_needs_scales():
                                 None, None, None, None, FAKE, None)
     assert L.moe_grouped_ffn(ctypes.byref(d), FAKE, ctypes.byref(one_scale),
                              ctypes.byref(r), FAKE, ws, None) == -1
+
+
+def test_swiglu_needs_w3():
+    L = _lib.lib()
+    d = desc(activation=2)
+    ws = L.moe_workspace_size(ctypes.byref(d))
+    assert ws > 0
+    r = _lib.MoeRouting(*([FAKE] * 10))
+    w = _lib.MoeWeights(FAKE, None, None, FAKE, None, FAKE, None,
+                        None, None, None, None)
+    assert L.moe_grouped_ffn(ctypes.byref(d), FAKE, ctypes.byref(w),
+                             ctypes.byref(r), FAKE, ws, None) == -1
+    # fp32 SwiGLU runs any d_ff the fp32 kernel runs
+    assert L.moe_workspace_size(ctypes.byref(
+        desc(activation=2, dtype=0, d_ff=192))) > 0
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -91,6 +91,14 @@ WORKLOADS: Dict[str, Workload] = {
     "mixtral_decode_fp8": Workload(
         name="mixtral_decode_fp8", T=32, d=4096, E=8, k=2, d_ff=14336,
         dtype="bf16", router_var=0.02, calls=200, expert_fp8=True),
+    # Mixtral-8x7B's gated expert (SwiGLU: W2 (SiLU(W1 x) * W3 x)), prefill
+    # and decode shapes.
+    "mixtral_prefill_swiglu": Workload(
+        name="mixtral_prefill_swiglu", T=4096, d=4096, E=8, k=2, d_ff=14336,
+        dtype="bf16", router_var=0.02, activation="swiglu"),
+    "mixtral_decode_swiglu": Workload(
+        name="mixtral_decode_swiglu", T=32, d=4096, E=8, k=2, d_ff=14336,
+        dtype="bf16", router_var=0.02, calls=200, activation="swiglu"),
     # Expert choice: each of 64 experts picks C = floor(T/E * 2) = 256
     # tokens, the compute of top-2 routing on the Switch-sized layer.
     "expert_choice_c2": Workload(
