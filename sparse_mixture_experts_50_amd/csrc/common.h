@@ -38,9 +38,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// Exact-erf GELU: z/2 * (1 + erf(z / sqrt 2)), with the device erff.
+// GELU of the erf form, z * Phi(z) with Phi(z) = (1 + erf(z / sqrt 2)) / 2.
+// erf by the rational approximation 7.1.26 of Abramowitz and Stegun,
+// Handbook of Mathematical Functions (1964):
+//   erf(x) = 1 - q,  q = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2),
+//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7.
+// For -3 <= z < 0, Phi(z) = q / 2 is formed from the tail term directly
+// (no cancellation); for z >= 0, Phi(z) = 1 - q / 2.  The bound is
+// absolute, so q's relative error is at most 6e-5 down to z = -3 but grows
+// towards 38 % deep in the tail; below -3 (rare for pre-activations) the
+// device erfcf, accurate relative to its value, takes over.  With the
+// hardware reciprocal and exponential this costs a fraction of an erff.
 __device__ __forceinline__ float gelu_erf(float z) {
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+    const float x = fabsf(z) * 0.70710678118654752440f;
+    if (z < -3.0f) return 0.5f * z * erfcf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    const float q = poly * t * __expf(-x * x);
+    return z * (z < 0.0f ? 0.5f * q : fmaf(-0.5f, q, 1.0f));
 }
 
 // ------------------------------------------------------------- wave ops
@@ -152,8 +170,10 @@ struct GemmParams {
 
 enum { ACT_GELU = 0, ACT_SILU = 1, ACT_SWIGLU = 2 };
 
+// SiLU(z) = z / (1 + e^-z) with the hardware exponential and reciprocal
+// (relative error a few 1e-7).
 __device__ __forceinline__ float silu_f(float z) {
-    return z / (1.0f + expf(-z));
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 // Activation of an ungated up GEMM output.

@@ -1093,6 +1093,7 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_DMA64_128x256:
         return up ? launch_dma64<128, 256, 2, 2, true>(p, grid, s)
                   : launch_dma64<128, 256, 2, 2, false>(p, grid, s);
+
     case GEMM_BF16_STREAM_32x64:
         if (up)
             hipLaunchKernelGGL((gemm_stream<true, false, 32>), dim3(grid),

@@ -92,3 +92,43 @@ def test_swiglu_full_size_sampled(name):
     say(f"[swiglu full] {name}: {rep}")
     del inp, gpu
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "swiglu"])
+def test_activation_accuracy_through_identity_experts(act):
+    # E = 1, W1 = W3 = W2 = I: y = bf16(act(x)) (swiglu: SiLU(x) * x), so
+    # every element checks the device activation against its definition
+    # (the hidden rounding to bf16 is the only loss)
+    d = 1024
+    w = workloads.Workload(name="identity", T=512, d=d, E=1, k=1, d_ff=d,
+                           dtype="bf16", activation=act)
+    dev = device()
+    inp = inputs_on(w, dev)
+    grid = torch.linspace(-9.0, 9.0, w.T * d, device=dev)
+    inp["x"] = grid.view(w.T, d).to(torch.bfloat16)
+    eye = torch.eye(d, device=dev, dtype=torch.bfloat16)[None]
+    inp["w1"] = eye.clone()
+    inp["w2"] = eye.clone()
+    if act == "swiglu":
+        inp["w3"] = eye.clone()
+    gpu = gpu_forward(w, inp)
+    x = inp["x"].double().cpu()
+    if act == "gelu":
+        # Phi(x) = erfc(-x / sqrt 2) / 2: 1 + erf(x / sqrt 2) cancels to 0
+        # in float64 for x below about -6
+        ref = x * 0.5 * torch.special.erfc(-x / 2.0 ** 0.5)
+    elif act == "silu":
+        ref = x * torch.sigmoid(x)
+    else:
+        ref = x * torch.sigmoid(x) * x
+    ref = ref.numpy()
+    y = gpu["y"]
+    # one rounding of the hidden unit to bf16 (relative 2^-9), then W2 = I
+    # passes it on exactly; allow one bf16 ulp plus the approximation
+    err = np.abs(y - ref)
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-6 * (1 + np.abs(x.numpy()))
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-30)))
+    exact = (torch.from_numpy(ref).to(torch.bfloat16).double().numpy() == y)
+    say(f"[act accuracy] {act}: max err {err.max():.3g}, "
+        f"bf16-exact {exact.mean():.4f}")
+    assert exact.mean() > 0.99
