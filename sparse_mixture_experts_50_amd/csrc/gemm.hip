@@ -491,7 +491,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave / WN, wn = wave % WN;
     const int N = p.N, K = p.K, KT = K / BK;
     const int NTN = N / BN;
@@ -538,12 +538,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
             bp[j] = (const uint16_t *)weight_row(p, routed, g, n0 + rr, 2) +
                     ch * 8;
         }
+        // 8-row groups wholly past the group's end are not loaded (their
+        // stale LDS rows only feed outputs that are never stored)
         auto issue = [&](int ks) __attribute__((always_inline)) {
             u32x4 *st = smem + (ks & 1) * STAGE;
             const int ko = ks * BK;
 #pragma unroll
             for (int j = 0; j < IA; ++j)
-                dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
+                if ((wave + j * NW) * 8 < nrows)
+                    dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
 #pragma unroll
             for (int j = 0; j < IB; ++j)
                 dma16(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
@@ -1062,6 +1065,7 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_FP8_STREAM_64x64: return {32, 64, 256, 0};
     case GEMM_BF16_DMA64_256x256: return {256, 256, 512, 2 * 512 * 128};
     case GEMM_BF16_DMA64_128x256: return {128, 256, 256, 2 * 384 * 128};
+    case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
     default: return {64, 64, 256, 0};
     }
 }
@@ -1093,6 +1097,9 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_DMA64_128x256:
         return up ? launch_dma64<128, 256, 2, 2, true>(p, grid, s)
                   : launch_dma64<128, 256, 2, 2, false>(p, grid, s);
+    case GEMM_BF16_DMA64_320x256:
+        return up ? launch_dma64<320, 256, 2, 4, true>(p, grid, s)
+                  : launch_dma64<320, 256, 2, 4, false>(p, grid, s);
 
     case GEMM_BF16_STREAM_32x64:
         if (up)

@@ -62,6 +62,7 @@ enum GemmVariant {
     GEMM_FP8_STREAM_32x64 = 10,   // FP8 (E4M3) weights, bf16 activations
     GEMM_BF16_STREAM_64x64 = 11,  // streaming with 64-column units
     GEMM_FP8_STREAM_64x64 = 12,
+    GEMM_BF16_DMA64_320x256 = 13,  // 320-row tiles: one per ~257-320-row group
 };
 
 // Variants that stream weights over persistent (group, column-slab) units.

@@ -142,7 +142,7 @@ int variant_override(bool up, const moe_desc *d, int N) {
     const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
                         id == GEMM_FP8_STREAM_64x64;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_FP8_STREAM_64x64 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_DMA64_320x256 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
@@ -153,6 +153,24 @@ int variant_override(bool up, const moe_desc *d, int N) {
     if (id == GEMM_BF16_STREAM_64x64 && (d->d % 256 != 0 || d->d_ff % 256 != 0))
         return -1;
     return id;
+}
+
+// Expected cost of a grouped GEMM with BM-row tiles: whole rounds of
+// tiles over the persistent grid, each round costing a tile's time.  A
+// tile streams its BN-column weight panel whatever its height, which is
+// worth about 128 rows of the rest.  Top-k group sizes get 10 % headroom
+// for routing skew (at most the capacity); expert-choice groups hold
+// exactly C rows.
+double tile_cost(const moe_desc *d, int N, int bm, int slots) {
+    double avg = (double)routed_rows(d) / d->E;
+    if (!expert_choice(d)) {
+        avg *= 1.1;
+        if (d->capacity >= 0 && avg > d->capacity) avg = d->capacity;
+    }
+    const double mt = ceil(avg / bm) * d->E +
+                      (double)d->n_shared * ceil((double)d->T / bm);
+    const double tiles = mt * (N / 256);
+    return ceil(tiles / slots) * (bm + 128.0);
 }
 
 int pick_variant(const moe_desc *d, int N) {
@@ -167,7 +185,12 @@ int pick_variant(const moe_desc *d, int N) {
         return GEMM_BF16_STREAM_64x64;
     if (avg <= 48.0) return GEMM_BF16_32x256;
     if (avg <= 192.0) return GEMM_BF16_DMA64_128x256;
-    return GEMM_BF16_DMA64_256x256;
+    // 256- or 320-row tiles: 320 covers a ~257..320-row group in one tile
+    // and can turn a partial last round into a full one
+    const int slots = device_cus();
+    return tile_cost(d, N, 320, slots) < tile_cost(d, N, 256, slots)
+               ? GEMM_BF16_DMA64_320x256
+               : GEMM_BF16_DMA64_256x256;
 }
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
