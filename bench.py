@@ -95,6 +95,28 @@ def algorithmic(wl, counts, kept):
                 up_flops=up_flops, up_bytes=up_bytes)
 
 
+def dense_gemm_tflops(M, N, K, dev) -> float:
+    """torch.matmul (hipBLASLt) bf16 rate on one dense M x N x K product."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(N, K, device=dev, dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        torch.matmul(a, b.t())
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b.t())
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b
+    return 2.0 * M * N * K / (ms * 1e9)
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle, as it stands, on the first n tokens of the same inputs
     (n sized to the time budget), through the whole layer."""
@@ -178,9 +200,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     up_ev = []
+    step_ev = []
 
     def step(i, timed):
         x = xs[i % n_x]
+        if timed:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
         moe.moe_router_topk(desc, x, weights, r, ws)
         moe.moe_permute(desc, r, ws)
         if timed:
@@ -193,6 +220,9 @@ def main():
             up_ev.append((e0, e1))
         moe.moe_ffn_down(desc, weights, r, ws)
         moe.moe_combine(desc, r, y, ws)
+        if timed:
+            s1.record(stream)
+            step_ev.append((s0, s1))
 
     log(f"[bench] warmup {warmup}")
     for i in range(warmup):
@@ -213,6 +243,7 @@ def main():
     up_ms = [a.elapsed_time(b) for a, b in up_ev]
     up_avg_ms = float(np.mean(up_ms))
     ms_per_step = total_ms / steps
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
 
     # algorithmic work of the last call (counts of each call are similar;
     # decode calls differ, so average their touched/row counts)
@@ -230,6 +261,12 @@ def main():
         roof = dict(bound="mfma", achieved=alg["up_flops"] /
                     (up_avg_ms * 1e9), peak=peak, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "mfma" and wl.dtype == "bf16":
+        # the vendor library's dense bf16 GEMM of the same FLOPs as the up
+        # GEMM (rows x d_ff x d), measured here beside the nominal peak
+        roof["measured_dense_gemm_tflops"] = dense_gemm_tflops(
+            alg["rows"], wl.d_ff * (2 if wl.activation == "swiglu" else 1),
+            wl.d, dev)
     roof["traffic"] = recorded_traffic(wl.name)
     roof["kernel"] = "grouped GEMM up (moe_ffn_up)"
     roof["kernel_ms"] = up_avg_ms
@@ -259,6 +296,7 @@ def main():
                    "expert_weights": "e4m3" if wl.expert_fp8 else wl.dtype,
                    "activation": wl.activation,
                    "parallelism": "single-gpu"},
+        "ms_per_step_median": float(np.median(step_ms)),
         "layer_tflops": alg["flops"] / (ms_per_step * 1e9),
         "layer_hbm_gbs": alg["bytes"] / (ms_per_step * 1e6),
         "wall_s": wall,
