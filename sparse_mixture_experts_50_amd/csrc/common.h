@@ -38,26 +38,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// GELU of the erf form, z * Phi(z) with Phi(z) = (1 + erf(z / sqrt 2)) / 2.
-// erf by the rational approximation 7.1.26 of Abramowitz and Stegun,
-// Handbook of Mathematical Functions (1964):
-//   erf(x) = 1 - q,  q = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2),
-//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7.
-// For -3 <= z < 0, Phi(z) = q / 2 is formed from the tail term directly
-// (no cancellation); for z >= 0, Phi(z) = 1 - q / 2.  The bound is
-// absolute, so q's relative error is at most 6e-5 down to z = -3 but grows
-// towards 38 % deep in the tail; below -3 (rare for pre-activations) the
-// device erfcf, accurate relative to its value, takes over.  With the
-// hardware reciprocal and exponential this costs a fraction of an erff.
+// GELU of the erf form, z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.
+// erfc by the Chebyshev-fitted form of Numerical Recipes (Press et al.,
+// 2nd ed., sec. 6.2, "erfcc"): for x >= 0,
+//   erfc(x) = t exp(-x^2 + P(t)),  t = 1 / (1 + x / 2),
+// P a degree-9 polynomial, with fractional error below 1.2e-7 for every x.
+// The error being relative, the deep negative tail (where Phi is tiny) is
+// as accurate as the rest; with x = |z| / sqrt 2 and q = erfc(x),
+// Phi(z) = q / 2 for z < 0 and 1 - q / 2 otherwise.  No branch: a tile
+// epilogue evaluates hundreds of these per lane in straight-line code, so
+// independent evaluations interleave and hide the transcendental latency.
 __device__ __forceinline__ float gelu_erf(float z) {
     const float x = fabsf(z) * 0.70710678118654752440f;
-    if (z < -3.0f) return 0.5f * z * erfcf(x);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-    float poly = fmaf(1.061405429f, t, -1.453152027f);
-    poly = fmaf(poly, t, 1.421413741f);
-    poly = fmaf(poly, t, -0.284496736f);
-    poly = fmaf(poly, t, 0.254829592f);
-    const float q = poly * t * __expf(-x * x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
+    float r = fmaf(0.17087277f, t, -0.82215223f);
+    r = fmaf(r, t, 1.48851587f);
+    r = fmaf(r, t, -1.13520398f);
+    r = fmaf(r, t, 0.27886807f);
+    r = fmaf(r, t, -0.18628806f);
+    r = fmaf(r, t, 0.09678418f);
+    r = fmaf(r, t, 0.37409196f);
+    r = fmaf(r, t, 1.00002368f);
+    r = fmaf(r, t, -1.26551223f);
+    const float q = t * __expf(fmaf(-x, x, r));
     return z * (z < 0.0f ? 0.5f * q : fmaf(-0.5f, q, 1.0f));
 }
 

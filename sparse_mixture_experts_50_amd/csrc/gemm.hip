@@ -588,6 +588,295 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
 }
 
 // ---------------------------------------------------------------------
+// Four-wave 256 x 256 tile kernel for large groups (prefill).  One wave per
+// SIMD owns a 128 x 128 quarter as 8 x 8 v_mfma_f32_16x16x32_bf16 blocks.
+// The MFMAs are written as asm with the accumulator as an AGPR operand:
+// with the builtin, hipcc splits the 256 accumulators between AGPRs and
+// VGPRs and copies them back and forth every step.  As volatile asm they
+// also keep the order written here, which is the issue schedule: K is
+// walked in 64-deep stages through two LDS slots filled by direct-to-LDS
+// loads, and while one 32-deep sub-step's 64 MFMAs issue, the 16 fragment
+// reads of the next sub-step go between its first 48 MFMAs and the 16
+// loads of the stage after next between every fourth (in the second
+// sub-step of a stage).  A burst of loads would stall the only wave of the
+// SIMD at the memory pipe; spread out, their issue hides under the MFMAs.
+// The slots are two arrays named statically (two stages per loop trip), so
+// the compiler sees that the loads into one and the reads of the other do
+// not alias and adds no waits between them.
+namespace w4 {
+constexpr int BM = 256, BN = 256, SK = 64;   // stage depth SK
+constexpr int CPR = 8;                   // 16-byte chunks per row and stage
+constexpr int STAGE = (BM + BN) * CPR;   // 16-byte units per stage (64 KB)
+constexpr int LPW = BM / 8 / 4;          // loads per wave, operand and stage
+
+__device__ __forceinline__ void dma16b(const char *src, u32x4 *lds_row8) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src,
+        (__attribute__((address_space(3))) void *)lds_row8, 16, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_agpr(floatx4 &acc, const bf16x8 &a,
+                                          const bf16x8 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+}
+}  // namespace w4
+
+template <bool UP>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
+    using namespace w4;
+    __shared__ u32x4 slot0[STAGE], slot1[STAGE];
+    __shared__ TileTable tt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int N = p.N, K = p.K, KT = K / SK;
+    const int NTN = N / BN;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
+                     NTN);
+    const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const char *A = (const char *)p.A;
+    // Load j of a wave fills rows 8 (wave + 4 j) + lane/8 of an operand,
+    // lane%8 being the 16-byte slot; the lane fetches k-chunk
+    // (lane%8) ^ ((row/2) % 8), which depends on the lane only.  With that
+    // swizzle the fragment reads (16 rows at one chunk) are conflict-free.
+    const int lr = lane >> 3;
+    const int ch = (lane & 7) ^ ((4 * wave + (lr >> 1)) & 7);
+    const uint32_t b_lane = (uint32_t)(lr * K + ch * 8) * 2u;
+    const int l16 = lane & 15;
+    const int sw = (l16 >> 1) & 7;
+
+    for (int r = 0;; ++r) {
+        const int L = r * nb + xcd * per + loc;
+        if (L >= total) break;
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tt, G, L));
+        const int local = L - __builtin_amdgcn_readfirstlane(tt.base[g]);
+        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
+        const int n_tile = local / mt, m_tile = local - n_tile * mt;
+        const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) + m_tile * BM;
+        const int nrows = min(BM, __builtin_amdgcn_readfirstlane(tt.rows[g]) -
+                                      m_tile * BM);
+        const int n0 = n_tile * BN;
+        const bool routed = g < p.E;
+
+        // A rows past the group's end re-read the tile's first row: their
+        // products land in rows that are never stored
+        uint32_t a_off[LPW];
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            int rr = (wave + 4 * j) * 8 + lr;
+            if (rr >= nrows) rr = 0;
+            const int slot = row0 + rr;
+            int src = slot;
+            if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+            a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
+        }
+        const char *bbase[LPW];
+#pragma unroll
+        for (int j = 0; j < LPW; ++j)
+            bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
+
+        // load q (q < 8: A rows, else B rows) of stage ks into a slot
+        auto dma_one = [&](int ks, u32x4 *st, int q) __attribute__((always_inline)) {
+            const int j = q % LPW;
+            const size_t ko = (size_t)ks * SK * 2;
+            if (q < LPW)
+                dma16b(A + ko + a_off[j], st + (wave + 4 * j) * 64);
+            else
+                dma16b(bbase[j] + ko + b_lane, st + BM * CPR + (wave + 4 * j) * 64);
+        };
+        // fragment q (q < 8: A block q, else B block q - 8), sub-step kk
+        auto frag_one = [&](bf16x8 (&fa)[8], bf16x8 (&fb)[8], const u32x4 *st,
+                            int kk, int q) __attribute__((always_inline)) {
+            const int c = (kk * 4 + (lane >> 4)) ^ sw;
+            if (q < 8)
+                fa[q] = as_bf16x8(st[(wm * 128 + q * 16 + l16) * CPR + c]);
+            else
+                fb[q - 8] = as_bf16x8(
+                    st[BM * CPR + (wn * 128 + (q - 8) * 16 + l16) * CPR + c]);
+        };
+
+        floatx4 acc[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 fa0[8], fb0[8], fa1[8], fb1[8];
+
+        // every wave is done with both slots (previous tile) before the
+        // first loads of this one
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int q = 0; q < 2 * LPW; ++q) dma_one(0, slot0, q);
+#pragma unroll
+        for (int q = 0; q < 2 * LPW; ++q) dma_one(min(1, KT - 1), slot1, q);
+        wait_vmcnt<2 * LPW>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) frag_one(fa0, fb0, slot0, 0, q);
+
+        // Stage s: sub-step 2s on fa0 while the second half of stage s is
+        // read into fa1; then sub-step 2s+1 on fa1 while the first half of
+        // stage s+1 is read into fa0 and stage s+2 is loaded into the slot
+        // that stage s leaves.  Loads past the end re-load the last stage,
+        // reads past the end fill registers that are never used.
+        auto stage = [&](int s, u32x4 *cur, u32x4 *nxt) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+#pragma unroll
+            for (int q = 0; q < 64; ++q) {
+                mfma_agpr(acc[q >> 3][q & 7], fb0[q & 7], fa0[q >> 3]);
+                if (q % 3 == 0 && q / 3 < 16) frag_one(fa1, fb1, cur, 1, q / 3);
+            }
+            // own reads done, stage s+1 landed (this wave's part), then
+            // every wave's part
+            __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4));
+            __builtin_amdgcn_s_barrier();
+            const int nx = min(s + 2, KT - 1);
+#pragma unroll
+            for (int q = 0; q < 64; ++q) {
+                mfma_agpr(acc[q >> 3][q & 7], fb1[q & 7], fa1[q >> 3]);
+                if (q % 3 == 0 && q / 3 < 16) frag_one(fa0, fb0, nxt, 0, q / 3);
+                if (q % 4 == 1) dma_one(nx, cur, q / 4);
+            }
+        };
+        // The compiler does not know that the asm are MFMAs, so the wait
+        // states they need against other instructions are inserted here, in
+        // the loop body, where neither the accumulator zeroing before the
+        // loop nor the reads after it can be placed: a few before the first
+        // MFMA (a VALU write of its srcC), and after the last MFMA enough for
+        // a read of its result (an 8-pass XDL op).
+        for (int s = 0; s < KT; s += 2) {
+            asm volatile("s_nop 4");
+            stage(s, slot0, slot1);
+            stage(s + 1, slot1, slot0);
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+        }
+
+        // Epilogue through LDS.  A wave's MFMA layout gives each lane 4
+        // consecutive columns of 16 rows per block, so direct stores would
+        // write 32-byte pieces of 16 rows per instruction.  Instead each
+        // wave converts its quarter (bias, then the activation or SwiGLU,
+        // to bf16) into a staging copy of the output tile in the idle slots
+        // (rows 0-127 in slot0, 128-255 in slot1; 512-byte rows whose
+        // 16-byte chunks are XOR-swizzled by the row), and the block then
+        // writes whole row segments with 16-byte stores.
+        __builtin_amdgcn_s_waitcnt(0);   // re-loads landed, own reads done
+        __builtin_amdgcn_s_barrier();    // and every wave's
+        char *stg = (char *)(wm ? slot1 : slot0);
+        const int cq = 4 * (lane >> 4);
+        // 4 values at staging row rl (0..127), output column c (c % 4 == 0)
+        auto put = [&](int rl, int c, const float (&v)[4]) __attribute__((always_inline)) {
+            const int sc = (c >> 3) ^ (rl & 15);
+            u32x2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *(u32x2 *)(stg + rl * 512 + sc * 16 + ((c >> 2) & 1) * 8) = o;
+        };
+        const bool gated = UP && p.gated;
+        if (gated) {
+            // a wave's 128 columns are two 64-column chunks of the virtual
+            // panel: blocks 4c, 4c+1 are the gate rows and 4c+2, 4c+3 the
+            // up rows of the tile's output features 64 wn + 32 c + 16 jj + ...
+            const int F = N >> 1;
+            const uint16_t *b1 = routed
+                ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+                : (const uint16_t *)p.bias_s;
+            const uint16_t *b3 = routed
+                ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+                : (const uint16_t *)p.bias_s3;
+            float bv1[2][2][4], bv3[2][2][4];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int f = (n0 >> 1) + 64 * wn + 32 * c + 16 * jj + cq + t;
+                        bv1[c][jj][t] = b1 ? bf16_to_f32(b1[f]) : 0.0f;
+                        bv3[c][jj][t] = b3 ? bf16_to_f32(b3[f]) : 0.0f;
+                    }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        float h[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const float gv = acc[i][4 * c + jj][t] + bv1[c][jj][t];
+                            const float uv = acc[i][4 * c + 2 + jj][t] + bv3[c][jj][t];
+                            h[t] = silu_f(gv) * uv;
+                        }
+                        put(i * 16 + l16, 64 * wn + 32 * c + 16 * jj + cq, h);
+                    }
+        } else {
+            const uint16_t *bg = routed
+                ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+                : (const uint16_t *)p.bias_s;
+            // the activation is chosen once, outside the element loops, so
+            // those stay straight-line code
+            const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
+            float bv[8][4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = n0 + wn * 128 + j * 16 + cq;
+                if (bg) {
+                    const u32x2 bb = *(const u32x2 *)(bg + n);
+                    bv[j][0] = bf16_lo(bb.x);
+                    bv[j][1] = bf16_hi(bb.x);
+                    bv[j][2] = bf16_lo(bb.y);
+                    bv[j][3] = bf16_hi(bb.y);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) bv[j][t] = 0.0f;
+                }
+            }
+            auto convert = [&](auto fn) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
+                        put(i * 16 + l16, wn * 128 + j * 16 + cq, v);
+                    }
+            };
+            if (act == ACT_GELU)
+                convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
+            else if (act == ACT_SILU)
+                convert([](float z) __attribute__((always_inline)) { return silu_f(z); });
+            else
+                convert([](float z) __attribute__((always_inline)) { return z; });
+        }
+        __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        // 16-byte chunks per output row: 32 (256 columns) or 16 (gated)
+        const int cpr = gated ? 16 : 32;
+        const int rpp = 256 / cpr;                 // rows per block pass
+        const int rr = tid / cpr, cc = tid % cpr;
+        uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
+        for (int r0 = 0; r0 < BM; r0 += rpp) {
+            const int row = r0 + rr;
+            if (row < nrows) {
+                const char *sb = (const char *)(row < 128 ? slot0 : slot1);
+                const int rl = row & 127;
+                const u32x4 v = *(const u32x4 *)(sb + rl * 512 + ((cc ^ (rl & 15)) * 16));
+                *(u32x4 *)(out + (size_t)(row0 + row) * p.ldo) = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------
 // Weight-streaming kernel for groups of at most a few dozen rows (decode).
 // Work units are (group, 32-column slab) over the full K; the grid is
 // persistent and walks the units with a stride, so equal-cost units spread
@@ -1037,6 +1326,12 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <bool UP>
+hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(gemm_bf16_w4<UP>, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, bool UP>
 hipError_t launch_lds(const GemmParams &p, int grid, hipStream_t s) {
     const int lds = 2 * (BM + BN) * 8 * 16;
@@ -1066,6 +1361,7 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA64_256x256: return {256, 256, 512, 2 * 512 * 128};
     case GEMM_BF16_DMA64_128x256: return {128, 256, 256, 2 * 384 * 128};
     case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
+    case GEMM_BF16_W4_256x256: return {256, 256, 256, 2 * 512 * 128};
     default: return {64, 64, 256, 0};
     }
 }
@@ -1100,6 +1396,8 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_DMA64_320x256:
         return up ? launch_dma64<320, 256, 2, 4, true>(p, grid, s)
                   : launch_dma64<320, 256, 2, 4, false>(p, grid, s);
+    case GEMM_BF16_W4_256x256:
+        return up ? launch_w4<true>(p, grid, s) : launch_w4<false>(p, grid, s);
 
     case GEMM_BF16_STREAM_32x64:
         if (up)

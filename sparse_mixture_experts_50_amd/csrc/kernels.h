@@ -63,6 +63,7 @@ enum GemmVariant {
     GEMM_BF16_STREAM_64x64 = 11,  // streaming with 64-column units
     GEMM_FP8_STREAM_64x64 = 12,
     GEMM_BF16_DMA64_320x256 = 13,  // 320-row tiles: one per ~257-320-row group
+    GEMM_BF16_W4_256x256 = 14,     // four waves of 128 x 128, K % 128 == 0
 };
 
 // Variants that stream weights over persistent (group, column-slab) units.

@@ -133,6 +133,14 @@ bool gate_capable(int v) {
            v != GEMM_FP8_STREAM_32x64;
 }
 
+// The four-wave kernel walks K in pairs of 64-deep stages and addresses
+// its A operand with 32-bit byte offsets.
+bool w4_fits(const moe_desc *d, bool up) {
+    const long long K = up ? d->d : d->d_ff;
+    const long long rows = up ? d->T : routed_rows(d) + (long long)d->n_shared * d->T;
+    return K >= 128 && K % 128 == 0 && rows * K * 2 < (1ll << 32);
+}
+
 int variant_override(bool up, const moe_desc *d, int N) {
     const char *v = getenv(up ? "MOE_GEMM_VARIANT_UP" : "MOE_GEMM_VARIANT_DOWN");
     if (!v || !*v) return -1;
@@ -142,10 +150,11 @@ int variant_override(bool up, const moe_desc *d, int N) {
     const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
                         id == GEMM_FP8_STREAM_64x64;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_DMA64_320x256 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4_256x256 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
+    if (id == GEMM_BF16_W4_256x256 && !w4_fits(d, up)) return -1;
     // the streaming kernels split K in four quarters of whole load batches
     // (4 x 32 deep for 32-column units, 2 x 32 for 64-column ones)
     if (id == GEMM_BF16_STREAM_32x64 && (d->d % 512 != 0 || d->d_ff % 512 != 0))
@@ -156,12 +165,13 @@ int variant_override(bool up, const moe_desc *d, int N) {
 }
 
 // Expected cost of a grouped GEMM with BM-row tiles: whole rounds of
-// tiles over the persistent grid, each round costing a tile's time.  A
-// tile streams its BN-column weight panel whatever its height, which is
-// worth about 128 rows of the rest.  Top-k group sizes get 10 % headroom
-// for routing skew (at most the capacity); expert-choice groups hold
-// exactly C rows.
-double tile_cost(const moe_desc *d, int N, int bm, int slots) {
+// tiles over the persistent grid, each round costing a tile's time, in
+// units of one tile row.  A tile streams its BN-column weight panel and
+// runs its prologue and epilogue whatever its height: worth about 128 rows
+// for the eight-wave kernels and 40 for the four-wave one (measured on the
+// Mixtral-shaped GEMMs).  Top-k group sizes get 10 % headroom for routing
+// skew (at most the capacity); expert-choice groups hold exactly C rows.
+double tile_cost(const moe_desc *d, int N, int bm, int slots, double over) {
     double avg = (double)routed_rows(d) / d->E;
     if (!expert_choice(d)) {
         avg *= 1.1;
@@ -170,10 +180,10 @@ double tile_cost(const moe_desc *d, int N, int bm, int slots) {
     const double mt = ceil(avg / bm) * d->E +
                       (double)d->n_shared * ceil((double)d->T / bm);
     const double tiles = mt * (N / 256);
-    return ceil(tiles / slots) * (bm + 128.0);
+    return ceil(tiles / slots) * (bm + over);
 }
 
-int pick_variant(const moe_desc *d, int N) {
+int pick_variant(const moe_desc *d, int N, bool up) {
     if (d->dtype == MOE_F32) return GEMM_F32_64x64;
     if (d->expert_fp8) return GEMM_FP8_STREAM_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
@@ -186,11 +196,19 @@ int pick_variant(const moe_desc *d, int N) {
     if (avg <= 48.0) return GEMM_BF16_32x256;
     if (avg <= 192.0) return GEMM_BF16_DMA64_128x256;
     // 256- or 320-row tiles: 320 covers a ~257..320-row group in one tile
-    // and can turn a partial last round into a full one
+    // and can turn a partial last round into a full one; the four-wave
+    // 256-row kernel has the cheapest tile where K allows it
     const int slots = device_cus();
-    return tile_cost(d, N, 320, slots) < tile_cost(d, N, 256, slots)
-               ? GEMM_BF16_DMA64_320x256
-               : GEMM_BF16_DMA64_256x256;
+    int best = GEMM_BF16_DMA64_256x256;
+    double cost = tile_cost(d, N, 256, slots, 128.0);
+    const double c320 = tile_cost(d, N, 320, slots, 128.0);
+    if (c320 < cost) {
+        best = GEMM_BF16_DMA64_320x256;
+        cost = c320;
+    }
+    if (w4_fits(d, up) && tile_cost(d, N, 256, slots, 40.0) < cost)
+        best = GEMM_BF16_W4_256x256;
+    return best;
 }
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
@@ -313,7 +331,7 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
              bool up, const void *x, void *ws, hipStream_t s) {
     const GemmParams p = gemm_params(d, w, r, up, x, ws);
     int variant = variant_override(up, d, p.N);
-    if (variant < 0) variant = pick_variant(d, p.N);
+    if (variant < 0) variant = pick_variant(d, p.N, up);
     // check_desc keeps a gated N = 2*d_ff a multiple of 256, so pick_variant
     // never lands on a variant that cannot pair gate and up columns
     if (gated_up(d, up) && !gate_capable(variant)) return MOE_ERR_UNSUPPORTED;

@@ -69,7 +69,7 @@ def test_small_full_parity(name):
 
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7", "8",
-                                     "9", "11", "13"])
+                                     "9", "11", "13", "14"])
 def test_every_gemm_variant(variant, monkeypatch):
     """Each bf16 tile variant forced on a shape with groups of 0 to ~100
     rows (several row chunks for the small-tile kernels)."""
@@ -80,6 +80,21 @@ def test_every_gemm_variant(variant, monkeypatch):
     gpu = gpu_forward(w, inp)
     rep = check_layer(w, inp, gpu)
     say(f"[variant {variant}] {rep}")
+
+
+@pytest.mark.parametrize("variant", ["13", "14"])
+def test_large_tile_variants_multi_tile_groups(variant, monkeypatch):
+    """The 320- and four-wave 256-row kernels on groups of ~600 rows (three
+    row tiles, the last ragged), eight column tiles and 16 stages of K,
+    sampled rows against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", variant)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", variant)
+    w = scaled(W["mixtral_prefill"], T=2400, d=1024, d_ff=2048)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    tokens = sample_tokens(w.T, 48, seed=3)
+    rep = check_layer(w, inp, gpu, tokens=tokens)
+    say(f"[large tiles {variant}] {rep}")
 
 
 def test_step_entry_points_match_forward():
