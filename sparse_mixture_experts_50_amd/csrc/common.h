@@ -24,14 +24,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
-// Round-to-nearest-even float -> bfloat16 (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// float -> bfloat16, round to nearest even, by gfx950's v_cvt_pk_bf16_f32
+// (one instruction per pair; bit-identical to the integer rounding
+// u + 0x7FFF + ((u >> 16) & 1) on finite inputs, checked on the device over
+// every low-half pattern, ties included).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
