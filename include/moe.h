@@ -203,15 +203,19 @@ typedef struct moe_routing {
  * MOE_ERR_INVALID_ARG if T < 0 or E < 1. */
 int32_t moe_capacity(int32_t T, int32_t E, double cf);
 
-/* Host, pure.  Bytes of workspace the calls below need for this shape, or 0
- * if the descriptor is invalid.  One workspace serves every entry point;
+/* Host.  Bytes of workspace the calls below need for this shape, or 0 if
+ * the descriptor is invalid; a function of the descriptor alone (and of the
+ * MOE_ROUTER_SPLIT tuning variable, when set; a call whose workspace is
+ * then too small returns MOE_ERR_WORKSPACE).  One workspace serves every entry point;
  * moe_router_topk writes router partial sums into it that moe_permute reads,
  * and moe_grouped_ffn writes the expert outputs that moe_combine reads, so
  * run a sequence of calls with one workspace. */
 size_t moe_workspace_size(const moe_desc *desc);
 
-/* Router GEMM fused with bias, softmax, top-k and renormalisation
- * (layer steps 1-2).  Reads x [T][d] and the router weights; writes
+/* Router GEMM with bias, softmax, top-k and renormalisation (layer steps
+ * 1-2); bf16 layers run it as one kernel or, for deep or few-token shapes,
+ * as partial logits over depth ranges (fp32, in the workspace) followed by
+ * the routing kernel.  Reads x [T][d] and the router weights; writes
  * r->topk_idx, r->topk_w and per-token-tile probability column sums into
  * the workspace (consumed by moe_permute for p_i).  Expert choice: writes
  * topk_idx = e and topk_w = p[t,e] for all E experts, sets every entry of

@@ -9,6 +9,8 @@
 
 // Tokens per router block.
 #define MOE_ROUTER_TOKENS 32
+// Most depth ranges the bf16 router's logits are split into.
+#define MOE_ROUTER_MAX_SPLITS 8
 // Assignments per permute chunk.
 #define MOE_PERMUTE_CHUNK 256
 
@@ -23,8 +25,19 @@ struct RouterParams {
     float *zh_part;       // [ceil(T/32)][2]: sum lse^2, sum entropy (nats)
     float *scores;        // expert choice: logits [E][T]; null for top-k
     int32_t *slot_of;     // expert choice: [T][E], set to -1 here
+    float *part;          // split bf16 router: [S][T][E] fp32 partial sums
+                          // over S consecutive depth ranges of kc each
+    int S, kc;            // S = 0: the fused kernel
     int T, d, E, k;
 };
+
+// How the bf16 router runs: fused (one kernel, 32 tokens per block) or
+// split (partial logits over S depth ranges of kc each, then routing).
+struct RouterPlan {
+    int ep, tokens, S, kc;
+    bool split;
+};
+RouterPlan router_plan(int T, int d, int E, int cus);
 
 struct PermuteParams {
     const int32_t *topk_idx;  // [T*k]

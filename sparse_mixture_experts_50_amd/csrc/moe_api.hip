@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t p_part, zh_part, blk, scores, h, yp, total;
+    size_t p_part, zh_part, blk, scores, rpart, h, yp, total;
     int n_rtiles, n_chunks;
     size_t rows;
 };
@@ -69,6 +69,18 @@ int check_desc(const moe_desc *d) {
     return MOE_OK;
 }
 
+// The router's logits split depends on the shape only (sized for the
+// MI355X's 256 CUs), so the workspace size is a pure function of the
+// descriptor.
+RouterPlan plan(const moe_desc *d) {
+    RouterPlan r = router_plan(d->T, d->d, d->E, 256);
+    // tuning and test knob: MOE_ROUTER_SPLIT=0 / 1 forces the fused or the
+    // split bf16 router (read here, so the workspace size follows it)
+    const char *v = getenv("MOE_ROUTER_SPLIT");
+    if (v && (v[0] == '0' || v[0] == '1') && v[1] == 0) r.split = v[0] == '1';
+    return r;
+}
+
 WsLayout layout(const moe_desc *d) {
     WsLayout L;
     const size_t es = elem_bytes(d->dtype);
@@ -88,6 +100,9 @@ WsLayout layout(const moe_desc *d) {
     off += align_up((size_t)L.n_chunks * d->E * sizeof(int32_t));
     L.scores = off;       // expert choice: logits transposed, [E][T] fp32
     if (expert_choice(d)) off += align_up((size_t)d->E * d->T * sizeof(float));
+    L.rpart = off;        // bf16 router: partial logits, [S][T][E] fp32
+    if (d->dtype == MOE_BF16 && plan(d).split)
+        off += align_up((size_t)plan(d).S * d->T * d->E * sizeof(float));
     L.h = off;
     off += align_up(L.rows * d->d_ff * es);
     L.yp = off;
@@ -377,6 +392,10 @@ int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
     p.zh_part = (float *)at(ws, L.zh_part);
     p.scores = expert_choice(desc) ? (float *)at(ws, L.scores) : nullptr;
     p.slot_of = r->slot_of;
+    const RouterPlan rp = plan(desc);
+    p.part = (float *)at(ws, L.rpart);
+    p.S = rp.split ? rp.S : 0;
+    p.kc = rp.kc;
     p.T = desc->T;
     p.d = desc->d;
     p.E = desc->E;

@@ -5,13 +5,18 @@
 // sum 1; sec. 2.4: routing uses logits - b_i.  "AI-Research-SKILLs MoE
 // training guide", sec. 3.1: the router is an nn.Linear (additive bias).
 //
-// One block (16 waves) routes 32 tokens.  bf16 logits come from MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulate); fp32 logits from plain FMA.
-// The logits never leave the chip: each wave then takes 2 tokens and does
-// max, exp-sum, selection and renormalisation across its 64 lanes.  The
-// selection compares fp32 logits (softmax is monotonic), ties to the lower
-// expert index.  Each block also writes its column sums of the softmax
-// probabilities, reduced later in a fixed order for p_i.
+// bf16: two kernels.  router_logits spreads the logits GEMM over many
+// blocks: each block takes 32 (E <= 64) or 128 (E > 64) tokens, all
+// experts and one of S consecutive depth ranges, with MFMA 32x32x16 (fp32
+// accumulation), and writes fp32 partial sums; a single block per 32 tokens
+// would pull every token row through one CU.  router_route sums the S
+// partials in order (deterministic), then routes 32 tokens per block: for
+// E <= 32 one lane per token walks its E logits in registers (no cross-lane
+// traffic); for larger E each wave takes 2 tokens across its 64 lanes.
+// fp32: one kernel with FMA logits.  The selection compares fp32 logits
+// (softmax is monotonic), ties to the lower expert index.  Each 32-token
+// block also writes its column sums of the softmax probabilities, reduced
+// later in a fixed order for p_i, and its logsumexp / entropy sums.
 //
 // Expert choice ("AI-Research-SKILLs MoE training guide", sec. 4.2): no
 // top-k; every token writes the probabilities of all E experts and resets
@@ -181,11 +186,238 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
     }
 }
 
-// bf16 logits with MFMA.  EP = E rounded up to 32/64/128/256.  The 16
-// waves split the 32-expert tiles and, beyond that, the depth d, so even a
-// single block (a 32-token decode step) keeps 16 waves of loads in flight.
+// Partial logits over one depth range.  EP = E rounded up to 32..256.
+// E <= 64: a block is one 32-token tile; its 4 waves split the expert tiles
+// and then the depth range (KW interleaved 16-deep steps each), reduced
+// through LDS in wave order.  E > 64: a block is four 32-token tiles, one
+// per wave, each wave covering every expert tile over the whole range.
+// Rows past T and experts past E read a clamped valid row: their sums land
+// in entries that are never written out, so the loads need no predicate.
 template <int EP>
-__global__ __launch_bounds__(RW * 64) void router_bf16(RouterParams p) {
+__global__ __launch_bounds__(256) void router_logits(RouterParams p) {
+    constexpr int ET = EP / 32;                 // 32-expert tiles
+    constexpr bool SMALL = EP <= 64;
+    constexpr int KW = SMALL ? 4 / ET : 1;      // depth splits in a block
+    constexpr int TPW = SMALL ? 1 : ET;         // tiles per wave
+    __shared__ float red[SMALL ? KW : 1][32][SMALL ? EP : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int s = blockIdx.y;
+    const int k_lo = s * p.kc, k_hi = min(p.d, k_lo + p.kc);
+    const int tt = SMALL ? blockIdx.x : blockIdx.x * 4 + wave;   // token tile
+    const int t0 = tt * 32;
+    const int kw = SMALL ? wave / ET : 0;
+    const int tok = min(t0 + (lane & 31), p.T - 1);
+    const int kg = (lane >> 5) * 8;
+    const uint16_t *xrow = (const uint16_t *)p.x + (size_t)tok * p.d + kg;
+    const uint16_t *wrow[TPW];
+    int etile[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        etile[i] = SMALL ? wave % ET : i;
+        const int e = min(etile[i] * 32 + (lane & 31), p.E - 1);
+        wrow[i] = (const uint16_t *)p.wr + (size_t)e * p.d + kg;
+    }
+    floatx16 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+#pragma unroll 8
+    for (int k0 = k_lo + kw * 16; k0 < k_hi; k0 += 16 * KW) {
+        const u32x4 av = *(const u32x4 *)(xrow + k0);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const u32x4 bv = *(const u32x4 *)(wrow[i] + k0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(av), as_bf16x8(bv), acc[i], 0, 0, 0);
+        }
+    }
+    // D[token][expert]: lane holds expert column lane%32 and token rows
+    // 8*(v/4) + 4*(lane/32) + v%4.
+    float *part = p.part + (size_t)s * p.T * p.E;
+    if (SMALL) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int tl = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            red[kw][tl][etile[0] * 32 + (lane & 31)] = acc[0][v];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < 32 * p.E; i += 256) {
+            const int tl = i / p.E, e = i - tl * p.E;
+            if (t0 + tl >= p.T) continue;
+            float sum = red[0][tl][e];
+#pragma unroll
+            for (int w = 1; w < KW; ++w) sum += red[w][tl][e];
+            part[(size_t)(t0 + tl) * p.E + e] = sum;
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int e = etile[i] * 32 + (lane & 31);
+        if (e >= p.E) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = t0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (t < p.T) part[(size_t)t * p.E + e] = acc[i][v];
+        }
+    }
+}
+
+// One lane per token (E <= EP = 32): softmax, statistics and selection on
+// the token's logits held in registers, written as selects rather than
+// branches (padding experts hold -inf and never win a pick, k <= E); the
+// probabilities go to pr (LDS), from which the picked weights are
+// renormalised (the softmax denominator cancels).  lg: the block's summed
+// logits; addv / subv: the router and balancing biases (0 where absent).
+template <int EP>
+__device__ __forceinline__ void route_lanes(const float (*lg)[EP],
+                                            const RouterParams &p,
+                                            const float *addv,
+                                            const float *subv,
+                                            float (*pr)[EP + 1],
+                                            float (*zh)[2]) {
+    const int tl = threadIdx.x;          // 0..31
+    const int t = blockIdx.x * RT + tl;
+    float z = 0.0f, h = 0.0f;
+    if (t < p.T) {
+        float v[EP], ex[EP];
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            float s = lg[tl][e];
+            s = s + addv[e];
+            s = s - subv[e];
+            v[e] = e < p.E ? s : -INFINITY;
+            m = fmaxf(m, v[e]);
+        }
+        float S = 0.0f, pl = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            const bool real = e < p.E;
+            ex[e] = real ? expf(v[e] - m) : 0.0f;
+            S += ex[e];
+            pl += real ? ex[e] * (v[e] - m) : 0.0f;
+        }
+        const float inv = 1.0f / S;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) pr[tl][e] = ex[e] * inv;
+        // monitors: logsumexp = m + ln S; entropy (nats) = ln S - sum p (l - m)
+        const float lnS = logf(S);
+        const float lse = m + lnS;
+        z = lse * lse;
+        h = lnS - pl / S;
+        if (p.scores) {          // expert choice: all experts, weight p
+            for (int e = 0; e < p.E; ++e) {
+                p.topk_idx[(size_t)t * p.E + e] = e;
+                p.topk_w[(size_t)t * p.E + e] = pr[tl][e];
+                p.slot_of[(size_t)t * p.E + e] = -1;  // picks come later
+                p.scores[(size_t)e * p.T + t] = lg[tl][e] + addv[e] - subv[e];
+            }
+        } else {
+            // k rounds of (max logit, lowest index) over the untaken
+            // experts; the rounds run twice (the sum of the picked
+            // probabilities is needed before the first weight is written)
+            // rather than reading the picks back from memory
+            auto pick = [&](uint32_t taken) __attribute__((always_inline)) {
+                float bv = -INFINITY;
+                int be = -1;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) {
+                    const bool better = !((taken >> e) & 1u) &&
+                                        (be < 0 || v[e] > bv);
+                    bv = better ? v[e] : bv;
+                    be = better ? e : be;
+                }
+                return be;
+            };
+            uint32_t taken = 0;
+            float wsum = 0.0f;
+            for (int j = 0; j < p.k; ++j) {
+                const int be = pick(taken);
+                taken |= 1u << be;
+                wsum += pr[tl][be];
+            }
+            const float winv = 1.0f / wsum;
+            taken = 0;
+            for (int j = 0; j < p.k; ++j) {
+                const int be = pick(taken);
+                taken |= 1u << be;
+                p.topk_idx[(size_t)t * p.k + j] = be;
+                p.topk_w[(size_t)t * p.k + j] = pr[tl][be] * winv;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EP; ++e) pr[tl][e] = 0.0f;
+    }
+    zh[tl][0] = z;
+    zh[tl][1] = h;
+}
+
+// Sum the S partial logit planes of 32 tokens in order, then route them:
+// one lane per token in a 256-thread block (E <= 32: a handful of logits
+// per lane beats a chain of 64-lane reductions), or 2 tokens per wave in a
+// 1024-thread block.
+template <int EP>
+__global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterParams p) {
+    constexpr bool SMALL = EP <= 32;
+    __shared__ float lg[1][RT][EP];
+    __shared__ float pp[SMALL ? 1 : RW][EP];
+    __shared__ float pr[SMALL ? RT : 1][EP + 1];
+    __shared__ float zh[RT][2];
+    __shared__ float addv[SMALL ? EP : 1], subv[SMALL ? EP : 1];
+    const int t0 = blockIdx.x * RT;
+    const size_t plane = (size_t)p.T * p.E;
+    if (SMALL && threadIdx.x < EP) {
+        const int e = threadIdx.x;
+        addv[e] = (e < p.E && p.add) ? p.add[e] : 0.0f;
+        subv[e] = (e < p.E && p.sub) ? p.sub[e] : 0.0f;
+    }
+    for (int i = threadIdx.x; i < RT * p.E; i += blockDim.x) {
+        const int tl = i / p.E, e = i - tl * p.E;
+        const int t = min(t0 + tl, p.T - 1);
+        const float *src = p.part + (size_t)t * p.E + e;
+        // every load issued before the in-order sum
+        float a[MOE_ROUTER_MAX_SPLITS];
+#pragma unroll
+        for (int k = 0; k < MOE_ROUTER_MAX_SPLITS; ++k)
+            a[k] = k < p.S ? src[k * plane] : 0.0f;
+        float s = a[0];
+#pragma unroll
+        for (int k = 1; k < MOE_ROUTER_MAX_SPLITS; ++k)
+            if (k < p.S) s += a[k];
+        lg[0][tl][e] = s;
+    }
+    __syncthreads();
+    if (!SMALL) {
+        route_tokens<EP, 1>(lg, p, pp);
+        return;
+    }
+    if (threadIdx.x < RT) route_lanes<EP>(lg[0], p, addv, subv, pr, zh);
+    __syncthreads();
+    // block sums in token order: probability columns, then lse^2, entropy
+    for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+        float s = pr[0][e];
+        for (int tl = 1; tl < RT; ++tl) s += pr[tl][e];
+        p.p_part[(size_t)blockIdx.x * p.E + e] = s;
+    }
+    if (threadIdx.x >= 64 && threadIdx.x < 66) {
+        const int c = threadIdx.x - 64;
+        float s = zh[0][c];
+        for (int tl = 1; tl < RT; ++tl) s += zh[tl][c];
+        p.zh_part[(size_t)blockIdx.x * 2 + c] = s;
+    }
+}
+
+// bf16, fused: one block (16 waves) computes and routes 32 tokens.  The
+// waves split the 32-expert tiles and, beyond that, the depth d; the logits
+// stay in LDS.  Used when there are enough such blocks to fill the GPU and
+// each pulls little through its CU (short d, few experts).
+template <int EP>
+__global__ __launch_bounds__(RW * 64) void router_fused(RouterParams p) {
     constexpr int NTE = EP / 32;                  // 32-expert tiles
     constexpr int KS = NTE >= RW ? 1 : RW / NTE;  // k-splits across waves
     constexpr int TPW = NTE >= RW ? NTE / RW : 1; // tiles per wave
@@ -274,24 +506,75 @@ __global__ __launch_bounds__(RW * 64) void router_f32(RouterParams p) {
 
 }  // namespace
 
+RouterPlan router_plan(int T, int d, int E, int cus) {
+    RouterPlan r;
+    r.ep = E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+    // fused when its 32-token blocks fill the GPU and each reads at most
+    // ~200 KB (32 token rows and every router row)
+    const long long fblocks = ((long long)T + RT - 1) / RT;
+    const double fbytes = 2.0 * d * (RT + E);
+    r.split = !(fblocks >= cus && fbytes <= 200e3);
+    const bool small = r.ep <= 64;
+    r.tokens = small ? 32 : 128;
+    const int kw = small ? 4 / (r.ep / 32) : 1;
+    const long long blocks = T > 0 ? (T + r.tokens - 1) / r.tokens : 1;
+    // about two blocks per CU (one for E > 64, whose blocks are four times
+    // larger), each wave keeping at least 8 MFMA steps of its range
+    const long long want = (long long)cus * (small ? 2 : 1);
+    int S = (int)((want + blocks - 1) / blocks);
+    const int most = d / (16 * 8 * kw);
+    if (S > most) S = most;
+    if (S > MOE_ROUTER_MAX_SPLITS) S = MOE_ROUTER_MAX_SPLITS;
+    if (S < 1) S = 1;
+    // whole 16-deep steps per range (d is a multiple of 64)
+    int kc = (d + S - 1) / S;
+    kc = (kc + 15) / 16 * 16;
+    r.S = (d + kc - 1) / kc;
+    r.kc = kc;
+    return r;
+}
+
 hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
     const int blocks = (p.T + RT - 1) / RT;
     const dim3 grid(blocks), block(RW * 64);
     const int EP = p.E <= 32 ? 32 : p.E <= 64 ? 64 : p.E <= 128 ? 128 : 256;
+    if (dtype == 1 && !p.S) {
+        switch (EP) {
+        case 32: hipLaunchKernelGGL(router_fused<32>, grid, block, 0, s, p); break;
+        case 64: hipLaunchKernelGGL(router_fused<64>, grid, block, 0, s, p); break;
+        case 128: hipLaunchKernelGGL(router_fused<128>, grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL(router_fused<256>, grid, block, 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     if (dtype == 1) {
+        const int tokens = EP <= 64 ? 32 : 128;
+        const dim3 lgrid((p.T + tokens - 1) / tokens, p.S);
         switch (EP) {
-        case 32: hipLaunchKernelGGL(router_bf16<32>, grid, block, 0, s, p); break;
-        case 64: hipLaunchKernelGGL(router_bf16<64>, grid, block, 0, s, p); break;
-        case 128: hipLaunchKernelGGL(router_bf16<128>, grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL(router_bf16<256>, grid, block, 0, s, p); break;
+        case 32:
+            hipLaunchKernelGGL(router_logits<32>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_route<32>, grid, dim3(256), 0, s, p);
+            break;
+        case 64:
+            hipLaunchKernelGGL(router_logits<64>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_route<64>, grid, block, 0, s, p);
+            break;
+        case 128:
+            hipLaunchKernelGGL(router_logits<128>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_route<128>, grid, block, 0, s, p);
+            break;
+        default:
+            hipLaunchKernelGGL(router_logits<256>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_route<256>, grid, block, 0, s, p);
+            break;
         }
-    } else {
-        switch (EP) {
-        case 32: hipLaunchKernelGGL(router_f32<32>, grid, block, 0, s, p); break;
-        case 64: hipLaunchKernelGGL(router_f32<64>, grid, block, 0, s, p); break;
-        case 128: hipLaunchKernelGGL(router_f32<128>, grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL(router_f32<256>, grid, block, 0, s, p); break;
-        }
+        return hipGetLastError();
+    }
+    switch (EP) {
+    case 32: hipLaunchKernelGGL(router_f32<32>, grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL(router_f32<64>, grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL(router_f32<128>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(router_f32<256>, grid, block, 0, s, p); break;
     }
     return hipGetLastError();
 }
