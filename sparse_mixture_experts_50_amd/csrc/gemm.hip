@@ -623,24 +623,31 @@ __device__ __forceinline__ void mfma_agpr(floatx4 &acc, const bf16x8 &a,
 }
 }  // namespace w4
 
-template <bool UP>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
+// One tile.  Full: 256 rows, the waves 2 x 2 quarters of 128 x 128.  Half
+// (a tile of at most 128 rows, normally a group's last): the waves split
+// the 256 columns, 128 x 64 each, so the tile costs half the MFMAs and
+// half the A loads.  The issue schedule of a 32-deep sub-step: its MFMAs
+// with the next sub-step's fragment reads spread over the first three
+// quarters (full) or half (half), and in a stage's second sub-step the
+// loads of the stage after next spread over the MFMAs.
+template <bool UP, bool HALF>
+__device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
+                                        u32x4 *slot1, int g, int row0,
+                                        int nrows, int n0, bool routed,
+                                        int wave, int lane, int KT) {
     using namespace w4;
-    __shared__ u32x4 slot0[STAGE], slot1[STAGE];
-    __shared__ TileTable tt;
-
+    constexpr int TN = HALF ? 4 : 8;          // 16-column blocks per wave
+    constexpr int WC = HALF ? 64 : 128;       // columns per wave
+    constexpr int LA = HALF ? LPW / 2 : LPW;  // A loads per wave and stage
+    constexpr int NL = LA + LPW;              // loads per wave and stage
+    constexpr int NF = 8 + TN;                // fragment reads per sub-step
+    constexpr int NM = 8 * TN;                // MFMAs per sub-step
+    constexpr int RD = HALF ? 2 : 3;          // a read after every RD MFMAs
+    constexpr int DM = HALF ? 2 : 4;          // a load after every DM MFMAs
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int N = p.N, K = p.K, KT = K / SK;
-    const int NTN = N / BN;
-    const int G = p.E + p.n_shared;
-    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
-                     NTN);
-    const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
-    const int nb = gridDim.x, per = nb >> 3;
-    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int wm = HALF ? 0 : wave >> 1;
+    const int wn = HALF ? wave : wave & 1;
+    const int N = p.N, K = p.K;
     const char *A = (const char *)p.A;
     // Load j of a wave fills rows 8 (wave + 4 j) + lane/8 of an operand,
     // lane%8 being the 16-byte slot; the lane fetches k-chunk
@@ -652,6 +659,232 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     const int l16 = lane & 15;
     const int sw = (l16 >> 1) & 7;
 
+    // A rows past the group's end re-read the tile's first row: their
+    // products land in rows that are never stored
+    uint32_t a_off[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        int rr = (wave + 4 * j) * 8 + lr;
+        if (rr >= nrows) rr = 0;
+        const int slot = row0 + rr;
+        int src = slot;
+        if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+        a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
+    }
+    const char *bbase[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+        bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
+
+    // load q (q < LA: A rows, else B rows) of stage ks into a slot
+    auto dma_one = [&](int ks, u32x4 *st, int q) __attribute__((always_inline)) {
+        const size_t ko = (size_t)ks * SK * 2;
+        if (q < LA)
+            dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
+        else
+            dma16b(bbase[q - LA] + ko + b_lane,
+                   st + BM * CPR + (wave + 4 * (q - LA)) * 64);
+    };
+    // fragment q (q < 8: A block q, else B block q - 8), sub-step kk
+    auto frag_one = [&](bf16x8 (&fa)[8], bf16x8 (&fb)[TN], const u32x4 *st,
+                        int kk, int q) __attribute__((always_inline)) {
+        const int c = (kk * 4 + (lane >> 4)) ^ sw;
+        if (q < 8)
+            fa[q] = as_bf16x8(st[(wm * 128 + q * 16 + l16) * CPR + c]);
+        else
+            fb[q - 8] = as_bf16x8(
+                st[BM * CPR + (wn * WC + (q - 8) * 16 + l16) * CPR + c]);
+    };
+
+    floatx4 acc[8][TN];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa0[8], fb0[TN], fa1[8], fb1[TN];
+
+    // every wave is done with both slots (previous tile) before the first
+    // loads of this one
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < NL; ++q) dma_one(0, slot0, q);
+#pragma unroll
+    for (int q = 0; q < NL; ++q) dma_one(min(1, KT - 1), slot1, q);
+    wait_vmcnt<NL>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < NF; ++q) frag_one(fa0, fb0, slot0, 0, q);
+
+    // Stage s: sub-step 2s on fa0 while the second half of stage s is read
+    // into fa1; then sub-step 2s+1 on fa1 while the first half of stage s+1
+    // is read into fa0 and stage s+2 is loaded into the slot that stage s
+    // leaves.  Loads past the end re-load the last stage, reads past the
+    // end fill registers that are never used.
+    auto stage = [&](int s, u32x4 *cur, u32x4 *nxt) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+            mfma_agpr(acc[q / TN][q % TN], fb0[q % TN], fa0[q / TN]);
+            if (q % RD == 0 && q / RD < NF) frag_one(fa1, fb1, cur, 1, q / RD);
+        }
+        // own reads done, stage s+1 landed (this wave's part), then every
+        // wave's part
+        __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4));
+        __builtin_amdgcn_s_barrier();
+        const int nx = min(s + 2, KT - 1);
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+            mfma_agpr(acc[q / TN][q % TN], fb1[q % TN], fa1[q / TN]);
+            if (q % RD == 0 && q / RD < NF) frag_one(fa0, fb0, nxt, 0, q / RD);
+            if (q % DM == 1 && q / DM < NL) dma_one(nx, cur, q / DM);
+        }
+    };
+    // The compiler does not know that the asm are MFMAs, so the wait states
+    // they need against other instructions are inserted here, in the loop
+    // body, where neither the accumulator zeroing before the loop nor the
+    // reads after it can be placed: a few before the first MFMA (a VALU
+    // write of its srcC), and after the last MFMA enough for a read of its
+    // result (an 8-pass XDL op).
+    for (int s = 0; s < KT; s += 2) {
+        asm volatile("s_nop 4");
+        stage(s, slot0, slot1);
+        stage(s + 1, slot1, slot0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    }
+
+    // Epilogue through LDS.  A wave's MFMA layout gives each lane 4
+    // consecutive columns of 16 rows per block, so direct stores would
+    // write 32-byte pieces of 16 rows per instruction.  Instead each wave
+    // converts its part (bias, then the activation or SwiGLU, to bf16) into
+    // a staging copy of the output tile in the idle slots (rows 0-127 in
+    // slot0, 128-255 in slot1; 512-byte rows whose 16-byte chunks are
+    // XOR-swizzled by the row), and the block then writes whole row
+    // segments with 16-byte stores.
+    __builtin_amdgcn_s_waitcnt(0);   // re-loads landed, own reads done
+    __builtin_amdgcn_s_barrier();    // and every wave's
+    char *stg = (char *)(wm ? slot1 : slot0);
+    const int cq = 4 * (lane >> 4);
+    // 4 values at staging row rl (0..127), output column c (c % 4 == 0)
+    auto put = [&](int rl, int c, const float (&v)[4]) __attribute__((always_inline)) {
+        const int sc = (c >> 3) ^ (rl & 15);
+        u32x2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *(u32x2 *)(stg + rl * 512 + sc * 16 + ((c >> 2) & 1) * 8) = o;
+    };
+    const bool gated = UP && p.gated;
+    if (gated) {
+        // a wave's columns are whole 64-column chunks of the virtual panel:
+        // blocks 4c, 4c+1 are the gate rows and 4c+2, 4c+3 the up rows of
+        // the tile's output features WC wn / 2 + 32 c + 16 jj + ...
+        constexpr int NC = WC / 64;
+        const int F = N >> 1;
+        const uint16_t *b1 = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const uint16_t *b3 = routed
+            ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s3;
+        float bv1[NC][2][4], bv3[NC][2][4];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int f = (n0 >> 1) + (WC / 2) * wn + 32 * c + 16 * jj + cq + t;
+                    bv1[c][jj][t] = b1 ? bf16_to_f32(b1[f]) : 0.0f;
+                    bv3[c][jj][t] = b3 ? bf16_to_f32(b3[f]) : 0.0f;
+                }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    float h[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float gv = acc[i][4 * c + jj][t] + bv1[c][jj][t];
+                        const float uv = acc[i][4 * c + 2 + jj][t] + bv3[c][jj][t];
+                        h[t] = silu_f(gv) * uv;
+                    }
+                    put(i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
+                }
+    } else {
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+        // the activation is chosen once, outside the element loops, so
+        // those stay straight-line code
+        const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
+        float bv[TN][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * WC + j * 16 + cq;
+            if (bg) {
+                const u32x2 bb = *(const u32x2 *)(bg + n);
+                bv[j][0] = bf16_lo(bb.x);
+                bv[j][1] = bf16_hi(bb.x);
+                bv[j][2] = bf16_lo(bb.y);
+                bv[j][3] = bf16_hi(bb.y);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) bv[j][t] = 0.0f;
+            }
+        }
+        auto convert = [&](auto fn) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
+                    put(i * 16 + l16, wn * WC + j * 16 + cq, v);
+                }
+        };
+        if (act == ACT_GELU)
+            convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
+        else if (act == ACT_SILU)
+            convert([](float z) __attribute__((always_inline)) { return silu_f(z); });
+        else
+            convert([](float z) __attribute__((always_inline)) { return z; });
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    // 16-byte chunks per output row: 32 (256 columns) or 16 (gated)
+    const int cpr = gated ? 16 : 32;
+    const int rpp = 256 / cpr;                 // rows per block pass
+    const int rr = tid / cpr, cc = tid % cpr;
+    uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
+    for (int r0 = 0; r0 < (HALF ? 128 : BM); r0 += rpp) {
+        const int row = r0 + rr;
+        if (row < nrows) {
+            const char *sb = (const char *)(row < 128 ? slot0 : slot1);
+            const int rl = row & 127;
+            const u32x4 v = *(const u32x4 *)(sb + rl * 512 + ((cc ^ (rl & 15)) * 16));
+            *(u32x4 *)(out + (size_t)(row0 + row) * p.ldo) = v;
+        }
+    }
+}
+
+template <bool UP>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
+    using namespace w4;
+    __shared__ u32x4 slot0[STAGE], slot1[STAGE];
+    __shared__ TileTable tt;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KT = p.K / SK;
+    const int NTN = p.N / BN;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
+                     NTN);
+    const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
     for (int r = 0;; ++r) {
         const int L = r * nb + xcd * per + loc;
         if (L >= total) break;
@@ -664,215 +897,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
                                       m_tile * BM);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-
-        // A rows past the group's end re-read the tile's first row: their
-        // products land in rows that are never stored
-        uint32_t a_off[LPW];
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            int rr = (wave + 4 * j) * 8 + lr;
-            if (rr >= nrows) rr = 0;
-            const int slot = row0 + rr;
-            int src = slot;
-            if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
-            a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
-        }
-        const char *bbase[LPW];
-#pragma unroll
-        for (int j = 0; j < LPW; ++j)
-            bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
-
-        // load q (q < 8: A rows, else B rows) of stage ks into a slot
-        auto dma_one = [&](int ks, u32x4 *st, int q) __attribute__((always_inline)) {
-            const int j = q % LPW;
-            const size_t ko = (size_t)ks * SK * 2;
-            if (q < LPW)
-                dma16b(A + ko + a_off[j], st + (wave + 4 * j) * 64);
-            else
-                dma16b(bbase[j] + ko + b_lane, st + BM * CPR + (wave + 4 * j) * 64);
-        };
-        // fragment q (q < 8: A block q, else B block q - 8), sub-step kk
-        auto frag_one = [&](bf16x8 (&fa)[8], bf16x8 (&fb)[8], const u32x4 *st,
-                            int kk, int q) __attribute__((always_inline)) {
-            const int c = (kk * 4 + (lane >> 4)) ^ sw;
-            if (q < 8)
-                fa[q] = as_bf16x8(st[(wm * 128 + q * 16 + l16) * CPR + c]);
-            else
-                fb[q - 8] = as_bf16x8(
-                    st[BM * CPR + (wn * 128 + (q - 8) * 16 + l16) * CPR + c]);
-        };
-
-        floatx4 acc[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 fa0[8], fb0[8], fa1[8], fb1[8];
-
-        // every wave is done with both slots (previous tile) before the
-        // first loads of this one
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int q = 0; q < 2 * LPW; ++q) dma_one(0, slot0, q);
-#pragma unroll
-        for (int q = 0; q < 2 * LPW; ++q) dma_one(min(1, KT - 1), slot1, q);
-        wait_vmcnt<2 * LPW>();
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int q = 0; q < 16; ++q) frag_one(fa0, fb0, slot0, 0, q);
-
-        // Stage s: sub-step 2s on fa0 while the second half of stage s is
-        // read into fa1; then sub-step 2s+1 on fa1 while the first half of
-        // stage s+1 is read into fa0 and stage s+2 is loaded into the slot
-        // that stage s leaves.  Loads past the end re-load the last stage,
-        // reads past the end fill registers that are never used.
-        auto stage = [&](int s, u32x4 *cur, u32x4 *nxt) __attribute__((always_inline)) {
-            __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
-#pragma unroll
-            for (int q = 0; q < 64; ++q) {
-                mfma_agpr(acc[q >> 3][q & 7], fb0[q & 7], fa0[q >> 3]);
-                if (q % 3 == 0 && q / 3 < 16) frag_one(fa1, fb1, cur, 1, q / 3);
-            }
-            // own reads done, stage s+1 landed (this wave's part), then
-            // every wave's part
-            __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4));
-            __builtin_amdgcn_s_barrier();
-            const int nx = min(s + 2, KT - 1);
-#pragma unroll
-            for (int q = 0; q < 64; ++q) {
-                mfma_agpr(acc[q >> 3][q & 7], fb1[q & 7], fa1[q >> 3]);
-                if (q % 3 == 0 && q / 3 < 16) frag_one(fa0, fb0, nxt, 0, q / 3);
-                if (q % 4 == 1) dma_one(nx, cur, q / 4);
-            }
-        };
-        // The compiler does not know that the asm are MFMAs, so the wait
-        // states they need against other instructions are inserted here, in
-        // the loop body, where neither the accumulator zeroing before the
-        // loop nor the reads after it can be placed: a few before the first
-        // MFMA (a VALU write of its srcC), and after the last MFMA enough for
-        // a read of its result (an 8-pass XDL op).
-        for (int s = 0; s < KT; s += 2) {
-            asm volatile("s_nop 4");
-            stage(s, slot0, slot1);
-            stage(s + 1, slot1, slot0);
-            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-        }
-
-        // Epilogue through LDS.  A wave's MFMA layout gives each lane 4
-        // consecutive columns of 16 rows per block, so direct stores would
-        // write 32-byte pieces of 16 rows per instruction.  Instead each
-        // wave converts its quarter (bias, then the activation or SwiGLU,
-        // to bf16) into a staging copy of the output tile in the idle slots
-        // (rows 0-127 in slot0, 128-255 in slot1; 512-byte rows whose
-        // 16-byte chunks are XOR-swizzled by the row), and the block then
-        // writes whole row segments with 16-byte stores.
-        __builtin_amdgcn_s_waitcnt(0);   // re-loads landed, own reads done
-        __builtin_amdgcn_s_barrier();    // and every wave's
-        char *stg = (char *)(wm ? slot1 : slot0);
-        const int cq = 4 * (lane >> 4);
-        // 4 values at staging row rl (0..127), output column c (c % 4 == 0)
-        auto put = [&](int rl, int c, const float (&v)[4]) __attribute__((always_inline)) {
-            const int sc = (c >> 3) ^ (rl & 15);
-            u32x2 o;
-            o.x = pack_bf16x2(v[0], v[1]);
-            o.y = pack_bf16x2(v[2], v[3]);
-            *(u32x2 *)(stg + rl * 512 + sc * 16 + ((c >> 2) & 1) * 8) = o;
-        };
-        const bool gated = UP && p.gated;
-        if (gated) {
-            // a wave's 128 columns are two 64-column chunks of the virtual
-            // panel: blocks 4c, 4c+1 are the gate rows and 4c+2, 4c+3 the
-            // up rows of the tile's output features 64 wn + 32 c + 16 jj + ...
-            const int F = N >> 1;
-            const uint16_t *b1 = routed
-                ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
-                : (const uint16_t *)p.bias_s;
-            const uint16_t *b3 = routed
-                ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
-                : (const uint16_t *)p.bias_s3;
-            float bv1[2][2][4], bv3[2][2][4];
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int f = (n0 >> 1) + 64 * wn + 32 * c + 16 * jj + cq + t;
-                        bv1[c][jj][t] = b1 ? bf16_to_f32(b1[f]) : 0.0f;
-                        bv3[c][jj][t] = b3 ? bf16_to_f32(b3[f]) : 0.0f;
-                    }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        float h[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const float gv = acc[i][4 * c + jj][t] + bv1[c][jj][t];
-                            const float uv = acc[i][4 * c + 2 + jj][t] + bv3[c][jj][t];
-                            h[t] = silu_f(gv) * uv;
-                        }
-                        put(i * 16 + l16, 64 * wn + 32 * c + 16 * jj + cq, h);
-                    }
-        } else {
-            const uint16_t *bg = routed
-                ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
-                : (const uint16_t *)p.bias_s;
-            // the activation is chosen once, outside the element loops, so
-            // those stay straight-line code
-            const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
-            float bv[8][4];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int n = n0 + wn * 128 + j * 16 + cq;
-                if (bg) {
-                    const u32x2 bb = *(const u32x2 *)(bg + n);
-                    bv[j][0] = bf16_lo(bb.x);
-                    bv[j][1] = bf16_hi(bb.x);
-                    bv[j][2] = bf16_lo(bb.y);
-                    bv[j][3] = bf16_hi(bb.y);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) bv[j][t] = 0.0f;
-                }
-            }
-            auto convert = [&](auto fn) __attribute__((always_inline)) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        float v[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
-                        put(i * 16 + l16, wn * 128 + j * 16 + cq, v);
-                    }
-            };
-            if (act == ACT_GELU)
-                convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
-            else if (act == ACT_SILU)
-                convert([](float z) __attribute__((always_inline)) { return silu_f(z); });
-            else
-                convert([](float z) __attribute__((always_inline)) { return z; });
-        }
-        __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        // 16-byte chunks per output row: 32 (256 columns) or 16 (gated)
-        const int cpr = gated ? 16 : 32;
-        const int rpp = 256 / cpr;                 // rows per block pass
-        const int rr = tid / cpr, cc = tid % cpr;
-        uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
-        for (int r0 = 0; r0 < BM; r0 += rpp) {
-            const int row = r0 + rr;
-            if (row < nrows) {
-                const char *sb = (const char *)(row < 128 ? slot0 : slot1);
-                const int rl = row & 127;
-                const u32x4 v = *(const u32x4 *)(sb + rl * 512 + ((cc ^ (rl & 15)) * 16));
-                *(u32x4 *)(out + (size_t)(row0 + row) * p.ldo) = v;
-            }
-        }
+        if (nrows <= 128)
+            w4_tile<UP, true>(p, slot0, slot1, g, row0, nrows, n0, routed,
+                              wave, lane, KT);
+        else
+            w4_tile<UP, false>(p, slot0, slot1, g, row0, nrows, n0, routed,
+                               wave, lane, KT);
     }
 }
 
