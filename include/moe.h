@@ -212,6 +212,13 @@ int32_t moe_capacity(int32_t T, int32_t E, double cf);
  * run a sequence of calls with one workspace. */
 size_t moe_workspace_size(const moe_desc *desc);
 
+/* Host.  The grouped-GEMM kernel variant moe_ffn_up (up != 0) or
+ * moe_ffn_down would run for this descriptor on the current device (an
+ * internal id, for diagnostics and benchmark reports), or a negative
+ * status if the descriptor is invalid.  Depends on the descriptor, the
+ * device's CU count and the MOE_GEMM_VARIANT_UP / _DOWN tuning variables. */
+int moe_gemm_variant(const moe_desc *desc, int up);
+
 /* Router GEMM with bias, softmax, top-k and renormalisation (layer steps
  * 1-2); bf16 layers run it as one kernel or, for deep or few-token shapes,
  * as partial logits over depth ranges (fp32, in the workspace) followed by

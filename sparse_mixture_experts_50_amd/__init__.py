@@ -7,7 +7,8 @@ binding: torch supplies device memory and streams only.
 from ._lib import MoeError, MoeDesc, MoeRouting, MoeWeights, lib  # noqa: F401
 from .layer import (MoeLayer, Routing, Weights, make_desc,  # noqa: F401
                     moe_bias_update, moe_capacity, moe_combine,
-                    moe_ffn_down, moe_ffn_up, moe_forward, moe_grouped_ffn,
-                    moe_permute, moe_router_topk, moe_workspace_size)
+                    moe_ffn_down, moe_ffn_up, moe_forward, moe_gemm_variant,
+                    moe_grouped_ffn, moe_permute, moe_router_topk,
+                    moe_workspace_size)
 
 __version__ = "0.1.0"

@@ -59,6 +59,7 @@ class MoeRouting(ctypes.Structure):
 SIGNATURES = {
     "moe_capacity": (c_i32, [c_i32, c_i32, ctypes.c_double]),
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MoeDesc)]),
+    "moe_gemm_variant": (ctypes.c_int, [ctypes.POINTER(MoeDesc), ctypes.c_int]),
     "moe_router_topk": (ctypes.c_int, [ctypes.POINTER(MoeDesc), c_vp,
                                        ctypes.POINTER(MoeWeights),
                                        ctypes.POINTER(MoeRouting), c_vp,

@@ -870,7 +870,10 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     }
 }
 
-template <bool UP>
+// TM_ROWS = 256: full tiles, a group's last <= 128 rows as a half tile;
+// TM_ROWS = 128: every tile half-height (twice the tiles, for GEMMs whose
+// 256-row tiles leave a partial last round).
+template <bool UP, int TM_ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     using namespace w4;
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
@@ -880,8 +883,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     const int KT = p.K / SK;
     const int NTN = p.N / BN;
     const int G = p.E + p.n_shared;
-    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM,
-                     NTN);
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
+                     TM_ROWS, NTN);
     const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
     const int nb = gridDim.x, per = nb >> 3;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
@@ -892,12 +895,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         const int local = L - __builtin_amdgcn_readfirstlane(tt.base[g]);
         const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
         const int n_tile = local / mt, m_tile = local - n_tile * mt;
-        const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) + m_tile * BM;
-        const int nrows = min(BM, __builtin_amdgcn_readfirstlane(tt.rows[g]) -
-                                      m_tile * BM);
+        const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) +
+                         m_tile * TM_ROWS;
+        const int nrows = min(TM_ROWS, __builtin_amdgcn_readfirstlane(tt.rows[g]) -
+                                           m_tile * TM_ROWS);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        if (nrows <= 128)
+        if (TM_ROWS == 128 || nrows <= 128)
             w4_tile<UP, true>(p, slot0, slot1, g, row0, nrows, n0, routed,
                               wave, lane, KT);
         else
@@ -1356,9 +1360,9 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool UP>
+template <bool UP, int TM_ROWS>
 hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(gemm_bf16_w4<UP>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1392,6 +1396,7 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA64_128x256: return {128, 256, 256, 2 * 384 * 128};
     case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
     case GEMM_BF16_W4_256x256: return {256, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
     default: return {64, 64, 256, 0};
     }
 }
@@ -1427,7 +1432,11 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
         return up ? launch_dma64<320, 256, 2, 4, true>(p, grid, s)
                   : launch_dma64<320, 256, 2, 4, false>(p, grid, s);
     case GEMM_BF16_W4_256x256:
-        return up ? launch_w4<true>(p, grid, s) : launch_w4<false>(p, grid, s);
+        return up ? launch_w4<true, 256>(p, grid, s)
+                  : launch_w4<false, 256>(p, grid, s);
+    case GEMM_BF16_W4_128x256:
+        return up ? launch_w4<true, 128>(p, grid, s)
+                  : launch_w4<false, 128>(p, grid, s);
 
     case GEMM_BF16_STREAM_32x64:
         if (up)

@@ -77,6 +77,7 @@ enum GemmVariant {
     GEMM_FP8_STREAM_64x64 = 12,
     GEMM_BF16_DMA64_320x256 = 13,  // 320-row tiles: one per ~257-320-row group
     GEMM_BF16_W4_256x256 = 14,     // four waves of 128 x 128, K % 128 == 0
+    GEMM_BF16_W4_128x256 = 15,     // the same kernel, every tile 128 x 256
 };
 
 // Variants that stream weights over persistent (group, column-slab) units.

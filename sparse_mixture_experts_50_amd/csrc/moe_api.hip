@@ -165,11 +165,13 @@ int variant_override(bool up, const moe_desc *d, int N) {
     const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
                         id == GEMM_FP8_STREAM_64x64;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4_256x256 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4_128x256 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
-    if (id == GEMM_BF16_W4_256x256 && !w4_fits(d, up)) return -1;
+    if ((id == GEMM_BF16_W4_256x256 || id == GEMM_BF16_W4_128x256) &&
+        !w4_fits(d, up))
+        return -1;
     // the streaming kernels split K in four quarters of whole load batches
     // (4 x 32 deep for 32-column units, 2 x 32 for 64-column ones)
     if (id == GEMM_BF16_STREAM_32x64 && (d->d % 512 != 0 || d->d_ff % 512 != 0))
@@ -179,49 +181,100 @@ int variant_override(bool up, const moe_desc *d, int N) {
     return id;
 }
 
-// Expected cost of a grouped GEMM with BM-row tiles: whole rounds of
-// tiles over the persistent grid, each round costing a tile's time, in
-// units of one tile row.  A tile streams its BN-column weight panel and
-// runs its prologue and epilogue whatever its height: worth about 128 rows
-// for the eight-wave kernels and 40 for the four-wave one (measured on the
-// Mixtral-shaped GEMMs).  Top-k group sizes get 10 % headroom for routing
-// skew (at most the capacity); expert-choice groups hold exactly C rows.
-double tile_cost(const moe_desc *d, int N, int bm, int slots, double over) {
-    double avg = (double)routed_rows(d) / d->E;
-    if (!expert_choice(d)) {
-        avg *= 1.1;
-        if (d->capacity >= 0 && avg > d->capacity) avg = d->capacity;
+// Expected row tiles of one routed group: E[ceil(X / bm)] with the group
+// size X ~ Normal(avg, avg (1 - 1/E)) (a binomial share of the T k
+// assignments), i.e. the sum over j of P(X > j bm); capped at the capacity.
+// Expert-choice groups hold exactly C rows.  full / half: the same split
+// for a kernel whose last <= 128 rows of a group take a half tile.
+struct TileCount {
+    double tiles, full, half;
+};
+TileCount group_tiles(const moe_desc *d, int bm) {
+    const double avg = (double)routed_rows(d) / d->E;
+    TileCount c = {0.0, 0.0, 0.0};
+    if (expert_choice(d) || avg <= 0.0) {
+        c.tiles = ceil(avg / bm);
+        c.full = floor(avg / bm);
+        c.half = (avg - c.full * bm) > 0 ? 1.0 : 0.0;
+        if (avg - c.full * bm > 128) {
+            c.full += 1.0;
+            c.half = 0.0;
+        }
+        return c;
     }
-    const double mt = ceil(avg / bm) * d->E +
-                      (double)d->n_shared * ceil((double)d->T / bm);
-    const double tiles = mt * (N / 256);
-    return ceil(tiles / slots) * (bm + over);
+    const double sd = sqrt(avg * (1.0 - 1.0 / d->E));
+    const double cap = d->capacity >= 0 ? (double)d->capacity : 1e30;
+    auto above = [&](double x) {      // P(X > x), 0 at or above the cap
+        if (x >= cap) return 0.0;
+        return 0.5 * erfc((x - avg) / (sd * sqrt(2.0)));
+    };
+    for (int j = 0; j * (double)bm < avg + 8.0 * sd + bm && j < 1 << 20; ++j) {
+        const double pj = above(j * (double)bm);
+        c.tiles += pj;
+        // the tile starting at j bm is half height when the group ends
+        // within its first 128 rows
+        const double ph = pj - above(j * (double)bm + 128.0);
+        c.half += ph;
+        c.full += pj - ph;
+    }
+    return c;
 }
 
+// Expected cost of a grouped GEMM: whole rounds of tiles over the
+// persistent grid, each round costing a tile's time, in units of one tile
+// row.  A tile streams its 256-column weight panel and runs its prologue
+// and epilogue whatever its height: worth about 128 rows for the
+// eight-wave kernels and 40 for the four-wave one (measured on the
+// Mixtral-shaped GEMMs), whose half-height tiles cost about 0.65 of a full
+// one.
+double tile_cost(const moe_desc *d, int N, int bm, int slots, double over,
+                 bool halves) {
+    const TileCount g = group_tiles(d, bm);
+    const double shared = (double)d->n_shared * ceil((double)d->T / bm);
+    const double per_group = halves ? g.full + 0.65 * g.half : g.tiles;
+    const double tiles = (per_group * d->E + shared) * (N / 256);
+    // an expected few percent of a round past a whole number (a rare
+    // group just over a tile boundary) is not charged a whole round
+    return ceil(tiles / slots - 0.05) * (bm + over);
+}
+
+// Variant choice, from sweeps of group size, depth and width on MI355X:
+// streaming up to 32 rows per expert; 32-row tiles to 48; the four-wave
+// kernel with 128-row tiles to 128 (one or two half tiles per group; the
+// eight-wave 256-row kernel where K does not suit it); the eight-wave
+// 256-row kernel to 192; above that the cheapest of 256- and 320-row
+// eight-wave tiles and the four-wave 256-row kernel.  The last only for
+// K >= 2048 (shallower GEMMs are dominated by its one-wave-per-SIMD
+// epilogue) and groups of >= 768 rows: then the row tiles of one expert
+// run side by side and share each weight panel through L2; with one or
+// two tiles per expert (DeepSeek-shaped layers, multi-GB expert weights)
+// the tiles stream distinct weights and the taller 320-row tile, with more
+// FLOPs per weight byte, is faster.
 int pick_variant(const moe_desc *d, int N, bool up) {
     if (d->dtype == MOE_F32) return GEMM_F32_64x64;
     if (d->expert_fp8) return GEMM_FP8_STREAM_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
     const double avg = (double)routed_rows(d) / d->E;
+    const int K = up ? d->d : d->d_ff;
     // the streaming kernel splits K in four quarters of whole 64-deep
     // load batches; 64-column units re-read the token rows half as often
     // as 32-column ones
     if (avg <= 32.0 && d->d % 256 == 0 && d->d_ff % 256 == 0)
         return GEMM_BF16_STREAM_64x64;
     if (avg <= 48.0) return GEMM_BF16_32x256;
-    if (avg <= 192.0) return GEMM_BF16_DMA64_128x256;
-    // 256- or 320-row tiles: 320 covers a ~257..320-row group in one tile
-    // and can turn a partial last round into a full one; the four-wave
-    // 256-row kernel has the cheapest tile where K allows it
+    if (avg <= 128.0)
+        return w4_fits(d, up) ? GEMM_BF16_W4_128x256 : GEMM_BF16_DMA64_256x256;
+    if (avg <= 192.0) return GEMM_BF16_DMA64_256x256;
     const int slots = device_cus();
     int best = GEMM_BF16_DMA64_256x256;
-    double cost = tile_cost(d, N, 256, slots, 128.0);
-    const double c320 = tile_cost(d, N, 320, slots, 128.0);
+    double cost = tile_cost(d, N, 256, slots, 128.0, false);
+    const double c320 = tile_cost(d, N, 320, slots, 128.0, false);
     if (c320 < cost) {
         best = GEMM_BF16_DMA64_320x256;
         cost = c320;
     }
-    if (w4_fits(d, up) && tile_cost(d, N, 256, slots, 40.0) < cost)
+    if (w4_fits(d, up) && K >= 2048 && avg >= 768.0 &&
+        tile_cost(d, N, 256, slots, 40.0, true) < cost)
         best = GEMM_BF16_W4_256x256;
     return best;
 }
@@ -364,6 +417,17 @@ int32_t moe_capacity(int32_t T, int32_t E, double cf) {
     const double c = floor(((double)T / (double)E) * cf);
     if (c > 2147483647.0) return 2147483647;
     return (int32_t)c;
+}
+
+int moe_gemm_variant(const moe_desc *desc, int up) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const int N = up ? (desc->activation == MOE_ACT_SWIGLU ? 2 * desc->d_ff
+                                                           : desc->d_ff)
+                     : desc->d;
+    int v = variant_override(up != 0, desc, N);
+    if (v < 0) v = pick_variant(desc, N, up != 0);
+    return v;
 }
 
 size_t moe_workspace_size(const moe_desc *desc) {

@@ -90,6 +90,14 @@ def moe_workspace_size(desc: MoeDesc) -> int:
     return n
 
 
+def moe_gemm_variant(desc: MoeDesc, up: bool) -> int:
+    """Internal id of the grouped-GEMM kernel the up (or down) projection
+    runs for this descriptor (diagnostics, benchmark reports)."""
+    v = _lib.lib().moe_gemm_variant(ctypes.byref(desc), 1 if up else 0)
+    check("moe_gemm_variant", min(v, 0))
+    return v
+
+
 def _codes(t):
     """float8_e4m3fn tensors are passed as their uint8 codes."""
     if t is not None and t.dtype == torch.float8_e4m3fn:

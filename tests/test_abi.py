@@ -236,3 +236,55 @@ def test_binding_checks_tensor_shapes():
     with pytest.raises(ValueError):
         moe.Weights(wr, w1, w2, b_router=torch.zeros(2,
                                                      dtype=torch.bfloat16))
+
+
+def _desc_of(w):
+    import torch
+    cap = (moe.moe_capacity(w.T, w.E, w.capacity_factor)
+           if w.capacity_factor is not None else -1)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, dt, n_shared=w.n_shared,
+                         capacity=cap, routing=w.routing,
+                         expert_fp8=w.expert_fp8,
+                         activation=w.activation or "gelu")
+
+
+# (up, down) grouped-GEMM kernel ids the host picks on a 256-CU device
+# (host side only: no GPU needed).  4: fp32 SIMT; 8 / 13: eight-wave
+# 256- / 320-row tiles; 11 / 12: bf16 / FP8 weight streaming; 14: four-wave
+# 256-row tiles with half-height tails; 15: four-wave 128-row tiles.
+PICKS = {
+    "tiny_top2_f32": (4, 4),
+    "switch_top1_cap": (15, 15),
+    "mixtral_prefill": (14, 14),
+    "mixtral_decode": (11, 11),
+    "deepseek_v3": (13, 13),
+    "mixtral_decode_fp8": (12, 12),
+    "mixtral_prefill_swiglu": (14, 14),
+    "mixtral_decode_swiglu": (11, 11),
+    "expert_choice_c2": (8, 8),
+}
+
+
+@pytest.mark.parametrize("name", list(PICKS))
+def test_gemm_variant_choice(name, monkeypatch):
+    import workloads
+    monkeypatch.delenv("MOE_GEMM_VARIANT_UP", raising=False)
+    monkeypatch.delenv("MOE_GEMM_VARIANT_DOWN", raising=False)
+    d = _desc_of(workloads.WORKLOADS[name])
+    assert (moe.moe_gemm_variant(d, True),
+            moe.moe_gemm_variant(d, False)) == PICKS[name]
+
+
+def test_gemm_variant_override_is_validated(monkeypatch):
+    import workloads
+    d = _desc_of(workloads.WORKLOADS["mixtral_prefill"])
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "15")
+    assert moe.moe_gemm_variant(d, True) == 15
+    # the four-wave kernels need K % 128 == 0: refused, back to the pick
+    import dataclasses
+    w = dataclasses.replace(workloads.WORKLOADS["mixtral_prefill"], d=4096 + 64)
+    assert moe.moe_gemm_variant(_desc_of(w), True) != 15
+    # an id out of range is ignored
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "99")
+    assert moe.moe_gemm_variant(d, True) == 14
