@@ -269,6 +269,9 @@ def main():
             wl.d, dev)
     roof["traffic"] = recorded_traffic(wl.name)
     roof["kernel"] = "grouped GEMM up (moe_ffn_up)"
+    # the library's kernel variant ids of the up and down GEMMs
+    roof["gemm_variants"] = [moe.moe_gemm_variant(desc, True),
+                             moe.moe_gemm_variant(desc, False)]
     roof["kernel_ms"] = up_avg_ms
 
     cpu = None

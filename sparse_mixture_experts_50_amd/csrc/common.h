@@ -95,9 +95,11 @@ struct TileTable {
 };
 
 // Build the table in LDS with the whole block; ends with __syncthreads().
-__device__ __forceinline__ void build_tile_table(
+// mt_of(rows): the group's row tiles (ceil(rows / BM) for plain tiles).
+template <typename F>
+__device__ __forceinline__ void build_tile_table_by(
     TileTable &tt, const int32_t *__restrict__ offsets, int E, int n_shared,
-    int shared_base, int T, int BM, int n_tiles_n) {
+    int shared_base, int T, int n_tiles_n, F mt_of) {
     const int G = E + n_shared;
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
         int st, rw;
@@ -108,7 +110,7 @@ __device__ __forceinline__ void build_tile_table(
             st = shared_base;
             rw = T;
         }
-        int mt = (rw + BM - 1) / BM;
+        const int mt = mt_of(rw);
         tt.start[g] = st;
         tt.rows[g] = rw;
         tt.mt[g] = mt;
@@ -137,6 +139,13 @@ __device__ __forceinline__ void build_tile_table(
         if (lane == 63) tt.base[G] = incl;
     }
     __syncthreads();
+}
+
+__device__ __forceinline__ void build_tile_table(
+    TileTable &tt, const int32_t *__restrict__ offsets, int E, int n_shared,
+    int shared_base, int T, int BM, int n_tiles_n) {
+    build_tile_table_by(tt, offsets, E, n_shared, shared_base, T, n_tiles_n,
+                        [BM](int rows) { return (rows + BM - 1) / BM; });
 }
 
 // Largest g with base[g] <= L (base[G] > L assumed).

@@ -870,34 +870,84 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     }
 }
 
-// TM_ROWS = 256: full tiles, a group's last <= 128 rows as a half tile;
-// TM_ROWS = 128: every tile half-height (twice the tiles, for GEMMs whose
-// 256-row tiles leave a partial last round).
+// TM_ROWS = 256: full tiles, a group's last <= 128 rows as a half tile.
+// With four or more rounds of tiles, the full tiles of every group come
+// first and the half tiles after them: the 4-5 row tiles of one (expert,
+// column) panel then run side by side at one pace and share the panel's
+// k-slices through L2 (a half tile among them finishes early and breaks
+// that: the Mixtral up GEMM fetched 3.3 GB instead of 2.1), and the cheaper
+// half tiles fill the end of the schedule.  With fewer rounds the tiles
+// stay in group order, where the half tiles spread over the last round
+// (the Mixtral down GEMM's 2.25 rounds: 5 % faster that way).
+// TM_ROWS = 128: every tile half-height (for groups of up to ~128 rows).
 template <bool UP, int TM_ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     using namespace w4;
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
-    __shared__ TileTable tt;
+    __shared__ TileTable tf, th;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KT = p.K / SK;
     const int NTN = p.N / BN;
     const int G = p.E + p.n_shared;
-    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
-                     TM_ROWS, NTN);
-    const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
+    if (TM_ROWS == 128) {
+        build_tile_table(tf, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
+                         128, NTN);
+    } else {
+        // full-height tiles: whole 256-row blocks and a last block of more
+        // than 128 rows; half tiles: a last block of 1..128 rows
+        build_tile_table_by(tf, p.offsets, p.E, p.n_shared, p.shared_base,
+                            p.T, NTN, [](int rows) {
+                                return (rows >> 8) + ((rows & 255) > 128);
+                            });
+        build_tile_table_by(th, p.offsets, p.E, p.n_shared, p.shared_base,
+                            p.T, NTN, [](int rows) {
+                                const int rem = rows & 255;
+                                return rem > 0 && rem <= 128 ? 1 : 0;
+                            });
+    }
+    const int total_f = __builtin_amdgcn_readfirstlane(tf.base[G]);
+    const int total = total_f + (TM_ROWS == 128
+                                     ? 0
+                                     : __builtin_amdgcn_readfirstlane(th.base[G]));
     const int nb = gridDim.x, per = nb >> 3;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const bool halves_last = TM_ROWS == 256 && total >= 4 * nb;
     for (int r = 0;; ++r) {
         const int L = r * nb + xcd * per + loc;
         if (L >= total) break;
-        const int g = __builtin_amdgcn_readfirstlane(find_group(tt, G, L));
-        const int local = L - __builtin_amdgcn_readfirstlane(tt.base[g]);
-        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
-        const int n_tile = local / mt, m_tile = local - n_tile * mt;
-        const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) +
+        int g, n_tile, m_tile;
+        if (!halves_last) {
+            // group order: the group's tiles n-tile major, m-tile minor,
+            // the half tile (if any) last of each column
+            g = 0;
+            int lo = 0, hi = G;
+            while (hi - lo > 1) {     // largest g with tile base <= L
+                const int mid = (lo + hi) >> 1;
+                if (tf.base[mid] + (TM_ROWS == 256 ? th.base[mid] : 0) <= L) lo = mid;
+                else hi = mid;
+            }
+            g = __builtin_amdgcn_readfirstlane(lo);
+            const int base = tf.base[g] + (TM_ROWS == 256 ? th.base[g] : 0);
+            const int mt = tf.mt[g] + (TM_ROWS == 256 ? th.mt[g] : 0);
+            const int local = __builtin_amdgcn_readfirstlane(L - base);
+            n_tile = local / mt;
+            m_tile = local - n_tile * mt;
+        } else {
+            const bool first = L < total_f;
+            const TileTable &tt = first ? tf : th;
+            const int Lg = first ? L : L - total_f;
+            g = __builtin_amdgcn_readfirstlane(find_group(tt, G, Lg));
+            const int local = Lg - __builtin_amdgcn_readfirstlane(tt.base[g]);
+            const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
+            n_tile = local / mt;
+            // a half tile follows the group's full tiles
+            m_tile = first ? local - n_tile * mt
+                           : __builtin_amdgcn_readfirstlane(tf.mt[g]);
+        }
+        const int row0 = __builtin_amdgcn_readfirstlane(tf.start[g]) +
                          m_tile * TM_ROWS;
-        const int nrows = min(TM_ROWS, __builtin_amdgcn_readfirstlane(tt.rows[g]) -
+        const int nrows = min(TM_ROWS, __builtin_amdgcn_readfirstlane(tf.rows[g]) -
                                            m_tile * TM_ROWS);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
