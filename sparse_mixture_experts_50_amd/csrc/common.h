@@ -182,6 +182,13 @@ struct GemmParams {
     int act;                  // up epilogue: ACT_GELU, ACT_SILU, ACT_SWIGLU
     int gated;                // 1 for the SwiGLU up GEMM
     int ldo;                  // output row stride (elements)
+    // Four-wave 256-row kernel, tail_split > 1: each half-height tile (a
+    // group's last 1..128 rows) runs as tail_split units over consecutive
+    // ranges of K, writing fp32 partial sums to part, laid out
+    // [tail_split][E + n_shared][128][N] (rows of the group's tail); the
+    // tail reduction adds them in order and finishes the rows.
+    float *part;
+    int tail_split;
 };
 
 enum { ACT_GELU = 0, ACT_SILU = 1, ACT_SWIGLU = 2 };

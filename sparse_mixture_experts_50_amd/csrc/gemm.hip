@@ -630,11 +630,14 @@ __device__ __forceinline__ void mfma_agpr(floatx4 &acc, const bf16x8 &a,
 // with the next sub-step's fragment reads spread over the first three
 // quarters (full) or half (half), and in a stage's second sub-step the
 // loads of the stage after next spread over the MFMAs.
-template <bool UP, bool HALF>
+// PART: write the fp32 sums over stages kt0 .. kt0 + KT - 1 to the tail
+// partial buffer (plane ks) instead of finishing the tile.
+template <bool UP, bool HALF, bool PART>
 __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                                         u32x4 *slot1, int g, int row0,
                                         int nrows, int n0, bool routed,
-                                        int wave, int lane, int KT) {
+                                        int wave, int lane, int kt0, int KT,
+                                        int ks) {
     using namespace w4;
     constexpr int TN = HALF ? 4 : 8;          // 16-column blocks per wave
     constexpr int WC = HALF ? 64 : 128;       // columns per wave
@@ -676,9 +679,9 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     for (int j = 0; j < LPW; ++j)
         bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
 
-    // load q (q < LA: A rows, else B rows) of stage ks into a slot
-    auto dma_one = [&](int ks, u32x4 *st, int q) __attribute__((always_inline)) {
-        const size_t ko = (size_t)ks * SK * 2;
+    // load q (q < LA: A rows, else B rows) of stage kt0 + kl into a slot
+    auto dma_one = [&](int kl, u32x4 *st, int q) __attribute__((always_inline)) {
+        const size_t ko = (size_t)(kt0 + kl) * SK * 2;
         if (q < LA)
             dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
         else
@@ -751,6 +754,25 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         stage(s, slot0, slot1);
         stage(s + 1, slot1, slot0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    }
+
+    if (PART) {
+        // fp32 partial sums of this K range, rows of the group's tail
+        const int G = p.E + p.n_shared;
+        float *dst = p.part + ((size_t)ks * G + g) * 128 * N;
+        __builtin_amdgcn_s_waitcnt(0);   // re-loads landed before the next tile
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = i * 16 + l16;
+            if (r >= nrows) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int c = n0 + wn * WC + j * 16 + 4 * (lane >> 4);
+                *(float4 *)(dst + (size_t)r * N + c) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        }
+        return;
     }
 
     // Epilogue through LDS.  A wave's MFMA layout gives each lane 4
@@ -906,17 +928,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
                                 return rem > 0 && rem <= 128 ? 1 : 0;
                             });
     }
+    // S > 1: the half tiles run as S units each over a 1/S range of K
+    const int S = TM_ROWS == 256 && p.tail_split > 1 ? p.tail_split : 1;
     const int total_f = __builtin_amdgcn_readfirstlane(tf.base[G]);
     const int total = total_f + (TM_ROWS == 128
                                      ? 0
-                                     : __builtin_amdgcn_readfirstlane(th.base[G]));
+                                     : S * __builtin_amdgcn_readfirstlane(th.base[G]));
     const int nb = gridDim.x, per = nb >> 3;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    const bool halves_last = TM_ROWS == 256 && total >= 4 * nb;
+    const bool halves_last = TM_ROWS == 256 && (S > 1 || total >= 4 * nb);
     for (int r = 0;; ++r) {
         const int L = r * nb + xcd * per + loc;
         if (L >= total) break;
-        int g, n_tile, m_tile;
+        int g, n_tile, m_tile, ks = 0;
         if (!halves_last) {
             // group order: the group's tiles n-tile major, m-tile minor,
             // the half tile (if any) last of each column
@@ -936,7 +960,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         } else {
             const bool first = L < total_f;
             const TileTable &tt = first ? tf : th;
-            const int Lg = first ? L : L - total_f;
+            int Lg = first ? L : L - total_f;
+            if (!first) {             // unit ks of half tile Lg / S
+                ks = Lg % S;
+                Lg /= S;
+            }
             g = __builtin_amdgcn_readfirstlane(find_group(tt, G, Lg));
             const int local = Lg - __builtin_amdgcn_readfirstlane(tt.base[g]);
             const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
@@ -951,12 +979,76 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
                                            m_tile * TM_ROWS);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
-        if (TM_ROWS == 128 || nrows <= 128)
-            w4_tile<UP, true>(p, slot0, slot1, g, row0, nrows, n0, routed,
-                              wave, lane, KT);
+        if (S > 1 && L >= total_f)
+            w4_tile<UP, true, true>(p, slot0, slot1, g, row0, nrows, n0,
+                                    routed, wave, lane, ks * (KT / S), KT / S,
+                                    ks);
+        else if (TM_ROWS == 128 || nrows <= 128)
+            w4_tile<UP, true, false>(p, slot0, slot1, g, row0, nrows, n0,
+                                     routed, wave, lane, 0, KT, 0);
         else
-            w4_tile<UP, false>(p, slot0, slot1, g, row0, nrows, n0, routed,
-                               wave, lane, KT);
+            w4_tile<UP, false, false>(p, slot0, slot1, g, row0, nrows, n0,
+                                      routed, wave, lane, 0, KT, 0);
+    }
+}
+
+// Finishing the split tails: for each group whose last 1..128 rows ran as
+// split units, out[row] = epilogue(sum over ks in order of the fp32 partial
+// rows + bias), 8 outputs per thread and step.  Block (group, 128-column
+// chunk of the output).  Gated: output feature f pairs virtual columns
+// 64 (f / 32) + f % 32 (gate) and that + 32 (up).
+template <bool UP>
+__global__ __launch_bounds__(256) void w4_tail_reduce(GemmParams p) {
+    const int G = p.E + p.n_shared;
+    const bool gated = UP && p.gated;
+    const int N = p.N;
+    const int OC = gated ? N >> 1 : N;
+    const int nch = OC / 128;
+    const int g = blockIdx.x / nch, c0 = (blockIdx.x - g * nch) * 128;
+    const bool routed = g < p.E;
+    const int st = routed ? p.offsets[g] : p.shared_base;
+    const int rw = routed ? p.offsets[g + 1] - st : p.T;
+    const int rem = rw & 255;
+    if (rem == 0 || rem > 128) return;
+    const int S = p.tail_split;
+    const size_t plane = (size_t)G * 128 * N;
+    const float *part = p.part + (size_t)g * 128 * N;
+    const int Fb = gated ? N >> 1 : N;         // bias row length
+    const uint16_t *b1 = routed
+        ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * Fb : nullptr)
+        : (const uint16_t *)p.bias_s;
+    const uint16_t *b3 = !gated ? nullptr
+        : routed ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * Fb : nullptr)
+                 : (const uint16_t *)p.bias_s3;
+    uint16_t *out = (uint16_t *)p.out;
+    for (int i = threadIdx.x; i < rem * 16; i += blockDim.x) {
+        const int r = i >> 4, c = c0 + (i & 15) * 8;
+        const float *src = part + (size_t)r * N;
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int f = c + t;
+            if (gated) {
+                const int cg = 64 * (f >> 5) + (f & 31);
+                float gv = src[cg], uv = src[cg + 32];
+                for (int k = 1; k < S; ++k) {
+                    gv += src[k * plane + cg];
+                    uv += src[k * plane + cg + 32];
+                }
+                if (b1) gv += bf16_to_f32(b1[f]);
+                if (b3) uv += bf16_to_f32(b3[f]);
+                v[t] = silu_f(gv) * uv;
+            } else {
+                float s = src[f];
+                for (int k = 1; k < S; ++k) s += src[k * plane + f];
+                if (b1) s += bf16_to_f32(b1[f]);
+                v[t] = UP ? act_up(p.act, s) : s;
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
+        *(u32x4 *)(out + (size_t)(st + rw - rem + r) * p.ldo + c) = o;
     }
 }
 
@@ -1413,6 +1505,12 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
 template <bool UP, int TM_ROWS>
 hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
+    if (TM_ROWS == 256 && p.tail_split > 1) {
+        const int G = p.E + p.n_shared;
+        const int oc = UP && p.gated ? p.N / 2 : p.N;
+        hipLaunchKernelGGL(w4_tail_reduce<UP>, dim3(G * (oc / 128)), dim3(256),
+                           0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t p_part, zh_part, blk, scores, rpart, h, yp, total;
+    size_t p_part, zh_part, blk, scores, rpart, tpart, h, yp, total;
     int n_rtiles, n_chunks;
     size_t rows;
 };
@@ -69,6 +69,84 @@ int check_desc(const moe_desc *d) {
     return MOE_OK;
 }
 
+// Expected row tiles of one routed group: E[ceil(X / bm)] with the group
+// size X ~ Normal(avg, avg (1 - 1/E)) (a binomial share of the T k
+// assignments), i.e. the sum over j of P(X > j bm); capped at the capacity.
+// Expert-choice groups hold exactly C rows.  full / half: the same split
+// for a kernel whose last <= 128 rows of a group take a half tile.
+struct TileCount {
+    double tiles, full, half;
+};
+TileCount group_tiles(const moe_desc *d, int bm) {
+    const double avg = (double)routed_rows(d) / d->E;
+    TileCount c = {0.0, 0.0, 0.0};
+    if (expert_choice(d) || avg <= 0.0) {
+        c.tiles = ceil(avg / bm);
+        c.full = floor(avg / bm);
+        c.half = (avg - c.full * bm) > 0 ? 1.0 : 0.0;
+        if (avg - c.full * bm > 128) {
+            c.full += 1.0;
+            c.half = 0.0;
+        }
+        return c;
+    }
+    const double sd = sqrt(avg * (1.0 - 1.0 / d->E));
+    const double cap = d->capacity >= 0 ? (double)d->capacity : 1e30;
+    auto above = [&](double x) {      // P(X > x), 0 at or above the cap
+        if (x >= cap) return 0.0;
+        return 0.5 * erfc((x - avg) / (sd * sqrt(2.0)));
+    };
+    for (int j = 0; j * (double)bm < avg + 8.0 * sd + bm && j < 1 << 20; ++j) {
+        const double pj = above(j * (double)bm);
+        c.tiles += pj;
+        // the tile starting at j bm is half height when the group ends
+        // within its first 128 rows
+        const double ph = pj - above(j * (double)bm + 128.0);
+        c.half += ph;
+        c.full += pj - ph;
+    }
+    return c;
+}
+
+// How many K ranges the four-wave 256-row kernel splits each half-height
+// tile into (1: none).  When the full tiles fill whole rounds and the half
+// tiles would run as a sparse extra round (the Mixtral down GEMM: 512 full
+// tiles, two rounds of the 256 CUs, then 64 half tiles), each half tile
+// runs as S units over 1/S of K so that the last round fills the CUs; the
+// units' fp32 partials are added by the tail reduction.  A function of the
+// shape only (sized for 256 CUs), so the workspace size is too.
+int tail_split(const moe_desc *d, bool up) {
+    if (d->dtype != MOE_BF16 || d->expert_fp8) return 1;
+    const int N = up ? (d->activation == MOE_ACT_SWIGLU ? 2 * d->d_ff : d->d_ff)
+                     : d->d;
+    const int K = up ? d->d : d->d_ff;
+    if (N % 256 != 0 || K % 128 != 0 || K < 256) return 1;
+    const TileCount g = group_tiles(d, 256);
+    const int rem = d->T & 255;
+    const double shared_half = (double)d->n_shared * (rem > 0 && rem <= 128);
+    const double H = (g.half * d->E + shared_half) * (N / 256);
+    if (H < 1.0) return 1;
+    int S = (int)floor(256.0 / H);
+    if (S > 8) S = 8;
+    while (S > 1 && (K / 64) % (2 * S) != 0) --S;   // whole stage pairs
+    if (S > 1 && (double)S * (d->E + d->n_shared) * 128.0 * N * 4.0 > 512e6)
+        S = 1;
+    // tuning and test knob: MOE_TAIL_SPLIT=1..8 caps the split (1: none);
+    // read here, so the workspace size follows it
+    const char *v = getenv("MOE_TAIL_SPLIT");
+    if (v && v[0] >= '1' && v[0] <= '8' && v[1] == 0 && S > v[0] - '0')
+        S = v[0] - '0';
+    return S;
+}
+
+size_t tail_part_bytes(const moe_desc *d, bool up) {
+    const int S = tail_split(d, up);
+    if (S < 2) return 0;
+    const int N = up ? (d->activation == MOE_ACT_SWIGLU ? 2 * d->d_ff : d->d_ff)
+                     : d->d;
+    return (size_t)S * (d->E + d->n_shared) * 128 * N * sizeof(float);
+}
+
 // The router's logits split depends on the shape only (sized for the
 // MI355X's 256 CUs), so the workspace size is a pure function of the
 // descriptor.
@@ -103,6 +181,11 @@ WsLayout layout(const moe_desc *d) {
     L.rpart = off;        // bf16 router: partial logits, [S][T][E] fp32
     if (d->dtype == MOE_BF16 && plan(d).split)
         off += align_up((size_t)plan(d).S * d->T * d->E * sizeof(float));
+    L.tpart = off;        // split tails of the four-wave GEMM: fp32 partials
+    {
+        const size_t a = tail_part_bytes(d, true), b = tail_part_bytes(d, false);
+        off += align_up(a > b ? a : b);
+    }
     L.h = off;
     off += align_up(L.rows * d->d_ff * es);
     L.yp = off;
@@ -179,45 +262,6 @@ int variant_override(bool up, const moe_desc *d, int N) {
     if (id == GEMM_BF16_STREAM_64x64 && (d->d % 256 != 0 || d->d_ff % 256 != 0))
         return -1;
     return id;
-}
-
-// Expected row tiles of one routed group: E[ceil(X / bm)] with the group
-// size X ~ Normal(avg, avg (1 - 1/E)) (a binomial share of the T k
-// assignments), i.e. the sum over j of P(X > j bm); capped at the capacity.
-// Expert-choice groups hold exactly C rows.  full / half: the same split
-// for a kernel whose last <= 128 rows of a group take a half tile.
-struct TileCount {
-    double tiles, full, half;
-};
-TileCount group_tiles(const moe_desc *d, int bm) {
-    const double avg = (double)routed_rows(d) / d->E;
-    TileCount c = {0.0, 0.0, 0.0};
-    if (expert_choice(d) || avg <= 0.0) {
-        c.tiles = ceil(avg / bm);
-        c.full = floor(avg / bm);
-        c.half = (avg - c.full * bm) > 0 ? 1.0 : 0.0;
-        if (avg - c.full * bm > 128) {
-            c.full += 1.0;
-            c.half = 0.0;
-        }
-        return c;
-    }
-    const double sd = sqrt(avg * (1.0 - 1.0 / d->E));
-    const double cap = d->capacity >= 0 ? (double)d->capacity : 1e30;
-    auto above = [&](double x) {      // P(X > x), 0 at or above the cap
-        if (x >= cap) return 0.0;
-        return 0.5 * erfc((x - avg) / (sd * sqrt(2.0)));
-    };
-    for (int j = 0; j * (double)bm < avg + 8.0 * sd + bm && j < 1 << 20; ++j) {
-        const double pj = above(j * (double)bm);
-        c.tiles += pj;
-        // the tile starting at j bm is half height when the group ends
-        // within its first 128 rows
-        const double ph = pj - above(j * (double)bm + 128.0);
-        c.half += ph;
-        c.full += pj - ph;
-    }
-    return c;
 }
 
 // Expected cost of a grouped GEMM: whole rounds of tiles over the
@@ -404,6 +448,12 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
     // never lands on a variant that cannot pair gate and up columns
     if (gated_up(d, up) && !gate_capable(variant)) return MOE_ERR_UNSUPPORTED;
     const int grid = gemm_grid(d, variant, p.N);
+    if (variant == GEMM_BF16_W4_256x256) {
+        GemmParams q = p;
+        q.tail_split = tail_split(d, up);
+        if (q.tail_split > 1) q.part = (float *)at(ws, layout(d).tpart);
+        return to_status(launch_gemm(q, variant, up, grid, s));
+    }
     return to_status(launch_gemm(p, variant, up, grid, s));
 }
 
