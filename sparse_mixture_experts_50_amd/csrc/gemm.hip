@@ -1360,6 +1360,333 @@ __global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------------
+// Weight-ring kernel for groups of at most 16 rows (decode).  HBM delivers
+// the most when each row of a weight panel is read in runs of a few KB
+// requested together, which the MFMA operand layout cannot give when
+// loading straight into registers (one load instruction covers 64 bytes of
+// each of 16 rows).  Here the weights pass through LDS instead: a stage is
+// 16 weight rows x CB bytes, fetched with non-temporal direct-to-LDS loads
+// in whole 1 KB runs per wave instruction, into a ring of four stages
+// (three in flight).  A unit is (group, 16-row chunk of the group, 64
+// output columns = four groups of 16 weight rows; gated: 32 features, their
+// gate rows then their up rows) over the whole of K, walked k range by k
+// range and, inside each, row group by row group; the token rows of a k
+// range are loaded into registers once, with its first stage, and serve
+// its four stages.  The ring runs on across the units of a block, so
+// nothing drains between units; every step issues a fixed set of loads
+// (past the last stage they re-read one line), so the waits are fixed
+// counts.  The four waves split each stage's k range in quarters; a unit's
+// partial sums are added through LDS (the slot its last stage leaves) in a
+// fixed order.  Each LDS row of a stage is padded by one 16-byte chunk, so
+// that the fragment reads (16 rows, one chunk) fall in distinct bank groups
+// while every sub-step's read is at a fixed offset from one address.
+namespace ring {
+constexpr int MAXTOK = MOE_RING_MAXTOK;
+
+__device__ __forceinline__ void dma16nt(const char *src, u32x4 *lds) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src, (__attribute__((address_space(3))) void *)lds, 16,
+        0, 2 /* non-temporal */);
+}
+
+__device__ __forceinline__ void dma4(const char *src, u32x4 *lds) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src, (__attribute__((address_space(3))) void *)lds, 4,
+        0, 0);
+}
+}  // namespace ring
+
+template <bool UP, bool FP8, int CB>
+__global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
+    constexpr int CPR = CB / 16;          // 16-byte chunks of a row per stage
+    constexpr int RS = CPR + 1;           // LDS row stride (chunks)
+    constexpr int CPS = 16 * RS;          // chunks per stage
+    constexpr int EPI = 32;               // epilogue chunks per wave and slot
+    constexpr int NI = CB / 256;          // 1 KB weight loads per wave
+    constexpr int SS = CB / 256;          // sub-steps per wave per stage
+    constexpr int NA = FP8 ? 2 * SS : SS; // token-row loads per k range
+    constexpr int PW = 2 + NI;            // loads of a stage (constants, weights)
+    constexpr int PA = PW + NA;           // ... of the first stage of a k range
+    constexpr int esz = FP8 ? 1 : 2;
+    static_assert(PW + PA < 64, "vmcnt range");
+    static_assert(CPS * 16 >= 4 * 4 * 16 * 16 * 4, "reduction fits a stage");
+    // A slot: the stage, then each wave's copy of the unit's epilogue
+    // constants, 128 dwords: 0-31 the bf16 biases of the 64 columns (gated:
+    // 0-15 the 32 gate biases, 32-47 the 32 up biases), 64-127 the FP8
+    // scales (gated: 64-95 gate, 96-127 up).
+    __shared__ u32x4 sl0[CPS + 4 * EPI], sl1[CPS + 4 * EPI],
+        sl2[CPS + 4 * EPI], sl3[CPS + 4 * EPI];
+    __shared__ int stok[ring::MAXTOK];
+    __shared__ TileTable tt;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q = lane >> 4;
+    const int G = p.E + p.n_shared;
+    const bool gated = UP && p.gated;
+    const int KC = p.K * esz / CB;        // k ranges
+    const int SPU = 4 * KC;               // stages per unit
+    const int NS = p.N / 64;              // 64-column slabs
+    if (UP) {
+        const int ns = p.offsets[p.E];
+        for (int i = tid; i < ns; i += 256) stok[i] = p.slot_token[i];
+    }
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, 16,
+                     NS);
+    const int units = tt.base[G];
+    const int bid = blockIdx.x, nb = gridDim.x;
+    const int nmine = bid < units ? (units - 1 - bid) / nb + 1 : 0;
+    const int total = nmine * SPU;
+    if (total == 0) return;
+
+    struct Unit { int g, slab, row0, nrows; };
+    auto unit_of = [&](int ui) __attribute__((always_inline)) {
+        const int u = bid + ui * nb;
+        Unit r;
+        r.g = __builtin_amdgcn_readfirstlane(find_group(tt, G, u));
+        const int local = u - __builtin_amdgcn_readfirstlane(tt.base[r.g]);
+        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[r.g]);
+        r.slab = local / mt;
+        const int mc = local - r.slab * mt;
+        r.row0 = __builtin_amdgcn_readfirstlane(tt.start[r.g]) + 16 * mc;
+        r.nrows = min(16, __builtin_amdgcn_readfirstlane(tt.rows[r.g]) - 16 * mc);
+        return r;
+    };
+
+    // Issue cursor: the next stage to issue is row group (stage index & 3)
+    // of k range ikc of unit iu.  On entering a unit: the first weight row
+    // of each row group, this lane's token row (at the lane's k offset) and
+    // the sources of this lane's two epilogue-constant dwords.
+    const size_t rowb = (size_t)p.K * esz;
+    int iu = 0, ikc = 0;
+    const char *wr[4] = {nullptr, nullptr, nullptr, nullptr};
+    const char *e0 = nullptr, *e1 = nullptr;
+    const uint16_t *arow = nullptr;
+    auto enter = [&](int ui) __attribute__((always_inline)) {
+        const Unit U = unit_of(ui);
+        const bool routed = U.g < p.E;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+            wr[rg] = weight_row(p, routed, U.g, 64 * U.slab + 16 * rg, esz);
+        const int slotrow = U.row0 + (l16 < U.nrows ? l16 : 0);
+        int src = slotrow;
+        if (UP) src = routed ? stok[slotrow] : slotrow - p.shared_base;
+        arow = (const uint16_t *)p.A + (size_t)src * p.K +
+               (FP8 ? (CB / 4) * wave + 16 * q : (CB / 8) * wave + 8 * q);
+        // constants: the unit's 64 columns, or (gated) its 32 features
+        const int F = gated ? p.N >> 1 : p.N;
+        const int c0 = gated ? 32 * U.slab : 64 * U.slab;
+        const uint16_t *b1 = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)U.g * F : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const uint16_t *b3 = !gated ? nullptr : routed
+            ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)U.g * F : nullptr)
+            : (const uint16_t *)p.bias_s3;
+        const float *s1 = !FP8 ? nullptr : routed ? p.scale + (size_t)U.g * F : p.scale_s;
+        const float *s3 = !(FP8 && gated) ? nullptr
+            : routed ? p.scale3 + (size_t)U.g * F : p.scale_s3;
+        e0 = nullptr;
+        e1 = nullptr;
+        if (gated) {
+            if (lane < 16) e0 = b1 ? (const char *)(b1 + c0) + 4 * lane : nullptr;
+            else if (lane >= 32 && lane < 48)
+                e0 = b3 ? (const char *)(b3 + c0) + 4 * (lane - 32) : nullptr;
+            if (lane < 32) e1 = s1 ? (const char *)(s1 + c0 + lane) : nullptr;
+            else e1 = s3 ? (const char *)(s3 + c0 + lane - 32) : nullptr;
+        } else {
+            if (lane < 32) e0 = b1 ? (const char *)(b1 + c0) + 4 * lane : nullptr;
+            e1 = s1 ? (const char *)(s1 + c0 + lane) : nullptr;
+        }
+        if (!e0) e0 = wr[0];
+        if (!e1) e1 = wr[0];
+    };
+
+    // Issue the next stage (row group RG of k range ikc): the constants and
+    // 16 weight rows x CB bytes into slot (this wave: rows 4 wave .. +3),
+    // and for row group 0 this wave's quarter of the k range's token rows
+    // into ab.  Past the last stage every load re-reads one line.
+    auto issue = [&](auto rgc, bool real, u32x4 *slot, u32x4 (&ab)[NA]) __attribute__((always_inline)) {
+        constexpr int RG = decltype(rgc)::value;
+        if (RG == 0 && real && ikc == 0) enter(iu);
+        u32x4 *ep = slot + CPS + EPI * wave;
+        ring::dma4(real ? e0 : wr[0], ep);
+        ring::dma4(real ? e1 : wr[0], ep + 16);
+        const char *wb = wr[RG] + (size_t)ikc * CB + 4 * wave * rowb;
+        const uint32_t loff = real ? (uint32_t)lane * 16 : 0u;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            // 1 KB of row 4 wave + jr (half h of a 2 KB run)
+            const int jr = NI == 8 ? j >> 1 : j, h = NI == 8 ? (j & 1) : 0;
+            const char *rb = real ? wb + jr * rowb + h * 1024 : wr[0];
+            ring::dma16nt(rb + loff, slot + (4 * wave + jr) * RS + h * 64);
+        }
+        if (RG == 0) {
+            const uint16_t *a = real ? arow + (size_t)ikc * (FP8 ? CB : CB / 2)
+                                     : (const uint16_t *)p.A;
+#pragma unroll
+            for (int s = 0; s < SS; ++s) {
+                if (FP8) {
+                    ab[2 * s] = *(const u32x4 *)(a + 64 * s);
+                    ab[2 * s + 1] = *(const u32x4 *)(a + 64 * s + 8);
+                } else {
+                    ab[s] = *(const u32x4 *)(a + 32 * s);
+                }
+            }
+        }
+        if (RG == 3 && real && ++ikc == KC) {
+            ikc = 0;
+            ++iu;
+        }
+    };
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint16_t *out = (uint16_t *)p.out;
+
+    // The unit's partial sums are complete: add the four waves' through
+    // the slot its last stage left, finish, store.
+    auto finish = [&](int ui, u32x4 *slot) __attribute__((always_inline)) {
+        const Unit U = unit_of(ui);
+        // [wave][row group][16 tokens][16 columns]: 16 KB, inside the
+        // stage part of the slot; every wave has read the stage first
+        float *red = (float *)slot;
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[((wave * 4 + rg) * 16 + l16) * 16 + 4 * q + v] = acc[rg][v];
+        __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        const uint32_t *ep = (const uint32_t *)(slot + CPS + EPI * wave);
+        const uint16_t *eb = (const uint16_t *)ep;
+        const float *es = (const float *)(ep + 64);
+        const bool routed = U.g < p.E;
+        const int m = tid >> 4;
+        auto sum = [&](int col) __attribute__((always_inline)) {
+            // virtual column col (0..63) of the unit: row group col / 16
+            const int rg = col >> 4, c = col & 15;
+            float x = red[((0 * 4 + rg) * 16 + m) * 16 + c] +
+                      red[((1 * 4 + rg) * 16 + m) * 16 + c];
+            x += red[((2 * 4 + rg) * 16 + m) * 16 + c];
+            x += red[((3 * 4 + rg) * 16 + m) * 16 + c];
+            return x;
+        };
+        if (gated) {
+            // features 2 (tid & 15), +1 of the unit's 32
+            const bool has_b1 = routed ? p.bias != nullptr : p.bias_s != nullptr;
+            const bool has_b3 = routed ? p.bias3 != nullptr : p.bias_s3 != nullptr;
+            float h[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int f = 2 * (tid & 15) + i;
+                float gv = sum(f), uv = sum(32 + f);
+                if (FP8) {
+                    gv *= es[f];
+                    uv *= es[32 + f];
+                }
+                if (has_b1) gv += bf16_to_f32(eb[f]);
+                if (has_b3) uv += bf16_to_f32(eb[64 + f]);
+                h[i] = silu_f(gv) * uv;
+            }
+            if (m < U.nrows)
+                *(uint32_t *)(out + (size_t)(U.row0 + m) * p.ldo + 32 * U.slab +
+                              2 * (tid & 15)) = pack_bf16x2(h[0], h[1]);
+        } else {
+            // columns 4 (tid & 15) .. +3 of the unit's 64
+            const bool has_b = routed ? p.bias != nullptr : p.bias_s != nullptr;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * (tid & 15) + i;
+                float x = sum(c);
+                if (FP8) x *= es[c];
+                if (has_b) x += bf16_to_f32(eb[c]);
+                v[i] = UP ? act_up(p.act, x) : x;
+            }
+            if (m < U.nrows) {
+                u32x2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *(u32x2 *)(out + (size_t)(U.row0 + m) * p.ldo + 64 * U.slab +
+                           4 * (tid & 15)) = o;
+            }
+        }
+    };
+
+    auto compute = [&](auto rgc, const u32x4 *slot, const u32x4 (&ab)[NA]) __attribute__((always_inline)) {
+        constexpr int RG = decltype(rgc)::value;
+        const u32x4 *brow = slot + l16 * RS + (CPR / 4) * wave + q;
+#pragma unroll
+        for (int s = 0; s < SS; ++s) {
+            // this lane's 16 weight bytes: row l16, chunk 4 s + q of the
+            // wave's quarter of the stage
+            const u32x4 b = brow[4 * s];
+            if (FP8) {
+                acc[RG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(e4m3x8_to_bf16x8(b[0], b[1])), as_bf16x8(ab[2 * s]),
+                    acc[RG], 0, 0, 0);
+                acc[RG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(e4m3x8_to_bf16x8(b[2], b[3])), as_bf16x8(ab[2 * s + 1]),
+                    acc[RG], 0, 0, 0);
+            } else {
+                acc[RG] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(b), as_bf16x8(ab[s]), acc[RG], 0, 0, 0);
+            }
+        }
+    };
+
+    // Step t (t % 8 == I): stage t landed everywhere (this wave's loads of
+    // the next two stages may still be in flight), stage t + 3 issued into
+    // the slot that stage t - 1 left, stage t (row group I % 4, token rows
+    // of set I / 4) consumed; the last stage of a unit finishes it (steps
+    // past the last stage change only acc).
+    int cu = 0, ckc = 0;
+    u32x4 abs0[NA], abs1[NA];
+    auto step = [&](auto ic, int t, u32x4 *cur, u32x4 *nxt) __attribute__((always_inline)) {
+        constexpr int I = decltype(ic)::value;
+        constexpr int RG = I % 4, NRG = (I + 3) % 4;
+        // loads issued after stage t: stages t + 1 and t + 2
+        constexpr int AFTER = ((I + 1) % 4 == 0 || (I + 2) % 4 == 0) ? PW + PA : 2 * PW;
+        wait_vmcnt<AFTER>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (((I + 3) / 4) % 2 == 0)
+            issue(std::integral_constant<int, NRG>{}, t + 3 < total, nxt, abs0);
+        else
+            issue(std::integral_constant<int, NRG>{}, t + 3 < total, nxt, abs1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (I / 4 == 0) compute(std::integral_constant<int, RG>{}, cur, abs0);
+        else compute(std::integral_constant<int, RG>{}, cur, abs1);
+        if (RG == 3 && ++ckc == KC) {
+            if (t < total) finish(cu, cur);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) acc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+            ckc = 0;
+            ++cu;
+        }        // keep this step's MFMAs ahead of the next step's barrier
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue(std::integral_constant<int, 0>{}, true, sl0, abs0);
+    issue(std::integral_constant<int, 1>{}, 1 < total, sl1, abs0);
+    issue(std::integral_constant<int, 2>{}, 2 < total, sl2, abs0);
+    // whole rounds of eight steps (two k ranges)
+    for (int t = 0; t < total; t += 8) {
+        step(std::integral_constant<int, 0>{}, t, sl0, sl3);
+        step(std::integral_constant<int, 1>{}, t + 1, sl1, sl0);
+        step(std::integral_constant<int, 2>{}, t + 2, sl2, sl1);
+        step(std::integral_constant<int, 3>{}, t + 3, sl3, sl2);
+        step(std::integral_constant<int, 4>{}, t + 4, sl0, sl3);
+        step(std::integral_constant<int, 5>{}, t + 5, sl1, sl0);
+        step(std::integral_constant<int, 6>{}, t + 6, sl2, sl1);
+        step(std::integral_constant<int, 7>{}, t + 7, sl3, sl2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing re-reads have landed
+}
+
 // fp32 grouped GEMM on the vector ALUs (64 x 64 x 16 tiles, 4 x 4 outputs
 // per thread, sequential fp32 FMA over k).
 template <bool UP>
@@ -1545,6 +1872,8 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
     case GEMM_BF16_W4_256x256: return {256, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
+    case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
     default: return {64, 64, 256, 0};
     }
 }
@@ -1586,6 +1915,22 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
         return up ? launch_w4<true, 128>(p, grid, s)
                   : launch_w4<false, 128>(p, grid, s);
 
+    case GEMM_BF16_RING_16x16:
+        if (up)
+            hipLaunchKernelGGL((gemm_ring<true, false, MOE_RING_CB_BF16>),
+                               dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_ring<false, false, MOE_RING_CB_BF16>),
+                               dim3(grid), dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_FP8_RING_16x16:
+        if (up)
+            hipLaunchKernelGGL((gemm_ring<true, true, MOE_RING_CB_FP8>),
+                               dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_ring<false, true, MOE_RING_CB_FP8>),
+                               dim3(grid), dim3(256), 0, s, p);
+        return hipGetLastError();
     case GEMM_BF16_STREAM_32x64:
         if (up)
             hipLaunchKernelGGL((gemm_stream<true, false, 32>), dim3(grid),

@@ -78,7 +78,19 @@ enum GemmVariant {
     GEMM_BF16_DMA64_320x256 = 13,  // 320-row tiles: one per ~257-320-row group
     GEMM_BF16_W4_256x256 = 14,     // four waves of 128 x 128, K % 128 == 0
     GEMM_BF16_W4_128x256 = 15,     // the same kernel, every tile 128 x 256
+    GEMM_BF16_RING_16x16 = 16,     // weight ring through LDS, 16-row passes
+    GEMM_FP8_RING_16x16 = 17,
 };
+
+// Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),
+// and the most routed slots whose tokens they stage in LDS.
+constexpr int MOE_RING_CB_BF16 = 2048;
+constexpr int MOE_RING_CB_FP8 = 1024;
+constexpr int MOE_RING_MAXTOK = 1024;
+
+inline bool ring_variant(int v) {
+    return v == GEMM_BF16_RING_16x16 || v == GEMM_FP8_RING_16x16;
+}
 
 // Variants that stream weights over persistent (group, column-slab) units.
 inline bool stream_variant(int v) {

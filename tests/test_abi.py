@@ -257,11 +257,11 @@ PICKS = {
     "tiny_top2_f32": (4, 4),
     "switch_top1_cap": (15, 15),
     "mixtral_prefill": (14, 14),
-    "mixtral_decode": (11, 11),
+    "mixtral_decode": (16, 16),
     "deepseek_v3": (13, 13),
-    "mixtral_decode_fp8": (12, 12),
+    "mixtral_decode_fp8": (12, 17),
     "mixtral_prefill_swiglu": (14, 14),
-    "mixtral_decode_swiglu": (11, 11),
+    "mixtral_decode_swiglu": (11, 16),
     "expert_choice_c2": (8, 8),
 }
 
@@ -288,3 +288,17 @@ def test_gemm_variant_override_is_validated(monkeypatch):
     # an id out of range is ignored
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "99")
     assert moe.moe_gemm_variant(d, True) == 14
+    # the weight ring stages at most 1024 routed slots' tokens: refused for
+    # this up projection (8192 slots), accepted for the down projection
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "16")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "16")
+    assert moe.moe_gemm_variant(d, True) == 14
+    assert moe.moe_gemm_variant(d, False) == 16
+    # ... and takes K in whole 2 KB row runs
+    assert moe.moe_gemm_variant(_desc_of(w), False) == 16
+    w2 = dataclasses.replace(workloads.WORKLOADS["mixtral_prefill"],
+                             d_ff=14336 + 512)
+    assert moe.moe_gemm_variant(_desc_of(w2), False) != 16
+    # the FP8 ring needs FP8 weights
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "17")
+    assert moe.moe_gemm_variant(d, False) == 14

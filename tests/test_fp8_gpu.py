@@ -53,7 +53,7 @@ def test_fp8_small_full_parity(name):
     say(f"[fp8 small] {name}: {rep}")
 
 
-@pytest.mark.parametrize("variant", ["10", "12"])
+@pytest.mark.parametrize("variant", ["10", "12", "17"])
 def test_fp8_every_kernel_variant(variant, monkeypatch):
     """Both FP8 streaming forms (split-K block, wave per unit) forced on a
     shape with 32-row chunks, a 16-row tail and a shared expert."""

@@ -69,7 +69,7 @@ def test_small_full_parity(name):
 
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7", "8",
-                                     "9", "11", "13", "14", "15"])
+                                     "9", "11", "13", "14", "15", "16"])
 def test_every_gemm_variant(variant, monkeypatch):
     """Each bf16 tile variant forced on a shape with groups of 0 to ~100
     rows (several row chunks for the small-tile kernels)."""
