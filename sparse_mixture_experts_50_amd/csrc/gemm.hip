@@ -1397,12 +1397,12 @@ __device__ __forceinline__ void dma4(const char *src, u32x4 *lds) {
 }
 }  // namespace ring
 
-template <bool UP, bool FP8, int CB>
-__global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
+template <bool UP, bool FP8, int CB, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_ring(GemmParams p) {
     constexpr int CPR = CB / 16;          // 16-byte chunks of a row per stage
     constexpr int RS = CPR + 1;           // LDS row stride (chunks)
     constexpr int CPS = 16 * RS;          // chunks per stage
-    constexpr int EPI = 32;               // epilogue chunks per wave and slot
+    constexpr int EPI = 32;               // epilogue chunks per slot
     constexpr int NI = CB / 256;          // 1 KB weight loads per wave
     constexpr int SS = CB / 256;          // sub-steps per wave per stage
     constexpr int NA = FP8 ? 2 * SS : SS; // token-row loads per k range
@@ -1411,12 +1411,12 @@ __global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
     constexpr int esz = FP8 ? 1 : 2;
     static_assert(PW + PA < 64, "vmcnt range");
     static_assert(CPS * 16 >= 4 * 4 * 16 * 16 * 4, "reduction fits a stage");
-    // A slot: the stage, then each wave's copy of the unit's epilogue
-    // constants, 128 dwords: 0-31 the bf16 biases of the 64 columns (gated:
-    // 0-15 the 32 gate biases, 32-47 the 32 up biases), 64-127 the FP8
-    // scales (gated: 64-95 gate, 96-127 up).
-    __shared__ u32x4 sl0[CPS + 4 * EPI], sl1[CPS + 4 * EPI],
-        sl2[CPS + 4 * EPI], sl3[CPS + 4 * EPI];
+    // A slot: the stage, then the unit's epilogue constants, 128 dwords
+    // (every wave loads the same copy): 0-31 the bf16 biases of the 64
+    // columns (gated: 0-15 the 32 gate biases, 32-47 the 32 up biases),
+    // 64-127 the FP8 scales (gated: 64-95 gate, 96-127 up).
+    __shared__ u32x4 sl0[CPS + EPI], sl1[CPS + EPI], sl2[CPS + EPI],
+        sl3[CPS + EPI];
     __shared__ int stok[ring::MAXTOK];
     __shared__ TileTable tt;
 
@@ -1435,8 +1435,13 @@ __global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
     build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, 16,
                      NS);
     const int units = tt.base[G];
-    const int bid = blockIdx.x, nb = gridDim.x;
-    const int nmine = bid < units ? (units - 1 - bid) / nb + 1 : 0;
+    // as few blocks as give every block the same number of units (a block
+    // with one unit fewer than the rest would leave its share of the
+    // bandwidth idle for a unit's time)
+    const int per = (units + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int nb = per > 0 ? (units + per - 1) / per : 0;
+    const int bid = blockIdx.x;
+    const int nmine = bid < units && bid < nb ? (units - 1 - bid) / nb + 1 : 0;
     const int total = nmine * SPU;
     if (total == 0) return;
 
@@ -1505,25 +1510,27 @@ __global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
     // Issue the next stage (row group RG of k range ikc): the constants and
     // 16 weight rows x CB bytes into slot (this wave: rows 4 wave .. +3),
     // and for row group 0 this wave's quarter of the k range's token rows
-    // into ab.  Past the last stage every load re-reads one line.
+    // into ab.  Past the last stage the cursor stays on the last unit and
+    // each weight load re-reads one line (its lane offset is multiplied by
+    // zero: a select between two addresses would give the compiler a
+    // second path and cost exact waits).
     auto issue = [&](auto rgc, bool real, u32x4 *slot, u32x4 (&ab)[NA]) __attribute__((always_inline)) {
         constexpr int RG = decltype(rgc)::value;
         if (RG == 0 && real && ikc == 0) enter(iu);
-        u32x4 *ep = slot + CPS + EPI * wave;
-        ring::dma4(real ? e0 : wr[0], ep);
-        ring::dma4(real ? e1 : wr[0], ep + 16);
+        u32x4 *ep = slot + CPS;
+        ring::dma4(e0, ep);
+        ring::dma4(e1, ep + 16);
         const char *wb = wr[RG] + (size_t)ikc * CB + 4 * wave * rowb;
-        const uint32_t loff = real ? (uint32_t)lane * 16 : 0u;
+        const uint32_t loff = (uint32_t)lane * 16 * (uint32_t)real;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             // 1 KB of row 4 wave + jr (half h of a 2 KB run)
             const int jr = NI == 8 ? j >> 1 : j, h = NI == 8 ? (j & 1) : 0;
-            const char *rb = real ? wb + jr * rowb + h * 1024 : wr[0];
-            ring::dma16nt(rb + loff, slot + (4 * wave + jr) * RS + h * 64);
+            ring::dma16nt(wb + jr * rowb + h * 1024 + loff,
+                          slot + (4 * wave + jr) * RS + h * 64);
         }
         if (RG == 0) {
-            const uint16_t *a = real ? arow + (size_t)ikc * (FP8 ? CB : CB / 2)
-                                     : (const uint16_t *)p.A;
+            const uint16_t *a = arow + (size_t)ikc * (FP8 ? CB : CB / 2);
 #pragma unroll
             for (int s = 0; s < SS; ++s) {
                 if (FP8) {
@@ -1560,7 +1567,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring(GemmParams p) {
                 red[((wave * 4 + rg) * 16 + l16) * 16 + 4 * q + v] = acc[rg][v];
         __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        const uint32_t *ep = (const uint32_t *)(slot + CPS + EPI * wave);
+        const uint32_t *ep = (const uint32_t *)(slot + CPS);
         const uint16_t *eb = (const uint16_t *)ep;
         const float *es = (const float *)(ep + 64);
         const bool routed = U.g < p.E;
@@ -1874,6 +1881,8 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
     case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
+    case GEMM_BF16_RING2_16x16: return {16, 16, 256, 4 * 16 * 1024};
+    case GEMM_FP8_RING2_16x16: return {16, 16, 256, 4 * 16 * 1024};
     default: return {64, 64, 256, 0};
     }
 }
@@ -1917,18 +1926,34 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
 
     case GEMM_BF16_RING_16x16:
         if (up)
-            hipLaunchKernelGGL((gemm_ring<true, false, MOE_RING_CB_BF16>),
+            hipLaunchKernelGGL((gemm_ring<true, false, MOE_RING_CB_BF16, 1>),
                                dim3(grid), dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((gemm_ring<false, false, MOE_RING_CB_BF16>),
+            hipLaunchKernelGGL((gemm_ring<false, false, MOE_RING_CB_BF16, 1>),
                                dim3(grid), dim3(256), 0, s, p);
         return hipGetLastError();
     case GEMM_FP8_RING_16x16:
         if (up)
-            hipLaunchKernelGGL((gemm_ring<true, true, MOE_RING_CB_FP8>),
+            hipLaunchKernelGGL((gemm_ring<true, true, MOE_RING_CB_FP8, 1>),
                                dim3(grid), dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((gemm_ring<false, true, MOE_RING_CB_FP8>),
+            hipLaunchKernelGGL((gemm_ring<false, true, MOE_RING_CB_FP8, 1>),
+                               dim3(grid), dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_BF16_RING2_16x16:
+        if (up)
+            hipLaunchKernelGGL((gemm_ring<true, false, 1024, 2>),
+                               dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_ring<false, false, 1024, 2>),
+                               dim3(grid), dim3(256), 0, s, p);
+        return hipGetLastError();
+    case GEMM_FP8_RING2_16x16:
+        if (up)
+            hipLaunchKernelGGL((gemm_ring<true, true, 1024, 2>),
+                               dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_ring<false, true, 1024, 2>),
                                dim3(grid), dim3(256), 0, s, p);
         return hipGetLastError();
     case GEMM_BF16_STREAM_32x64:

@@ -80,6 +80,8 @@ enum GemmVariant {
     GEMM_BF16_W4_128x256 = 15,     // the same kernel, every tile 128 x 256
     GEMM_BF16_RING_16x16 = 16,     // weight ring through LDS, 16-row passes
     GEMM_FP8_RING_16x16 = 17,
+    GEMM_BF16_RING2_16x16 = 18,    // 1 KB row runs, two blocks per CU
+    GEMM_FP8_RING2_16x16 = 19,
 };
 
 // Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),
@@ -89,7 +91,17 @@ constexpr int MOE_RING_CB_FP8 = 1024;
 constexpr int MOE_RING_MAXTOK = 1024;
 
 inline bool ring_variant(int v) {
-    return v == GEMM_BF16_RING_16x16 || v == GEMM_FP8_RING_16x16;
+    return v == GEMM_BF16_RING_16x16 || v == GEMM_FP8_RING_16x16 ||
+           v == GEMM_BF16_RING2_16x16 || v == GEMM_FP8_RING2_16x16;
+}
+
+// Blocks per CU of a weight-ring variant, and its bytes of each row per
+// stage.
+inline int ring_occupancy(int v) {
+    return v == GEMM_BF16_RING2_16x16 || v == GEMM_FP8_RING2_16x16 ? 2 : 1;
+}
+inline int ring_cb(int v) {
+    return v == GEMM_BF16_RING_16x16 ? MOE_RING_CB_BF16 : v == GEMM_FP8_RING_16x16 ? MOE_RING_CB_FP8 : 1024;
 }
 
 // Variants that stream weights over persistent (group, column-slab) units.

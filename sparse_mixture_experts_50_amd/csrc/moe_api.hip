@@ -241,10 +241,10 @@ bool w4_fits(const moe_desc *d, bool up) {
 
 // The weight-ring kernels take K in stages of whole row runs and stage
 // the routed slots' token indices in LDS.
-bool ring_fits(const moe_desc *d, bool up, bool fp8) {
+bool ring_fits(const moe_desc *d, bool up, int variant) {
+    const bool fp8 = variant == GEMM_FP8_RING_16x16 || variant == GEMM_FP8_RING2_16x16;
     const long long K = up ? d->d : d->d_ff;
-    const long long cb = fp8 ? MOE_RING_CB_FP8 : MOE_RING_CB_BF16;
-    if ((K * (fp8 ? 1 : 2)) % cb != 0) return false;
+    if ((K * (fp8 ? 1 : 2)) % ring_cb(variant) != 0) return false;
     return !up || routed_rows(d) <= MOE_RING_MAXTOK;
 }
 
@@ -256,10 +256,10 @@ int variant_override(bool up, const moe_desc *d, int N) {
     if (gated_up(d, up) && !gate_capable(id)) return -1;
     const bool fp8_id = id == GEMM_FP8_STREAM_32x64 ||
                         id == GEMM_FP8_STREAM_64x64 ||
-                        id == GEMM_FP8_RING_16x16;
-    if (ring_variant(id) && !ring_fits(d, up, fp8_id)) return -1;
+                        id == GEMM_FP8_RING_16x16 || id == GEMM_FP8_RING2_16x16;
+    if (ring_variant(id) && !ring_fits(d, up, id)) return -1;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_RING_16x16 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_FP8_RING2_16x16 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
@@ -310,23 +310,22 @@ int pick_variant(const moe_desc *d, int N, bool up) {
     const double avg = (double)routed_rows(d) / d->E;
     // The weight ring reads each weight byte once per 16-row chunk of a
     // group, so it is used where groups are expected to fit one chunk
-    // (and the shared expert too).  Measured on the Mixtral-shaped decode
-    // GEMMs it is faster than the register-streaming kernel for ungated
-    // bf16 panels and the FP8 down projection, slower for the gated and
-    // FP8 up projections (whose units read two panels, or token rows twice
-    // the weight bytes).
+    // (and the shared expert too), in its two-blocks-per-CU form.  Measured
+    // on the Mixtral-shaped decode GEMMs it is 8-18 % faster than the
+    // register-streaming kernel, except for the gated up projection (whose
+    // units read the W1 and W3 panels at the same offsets), 8 % slower.
     const bool ring_rows = avg <= 12.0 && (d->n_shared == 0 || d->T <= 16);
     if (d->expert_fp8)
-        return !up && ring_rows && ring_fits(d, up, true) ? GEMM_FP8_RING_16x16
-                                                          : GEMM_FP8_STREAM_64x64;
+        return ring_rows && !gated_up(d, up) && ring_fits(d, up, GEMM_FP8_RING2_16x16)
+                   ? GEMM_FP8_RING2_16x16 : GEMM_FP8_STREAM_64x64;
     if (N % 256 != 0) return GEMM_BF16_64x64;
     const int K = up ? d->d : d->d_ff;
     // the streaming kernel splits K in four quarters of whole 64-deep
     // load batches; 64-column units re-read the token rows half as often
     // as 32-column ones
     if (avg <= 32.0 && d->d % 256 == 0 && d->d_ff % 256 == 0) {
-        if (ring_rows && !gated_up(d, up) && ring_fits(d, up, false))
-            return GEMM_BF16_RING_16x16;
+        if (ring_rows && !gated_up(d, up) && ring_fits(d, up, GEMM_BF16_RING2_16x16))
+            return GEMM_BF16_RING2_16x16;
         return GEMM_BF16_STREAM_64x64;
     }
     if (avg <= 48.0) return GEMM_BF16_32x256;
@@ -349,7 +348,7 @@ int pick_variant(const moe_desc *d, int N, bool up) {
 
 int gemm_grid(const moe_desc *d, int variant, int N) {
     const GemmVariantInfo vi = gemm_variant_info(variant);
-    if (ring_variant(variant)) return device_cus();   // one block per CU
+    if (ring_variant(variant)) return device_cus() * ring_occupancy(variant);
     if (stream_variant(variant)) {              // persistent over units
         const long long units = (long long)(d->E + d->n_shared) * (N / vi.bn);
         const long long slots = (long long)device_cus() * 2;

@@ -257,11 +257,11 @@ PICKS = {
     "tiny_top2_f32": (4, 4),
     "switch_top1_cap": (15, 15),
     "mixtral_prefill": (14, 14),
-    "mixtral_decode": (16, 16),
+    "mixtral_decode": (18, 18),
     "deepseek_v3": (13, 13),
-    "mixtral_decode_fp8": (12, 17),
+    "mixtral_decode_fp8": (19, 19),
     "mixtral_prefill_swiglu": (14, 14),
-    "mixtral_decode_swiglu": (11, 16),
+    "mixtral_decode_swiglu": (11, 18),
     "expert_choice_c2": (8, 8),
 }
 

@@ -54,9 +54,16 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_ring_forced(name, monkeypatch):
+# each ring case on both forms: 2 KB bf16 row runs with one block per CU
+# (16; FP8 17) and 1 KB runs with two blocks per CU (18; FP8 19)
+FORMS = {16: 18, 17: 19}
+
+
+@pytest.mark.parametrize("name,form", [(n, f) for n in CASES for f in (0, 1)])
+def test_ring_forced(name, form, monkeypatch):
     w, variant = CASES[name]
+    if form:
+        variant = FORMS[variant]
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", str(variant))
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", str(variant))
     say(f"[ring {variant}] {name}: {w}")
@@ -70,8 +77,11 @@ def test_ring_forced(name, monkeypatch):
 
 
 @pytest.mark.parametrize("name,variant", [("mixtral_decode", 16),
+                                          ("mixtral_decode", 18),
                                           ("mixtral_decode_swiglu", 16),
-                                          ("mixtral_decode_fp8", 17)])
+                                          ("mixtral_decode_swiglu", 18),
+                                          ("mixtral_decode_fp8", 17),
+                                          ("mixtral_decode_fp8", 19)])
 def test_ring_full_size_sampled(name, variant, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", str(variant))
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", str(variant))
