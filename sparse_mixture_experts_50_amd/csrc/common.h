@@ -48,24 +48,30 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 //   erfc(x) = t exp(-x^2 + P(t)),  t = 1 / (1 + x / 2),
 // P a degree-9 polynomial, with fractional error below 1.2e-7 for every x.
 // The error being relative, the deep negative tail (where Phi is tiny) is
-// as accurate as the rest; with x = |z| / sqrt 2 and q = erfc(x),
-// Phi(z) = q / 2 for z < 0 and 1 - q / 2 otherwise.  No branch: a tile
-// epilogue evaluates hundreds of these per lane in straight-line code, so
-// independent evaluations interleave and hide the transcendental latency.
+// as accurate as the rest.  With x = |z| / sqrt 2 and q = erfc(x) / 2,
+// Phi(z) = q for z < 0 and 1 - q otherwise, so z Phi(z) = max(z, 0) - |z| q
+// for either sign, without a select.  The hardware exponential is base 2,
+// so P's coefficients below are those of the book times log2(e), with
+// log2(1/2) = -1 added to the constant term for the halving, and the 1/sqrt 2
+// of x is folded into the reciprocal's and the square's factors: about 19
+// vector instructions per value, two of them transcendental.  No branch: a
+// tile epilogue evaluates hundreds of these per lane in straight-line code,
+// so independent evaluations interleave and hide the latencies.
 __device__ __forceinline__ float gelu_erf(float z) {
-    const float x = fabsf(z) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
-    float r = fmaf(0.17087277f, t, -0.82215223f);
-    r = fmaf(r, t, 1.48851587f);
-    r = fmaf(r, t, -1.13520398f);
-    r = fmaf(r, t, 0.27886807f);
-    r = fmaf(r, t, -0.18628806f);
-    r = fmaf(r, t, 0.09678418f);
-    r = fmaf(r, t, 0.37409196f);
-    r = fmaf(r, t, 1.00002368f);
-    r = fmaf(r, t, -1.26551223f);
-    const float q = t * __expf(fmaf(-x, x, r));
-    return z * (z < 0.0f ? 0.5f * q : fmaf(-0.5f, q, 1.0f));
+    const float az = fabsf(z);
+    const float t = __builtin_amdgcn_rcpf(fmaf(az, 0.35355339f, 1.0f));
+    float r = fmaf(0.24651730f, t, -1.18611491f);
+    r = fmaf(r, t, 2.14747453f);
+    r = fmaf(r, t, -1.63775313f);
+    r = fmaf(r, t, 0.40232158f);
+    r = fmaf(r, t, -0.26875687f);
+    r = fmaf(r, t, 0.13963005f);
+    r = fmaf(r, t, 0.53970063f);
+    r = fmaf(r, t, 1.44272923f);
+    r = fmaf(r, t, -2.82574821f);
+    // log2 of erfc(x) / (2 t) = -x^2 log2(e) + (scaled P)(t), x^2 = z^2 / 2
+    const float q = t * __builtin_amdgcn_exp2f(fmaf(z * -0.72134752f, z, r));
+    return fmaf(-az, q, fmaxf(z, 0.0f));
 }
 
 // ------------------------------------------------------------- wave ops
