@@ -5,11 +5,12 @@
 // sum 1; sec. 2.4: routing uses logits - b_i.  "AI-Research-SKILLs MoE
 // training guide", sec. 3.1: the router is an nn.Linear (additive bias).
 //
-// bf16: two kernels.  router_logits spreads the logits GEMM over many
-// blocks: each block takes 32 (E <= 64) or 128 (E > 64) tokens, all
-// experts and one of S consecutive depth ranges, with MFMA 32x32x16 (fp32
-// accumulation), and writes fp32 partial sums; a single block per 32 tokens
-// would pull every token row through one CU.  router_route sums the S
+// bf16: two kernels.  The logits kernel spreads the logits GEMM over many
+// blocks: each block takes 32 (E <= 64, router_logits) or 256 (E > 64,
+// router_logits_lds, router rows staged in LDS) tokens, all experts and one
+// of S consecutive depth ranges, with MFMA 32x32x16 (fp32 accumulation),
+// and writes fp32 partial sums; a single block per 32 tokens would pull
+// every token row through one CU.  router_route sums the S
 // partials in order (deterministic), then routes 32 tokens per block: for
 // E <= 32 one lane per token walks its E logits in registers (no cross-lane
 // traffic); for larger E each wave takes 2 tokens across its 64 lanes.
@@ -266,6 +267,106 @@ __global__ __launch_bounds__(256) void router_logits(RouterParams p) {
     }
 }
 
+// Partial logits over one depth range for E > 64 (EP = 128 or 256).  A
+// block takes 256 tokens, 64 per wave (two 32-token MFMA tiles), and every
+// expert: each wave holds 2 x EP / 32 accumulator tiles of 32x32.  The
+// router rows of each 64-deep step are staged in LDS once per block (two
+// buffers, loaded into registers one step ahead, one barrier per step) and
+// every wave reads its B fragments there; with 64 tokens per wave each
+// fragment feeds two MFMAs.  Against one 32-token tile per wave reading
+// the router rows straight from L2, the router matrix is pulled from L2 a
+// quarter as often per token and half as often per MFMA.  Staged rows are
+// 128 bytes of eight 16-byte chunks, chunk c of row r at c ^ ((r / 2) % 8),
+// so that 32 lanes reading 32 rows at one chunk hit distinct bank groups.
+template <int EP>
+__global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
+    constexpr int ET = EP / 32;                 // 32-expert tiles
+    constexpr int CH = EP * 8;                  // 16-byte chunks per step
+    constexpr int PT = CH / 256;                // chunks per thread per step
+    __shared__ u32x4 wst0[CH], wst1[CH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.y;
+    const int k_lo = s * p.kc, k_hi = min(p.d, k_lo + p.kc);
+    const int t0 = blockIdx.x * 256 + wave * 64;
+    const int kg = (lane >> 5) * 8;
+    const uint16_t *xr[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int tok = min(t0 + 32 * m + (lane & 31), p.T - 1);
+        xr[m] = (const uint16_t *)p.x + (size_t)tok * p.d + kg;
+    }
+    const uint16_t *wsrc[PT];
+    int wdst[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 3, c = idx & 7;
+        const int e = min(r, p.E - 1);
+        wsrc[i] = (const uint16_t *)p.wr + (size_t)e * p.d + 8 * c;
+        wdst[i] = r * 8 + (c ^ ((r >> 1) & 7));
+    }
+    floatx16 acc[2][ET];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][et][v] = 0.0f;
+
+    u32x4 wreg[PT], areg[2][4];
+    auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) wreg[i] = *(const u32x4 *)(wsrc[i] + k0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                areg[m][j] = *(const u32x4 *)(xr[m] + k0 + 16 * j);
+    };
+    load(k_lo);
+    int buf = 0;
+    for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
+        u32x4 *st = buf ? wst1 : wst0;
+#pragma unroll
+        for (int i = 0; i < PT; ++i) st[wdst[i]] = wreg[i];
+        u32x4 a[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[m][j] = areg[m][j];
+        __syncthreads();
+        if (k0 + 64 < k_hi) load(k0 + 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 2 * j + (lane >> 5);
+#pragma unroll
+            for (int et = 0; et < ET; ++et) {
+                const int r = 32 * et + (lane & 31);
+                const u32x4 bv = st[r * 8 + (c ^ ((r >> 1) & 7))];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    acc[m][et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(a[m][j]), as_bf16x8(bv), acc[m][et], 0, 0, 0);
+            }
+        }
+        buf ^= 1;
+    }
+    // D[token][expert]: lane holds expert column lane%32 and token rows
+    // 8*(v/4) + 4*(lane/32) + v%4 of its tile
+    float *part = p.part + (size_t)s * p.T * p.E;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+            const int e = 32 * et + (lane & 31);
+            if (e >= p.E) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + 32 * m + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (t < p.T) part[(size_t)t * p.E + e] = acc[m][et][v];
+            }
+        }
+}
+
 // One lane per token (E <= EP = 32): softmax, statistics and selection on
 // the token's logits held in registers, written as selects rather than
 // branches (padding experts hold -inf and never win a pick, k <= E); the
@@ -515,20 +616,23 @@ RouterPlan router_plan(int T, int d, int E, int cus) {
     const double fbytes = 2.0 * d * (RT + E);
     r.split = !(fblocks >= cus && fbytes <= 200e3);
     const bool small = r.ep <= 64;
-    r.tokens = small ? 32 : 128;
+    r.tokens = small ? 32 : 256;
     const int kw = small ? 4 / (r.ep / 32) : 1;
     const long long blocks = T > 0 ? (T + r.tokens - 1) / r.tokens : 1;
-    // about two blocks per CU (one for E > 64, whose blocks are four times
-    // larger), each wave keeping at least 8 MFMA steps of its range
+    // about two blocks per CU (one for E > 64, whose blocks of 256 tokens
+    // hold a wave per SIMD), each wave keeping at least 8 16-deep MFMA
+    // steps of its range (E > 64: four 64-deep staged steps)
     const long long want = (long long)cus * (small ? 2 : 1);
     int S = (int)((want + blocks - 1) / blocks);
-    const int most = d / (16 * 8 * kw);
+    const int most = small ? d / (16 * 8 * kw) : d / 256;
     if (S > most) S = most;
     if (S > MOE_ROUTER_MAX_SPLITS) S = MOE_ROUTER_MAX_SPLITS;
     if (S < 1) S = 1;
-    // whole 16-deep steps per range (d is a multiple of 64)
+    // whole steps per range (d is a multiple of 64): 16 deep, or 64 deep
+    // for the staged kernel
+    const int step = small ? 16 : 64;
     int kc = (d + S - 1) / S;
-    kc = (kc + 15) / 16 * 16;
+    kc = (kc + step - 1) / step * step;
     r.S = (d + kc - 1) / kc;
     r.kc = kc;
     return r;
@@ -548,7 +652,7 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
         return hipGetLastError();
     }
     if (dtype == 1) {
-        const int tokens = EP <= 64 ? 32 : 128;
+        const int tokens = EP <= 64 ? 32 : 256;
         const dim3 lgrid((p.T + tokens - 1) / tokens, p.S);
         switch (EP) {
         case 32:
@@ -560,11 +664,11 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
             hipLaunchKernelGGL(router_route<64>, grid, block, 0, s, p);
             break;
         case 128:
-            hipLaunchKernelGGL(router_logits<128>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_logits_lds<128>, lgrid, dim3(256), 0, s, p);
             hipLaunchKernelGGL(router_route<128>, grid, block, 0, s, p);
             break;
         default:
-            hipLaunchKernelGGL(router_logits<256>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL(router_logits_lds<256>, lgrid, dim3(256), 0, s, p);
             hipLaunchKernelGGL(router_route<256>, grid, block, 0, s, p);
             break;
         }

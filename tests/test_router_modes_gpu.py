@@ -2,7 +2,8 @@
 MI355X, each forced on every shape (MOE_ROUTER_SPLIT): fused (logits and
 routing in one 32-token block) and split (partial logits over depth ranges,
 then routing: one lane per token for E <= 32, 64-lane waves above).  Shapes
-cover E = 8, 64 and 256, ragged T, router and balancing biases, a shared
+cover E = 8, 64, 100 and 256, ragged T, several token blocks and depth
+ranges of the staged logits kernel, router and balancing biases, a shared
 expert and expert choice.  Both forms must also agree on every routing
 decision that is not a near-tie."""
 import sys
@@ -35,6 +36,12 @@ CASES = {
     "e64_switch": scaled(W["switch_top1_cap"], T=300, d=256, d_ff=512),
     # E = 256 with the balancing bias and a shared expert, top-8
     "e256_deepseek": scaled(W["deepseek_v3"], T=200, d=512, d_ff=256),
+    # E = 256 over three 256-token blocks (the last ragged) and eight
+    # depth ranges of the staged logits kernel
+    "e256_blocks": scaled(W["deepseek_v3"], T=600, d=2048, d_ff=256),
+    # E = 100: the 128-expert staged kernel with experts past E clamped
+    "e100_ragged": scaled(W["deepseek_v3"], T=300, d=1024, E=100, k=6,
+                          d_ff=256),
     # E = 16 with router Linear biases and expert Linear biases
     "e16_biases": scaled(W["deepseek_v3"], T=150, d=256, E=16, k=4,
                          d_ff=256, n_shared=0, router_bias="linear",
@@ -63,7 +70,8 @@ def test_router_mode_expert_choice(mode, monkeypatch):
         say(f"[router split={mode}] ec E={E}: {check_expert_choice(w, inp, gpu)}")
 
 
-@pytest.mark.parametrize("name", ["e8_decode", "e64_switch", "e256_deepseek"])
+@pytest.mark.parametrize("name", ["e8_decode", "e64_switch", "e256_deepseek",
+                                  "e256_blocks", "e100_ragged"])
 def test_router_modes_agree(name, monkeypatch):
     w = CASES[name]
     inp = inputs_on(w, device())
