@@ -107,12 +107,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     int part = 0;
     if (active) {
         int b = c0;
-        for (; b + 8 <= c1; b += 8) {
-            int v[8];
+        for (; b + 16 <= c1; b += 16) {
+            int v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) part += v[u];
+            for (int u = 0; u < 16; ++u) part += v[u];
         }
         for (; b < c1; ++b) part += p.blk[(size_t)b * p.E + e];
         seg_i[seg * p.E + e] = part;
@@ -121,12 +121,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     if (active) {
         float ps = 0.0f;
         int b = seg;
-        for (; b + 7 * S < p.n_rtiles; b += 8 * S) {
-            float v[8];
+        for (; b + 15 * S < p.n_rtiles; b += 16 * S) {
+            float v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
+            for (int u = 0; u < 16; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) ps += v[u];
+            for (int u = 0; u < 16; ++u) ps += v[u];
         }
         for (; b < p.n_rtiles; b += S) ps += p.p_part[(size_t)b * p.E + e];
         seg_f[seg * p.E + e] = ps;
@@ -146,14 +146,27 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         }
     }
     __syncthreads();
-    // 4. rank bases: the segment's base plus a running count over its chunks
+    // 4. rank bases: the segment's base plus a running count over its
+    // chunks, 16 counts loaded before any base is written (one memory round
+    // trip per 16 chunks rather than per chunk)
     if (active && p.n_chunks > 0) {
         int run = 0;
         for (int q = 0; q < seg; ++q) run += seg_i[q * p.E + e];
-        for (int b = c0; b < c1; ++b) {
+        int b = c0;
+        for (; b + 16 <= c1; b += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                p.blk[(size_t)(b + u) * p.E + e] = run;   // rank base in chunk b+u
+                run += v[u];
+            }
+        }
+        for (; b < c1; ++b) {
             const size_t i = (size_t)b * p.E + e;
             const int v = p.blk[i];
-            p.blk[i] = run;               // rank base of expert e in chunk b
+            p.blk[i] = run;
             run += v;
         }
     }
@@ -221,23 +234,28 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
     const int a1 = min(n, a0 + CH);
     const int total = p.offsets[p.E];
     const unsigned long long lt = (1ull << lane) - 1ull;
+    // bits of an expert id: the lanes holding the same expert as this one
+    // are those whose ballot agrees with this lane's on every bit
+    const int nbits = p.E > 1 ? 32 - __clz(p.E - 1) : 1;
     for (int base = a0; base < a1; base += 64) {
         const int a = base + lane;
         int e = a < a1 ? p.topk_idx[a] : -1;
         if ((unsigned)e >= (unsigned)p.E) e = -1;
         const bool ok = e >= 0;
+        unsigned long long same = __ballot(ok);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const unsigned long long m = __ballot(on);
+            same &= on ? m : ~m;
+        }
+        // rank: the expert's running count plus the earlier lanes of the
+        // same expert; the group's last lane advances the count (every lane
+        // of the wave has read it before: one wave, LDS in program order)
         int rank = 0;
-        unsigned long long pending = __ballot(ok);
-        while (pending) {
-            const int leader = __ffsll((long long)pending) - 1;
-            const int le = __shfl(e, leader, 64);
-            const unsigned long long same = __ballot(e == le);
-            const int r0 = run[le];
-            if (e == le) rank = r0 + __popcll(same & lt);
-            __syncthreads();   // all lanes have read run[le]
-            if (lane == leader) run[le] = r0 + __popcll(same);
-            __syncthreads();
-            pending &= ~same;
+        if (ok) {
+            const int before = __popcll(same & lt);
+            rank = run[e] + before;
+            if (before == __popcll(same) - 1) run[e] = rank + 1;
         }
         if (a < a1) {
             int slot = -1;
