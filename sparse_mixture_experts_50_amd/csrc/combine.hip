@@ -19,11 +19,17 @@ namespace {
 constexpr int MAX_K = MOE_MAX_E;     // expert choice: k = E <= 256
 
 // 16 bytes of row `row_off` (elements) at vector index v: 8 bf16 or 4 fp32.
-template <bool BF16>
+// Each expert-output row is read once, by one block, in whole 1 KB runs per
+// wave.  NT: non-temporal loads, for expert outputs larger than the
+// last-level cache (which otherwise still holds them from the down
+// projection).
+template <bool BF16, bool NT>
 __device__ __forceinline__ u32x4 load_vec(const void *yp, size_t row_off,
                                           int v) {
-    if (BF16) return *((const u32x4 *)((const uint16_t *)yp + row_off) + v);
-    return *((const u32x4 *)((const float *)yp + row_off) + v);
+    const u32x4 *q = BF16 ? (const u32x4 *)((const uint16_t *)yp + row_off) + v
+                          : (const u32x4 *)((const float *)yp + row_off) + v;
+    if (NT) return __builtin_nontemporal_load(q);
+    return *q;
 }
 
 template <bool BF16>
@@ -56,7 +62,7 @@ __device__ __forceinline__ void add_vec(float *acc, u32x4 q) {
 // assignments (slot >= 0) into LDS in j order, so every thread then walks
 // only the rows it adds, with no per-j global loads; the sum order is the
 // j order either way.
-template <bool BF16>
+template <bool BF16, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     constexpr int VW = BF16 ? 8 : 4;
     __shared__ int s_slot[MAX_K];
@@ -88,21 +94,29 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         float acc[VW];
 #pragma unroll
         for (int i = 0; i < VW; ++i) acc[i] = 0.0f;
-        // four rows in flight, added in order
+        // eight (then four) rows in flight, added in order
         int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            u32x4 q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                q[u] = load_vec<BF16, NT>(p.yp, (size_t)s_slot[i + u] * p.d, v);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) fma_vec<BF16>(acc, s_w[i + u], q[u]);
+        }
         for (; i + 4 <= n; i += 4) {
             u32x4 q[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                q[u] = load_vec<BF16>(p.yp, (size_t)s_slot[i + u] * p.d, v);
+                q[u] = load_vec<BF16, NT>(p.yp, (size_t)s_slot[i + u] * p.d, v);
 #pragma unroll
             for (int u = 0; u < 4; ++u) fma_vec<BF16>(acc, s_w[i + u], q[u]);
         }
         for (; i < n; ++i)
             fma_vec<BF16>(acc, s_w[i],
-                          load_vec<BF16>(p.yp, (size_t)s_slot[i] * p.d, v));
+                          load_vec<BF16, NT>(p.yp, (size_t)s_slot[i] * p.d, v));
         if (p.n_shared)
-            add_vec<BF16>(acc, load_vec<BF16>(
+            add_vec<BF16>(acc, load_vec<BF16, NT>(
                 p.yp, (size_t)(p.shared_base + t) * p.d, v));
         if (BF16) {
             u32x4 o;
@@ -122,9 +136,16 @@ hipError_t launch_combine(const CombineParams &p, int dtype, hipStream_t s) {
     // one 16-byte vector per thread where the row allows it
     const int nv = p.d / (dtype == 1 ? 8 : 4);
     const int threads = nv >= 256 ? 256 : (nv + 63) / 64 * 64;
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(p.T), dim3(threads), 0, s, p);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(p.T), dim3(threads), 0, s, p);
+    // expert outputs beyond the 256 MB last-level cache: non-temporal
+    const double rows = (double)p.T * p.k + (double)p.n_shared * p.T;
+    const bool nt = rows * p.d * (dtype == 1 ? 2 : 4) > 256.0 * 1024 * 1024;
+    if (dtype == 1) {
+        if (nt)
+            hipLaunchKernelGGL((combine_kernel<true, true>), dim3(p.T), dim3(threads), 0, s, p);
+        else
+            hipLaunchKernelGGL((combine_kernel<true, false>), dim3(p.T), dim3(threads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((combine_kernel<false, false>), dim3(p.T), dim3(threads), 0, s, p);
+    }
     return hipGetLastError();
 }

@@ -107,12 +107,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     int part = 0;
     if (active) {
         int b = c0;
-        for (; b + 16 <= c1; b += 16) {
-            int v[16];
+        for (; b + 32 <= c1; b += 32) {
+            int v[32];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+            for (int u = 0; u < 32; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) part += v[u];
+            for (int u = 0; u < 32; ++u) part += v[u];
         }
         for (; b < c1; ++b) part += p.blk[(size_t)b * p.E + e];
         seg_i[seg * p.E + e] = part;
@@ -121,12 +121,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     if (active) {
         float ps = 0.0f;
         int b = seg;
-        for (; b + 15 * S < p.n_rtiles; b += 16 * S) {
-            float v[16];
+        for (; b + 31 * S < p.n_rtiles; b += 32 * S) {
+            float v[32];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
+            for (int u = 0; u < 32; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) ps += v[u];
+            for (int u = 0; u < 32; ++u) ps += v[u];
         }
         for (; b < p.n_rtiles; b += S) ps += p.p_part[(size_t)b * p.E + e];
         seg_f[seg * p.E + e] = ps;
@@ -147,18 +147,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     }
     __syncthreads();
     // 4. rank bases: the segment's base plus a running count over its
-    // chunks, 16 counts loaded before any base is written (one memory round
-    // trip per 16 chunks rather than per chunk)
+    // chunks, 32 counts loaded before any base is written (one memory round
+    // trip per 32 chunks rather than per chunk)
     if (active && p.n_chunks > 0) {
         int run = 0;
         for (int q = 0; q < seg; ++q) run += seg_i[q * p.E + e];
         int b = c0;
-        for (; b + 16 <= c1; b += 16) {
-            int v[16];
+        for (; b + 32 <= c1; b += 32) {
+            int v[32];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+            for (int u = 0; u < 32; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 p.blk[(size_t)(b + u) * p.E + e] = run;   // rank base in chunk b+u
                 run += v[u];
             }
