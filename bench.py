@@ -43,13 +43,17 @@ def parse():
     return ap.parse_args()
 
 
-GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_50_amd", "csrc",
-                           "gemm.hip")
+# the grouped-GEMM kernels and the headers they compile
+GEMM_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_50_amd", "csrc", f)
+                for f in ("gemm.hip", "common.h", "kernels.h")]
 
 
 def source_digest() -> str:
-    with open(GEMM_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
