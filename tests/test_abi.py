@@ -255,7 +255,7 @@ def _desc_of(w):
 # 256-row tiles with half-height tails; 15: four-wave 128-row tiles.
 PICKS = {
     "tiny_top2_f32": (4, 4),
-    "switch_top1_cap": (15, 15),
+    "switch_top1_cap": (2, 15),
     "mixtral_prefill": (14, 14),
     "mixtral_decode": (18, 18),
     "deepseek_v3": (13, 13),
