@@ -15,12 +15,23 @@
 // run of tiles, so the m-tiles that share one weight panel run on the same
 // XCD and hit its L2.
 //
-// bf16 kernel: BM x BN x 64 tiles, A and B staged through LDS (double
-// buffered, one barrier per k-step) with a 16-byte-chunk XOR swizzle that
-// keeps ds_read_b128 conflict-free; v_mfma_f32_32x32x16_bf16 with the
-// weight fragment as the MFMA A operand so each lane ends with 4
-// consecutive output features of one row (8-byte packed stores).  The A
-// operand of the up pass is gathered on load through slot_token[].
+// The kernels, by group size (the host picks one per GEMM, see the
+// variant ids in kernels.h):
+//   gemm_ring     groups of <= 16 rows (decode): weights through a
+//                 four-stage LDS ring in 1-2 KB row runs, non-temporal;
+//   gemm_stream   groups of <= 32 rows: weights straight into MFMA
+//                 fragments, K split over four waves;
+//   gemm_bf16_lds / _dma / _dma64   BM x BN x 64 tiles staged through LDS
+//                 (registers, or direct-to-LDS loads), 4 or 8 waves with
+//                 v_mfma_f32_32x32x16_bf16;
+//   gemm_bf16_w4  256 x 256 tiles, one wave per SIMD holding 128 x 128 in
+//                 256 accumulators (16x16x32 MFMAs issued in a fixed
+//                 order), half-height tiles for a group's last <= 128 rows,
+//                 optionally split over K;
+//   gemm_f32_simt the fp32 layer on the vector ALUs.
+// Common to the tiled kernels: 16-byte-chunk XOR swizzles that keep the
+// fragment reads conflict-free, the A operand of the up pass gathered on
+// load through slot_token[], bias and activation in the epilogue.
 #include "kernels.h"
 
 namespace {
