@@ -634,6 +634,29 @@ __device__ __forceinline__ void mfma_agpr(floatx4 &acc, const bf16x8 &a,
 }
 }  // namespace w4
 
+// bias[f0 + 16 b + t] (t < 4) of NB 16-column blocks into v[4 b + t], as
+// bf16 -> f32; zeros without a bias.  The 8-byte loads are issued together
+// under one uniform branch, so one wait covers them.
+template <int NB>
+__device__ __forceinline__ void load_bias4(const uint16_t *bias, int f0,
+                                           float *v) {
+    if (bias) {
+        u32x2 bb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bb[b] = *(const u32x2 *)(bias + f0 + 16 * b);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            v[4 * b + 0] = bf16_lo(bb[b].x);
+            v[4 * b + 1] = bf16_hi(bb[b].x);
+            v[4 * b + 2] = bf16_lo(bb[b].y);
+            v[4 * b + 3] = bf16_hi(bb[b].y);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4 * NB; ++b) v[b] = 0.0f;
+    }
+}
+
 // One tile.  Full: 256 rows, the waves 2 x 2 quarters of 128 x 128.  Half
 // (a tile of at most 128 rows, normally a group's last): the waves split
 // the 256 columns, 128 x 64 each, so the tile costs half the MFMAs and
@@ -658,7 +681,13 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     constexpr int NM = 8 * TN;                // MFMAs per sub-step
     constexpr int RD = HALF ? 2 : 3;          // a read after every RD MFMAs
     constexpr int DM = HALF ? 2 : 4;          // a load after every DM MFMAs
-    const int tid = threadIdx.x;
+    // The lane index is made opaque here, once per tile, so that the
+    // per-lane addresses below are recomputed for each tile instead of
+    // being hoisted out of the kernel's tile loop, where ~100 of them stay
+    // live across it and are spilled to scratch.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
     const int wm = HALF ? 0 : wave >> 1;
     const int wn = HALF ? wave : wave & 1;
     const int N = p.N, K = p.K;
@@ -819,19 +848,14 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         const uint16_t *b3 = routed
             ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
             : (const uint16_t *)p.bias_s3;
+        // 4 consecutive features per (c, jj): one 8-byte load each, all
+        // issued before the first use (no wait per element)
         float bv1[NC][2][4], bv3[NC][2][4];
+        const int fb = (n0 >> 1) + (WC / 2) * wn + cq;
+        load_bias4<NC * 2>(b1, fb, &bv1[0][0][0]);
+        load_bias4<NC * 2>(b3, fb, &bv3[0][0][0]);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int f = (n0 >> 1) + (WC / 2) * wn + 32 * c + 16 * jj + cq + t;
-                    bv1[c][jj][t] = b1 ? bf16_to_f32(b1[f]) : 0.0f;
-                    bv3[c][jj][t] = b3 ? bf16_to_f32(b3[f]) : 0.0f;
-                }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -845,6 +869,10 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                     }
                     put(i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
                 }
+            // one row block at a time: the accumulators are read as they
+            // are converted, not all at once
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         const uint16_t *bg = routed
             ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
@@ -853,23 +881,10 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         // those stay straight-line code
         const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
         float bv[TN][4];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WC + j * 16 + cq;
-            if (bg) {
-                const u32x2 bb = *(const u32x2 *)(bg + n);
-                bv[j][0] = bf16_lo(bb.x);
-                bv[j][1] = bf16_hi(bb.x);
-                bv[j][2] = bf16_lo(bb.y);
-                bv[j][3] = bf16_hi(bb.y);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) bv[j][t] = 0.0f;
-            }
-        }
+        load_bias4<TN>(bg, n0 + wn * WC + cq, &bv[0][0]);
         auto convert = [&](auto fn) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     float v[4];
@@ -877,6 +892,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                     for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
                     put(i * 16 + l16, wn * WC + j * 16 + cq, v);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
         if (act == ACT_GELU)
             convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
