@@ -1020,6 +1020,249 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------------
+// Two blocks per CU: 128 x 256 tiles, four waves of 128 x 64 (8 x 4
+// v_mfma_f32_16x16x32_bf16 blocks, 128 accumulators as AGPR operands, as in
+// the four-wave kernel).  With one wave per SIMD the four-wave kernel's
+// epilogue (bias, activation, bf16 conversion: ~6000 vector instructions a
+// wave and tile) and its tile prologue leave the matrix cores idle; here each
+// SIMD holds a wave of each of two independent blocks, so one block's
+// epilogue and load waits run under the other's MFMAs.  The price is half the
+// reuse per LDS byte, so the stages are 32 deep (64-byte row pieces) and the
+// LDS ring three slots of 24 KB (A 128 rows, B 256 rows), 72 KB a block.
+// Stage s+2 is requested when stage s is about to be used (two stages in
+// flight); a stage's fragments are read at the start of its own step, the
+// other block covering that latency.  Three statically named slot arrays
+// (three steps per loop trip) keep the compiler from seeing an alias between
+// the loads into one slot and the reads of another.
+namespace x2 {
+constexpr int BM = 128, BN = 256, SK = 32;   // stage depth SK
+constexpr int ROWB = SK * 2;                 // bytes of a row per stage
+constexpr int SLOT = (BM + BN) * ROWB;       // 24 KB
+constexpr int LA = BM / 16 / 4;              // A loads per wave and stage
+constexpr int LB = BN / 16 / 4;              // B loads per wave and stage
+}  // namespace x2
+
+template <bool UP>
+__device__ __forceinline__ void x2_tile(const GemmParams &p, char *s0,
+                                        char *s1, char *s2, int g, int row0,
+                                        int nrows, int n0, bool routed,
+                                        int wave) {
+    using namespace x2;
+    // opaque once per tile, so that the per-lane offsets are recomputed
+    // here instead of living across the tile loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int K = p.K, N = p.N, KT = K / SK;
+    const char *A = (const char *)p.A;
+    // Load j of a wave fills rows 16 (wave + 4 j) + lane/4 of an operand;
+    // position lane%4 of the row's 64 bytes receives k-chunk
+    // (lane%4) ^ (row/2 % 4) = (lane%4) ^ (lane/8 % 4).  With that swizzle
+    // the fragment reads (16 rows at one chunk) run without bank conflicts
+    // (measured: the swizzle by row/4 % 4, free of conflicts on a plain
+    // 64-bank model, costs every read a second pass on gfx950).
+    const int lr = lane >> 2;
+    const int ch = (lane & 3) ^ ((lane >> 3) & 3);
+    uint32_t a_off[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        int rr = 16 * (wave + 4 * j) + lr;
+        if (rr >= nrows) rr = 0;     // products land in rows never stored
+        const int slot = row0 + rr;
+        int src = slot;
+        if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+        a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
+    }
+    const char *bbase[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+        bbase[j] = weight_row(p, routed, g, n0 + 16 * (wave + 4 * j), 2);
+    const uint32_t b_lane = (uint32_t)(lr * K + ch * 8) * 2u;
+    auto dma = [&](int kt, char *slot) __attribute__((always_inline)) {
+        const size_t ko = (size_t)kt * SK * 2;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            w4::dma16b(A + ko + a_off[j], (u32x4 *)(slot + (wave + 4 * j) * 1024));
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            w4::dma16b(bbase[j] + ko + b_lane,
+                       (u32x4 *)(slot + BM * ROWB + (wave + 4 * j) * 1024));
+    };
+    const int l16 = lane & 15;
+    const int fpos = ((lane >> 4) ^ ((l16 >> 1) & 3)) * 16;
+    const int a_rd = l16 * ROWB + fpos;
+    const int b_rd = (BM + 64 * wave + l16) * ROWB + fpos;
+
+    floatx4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa[8], fb[4];
+
+    // every wave has read its staged outputs of the previous tile
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    dma(0, s0);
+    dma(min(1, KT - 1), s1);
+    // Step s: stage s landed (own loads, then everyone's), which also means
+    // every wave is past step s-1, so the slot of stage s-1 takes stage s+2;
+    // then stage s's fragments and its 32 MFMAs.  Loads past the end re-load
+    // the last stage into a slot that is no longer read.
+    auto step = [&](int s, const char *cur, char *nxt2) __attribute__((always_inline)) {
+        wait_vmcnt<LA + LB>();
+        __builtin_amdgcn_s_barrier();
+        dma(min(s + 2, KT - 1), nxt2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[j] = as_bf16x8(*(const u32x4 *)(cur + b_rd + j * 16 * ROWB));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            fa[i] = as_bf16x8(*(const u32x4 *)(cur + a_rd + i * 16 * ROWB));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w4::mfma_agpr(acc[i][j], fb[j], fa[i]);
+    };
+    // wait states of the asm MFMAs: before the first (a VALU write of its
+    // srcC) and after the last (a read of an 8-pass result)
+    // whole trips of three steps (a conditional step inside the trip makes
+    // the compiler lose track of which slot each load writes and wait for
+    // all of them), then the last KT % 3 steps
+    const int KT3 = KT - KT % 3;
+    int s = 0;
+    for (; s < KT3; s += 3) {
+        asm volatile("s_nop 4");
+        step(s, s0, s2);
+        step(s + 1, s1, s0);
+        step(s + 2, s2, s1);
+    }
+    if (s < KT) {
+        asm volatile("s_nop 4");
+        step(s, s0, s2);
+        if (s + 1 < KT) step(s + 1, s1, s0);
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+
+    // Epilogue: the re-loads have landed and every wave is done with the
+    // slots; each wave stages its own 128 x 64 outputs (128 x 32 gated) as
+    // bf16 in 16 KB of the slots, rows 0-63 and 64-127 in two 8 KB halves,
+    // 16-byte chunks XOR-swizzled by the row, and writes them back as whole
+    // row segments, with no block barrier between.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    const bool gated = UP && p.gated;
+    const int RS = gated ? 64 : 128;        // staged bytes per row
+    const int CPR = RS / 16;
+    const int SH = gated ? 2 : 1;           // rows per 256 bytes: 1 << SH
+    char *h0 = wave == 3 ? s0 + 16384 : (wave == 0 ? s0 : wave == 1 ? s1 : s2);
+    char *h1 = wave == 3 ? s1 + 16384 : h0 + 8192;
+    const int cq = 4 * (lane >> 4);
+    auto put = [&](int rl, int c, const float (&v)[4]) __attribute__((always_inline)) {
+        char *base = rl < 64 ? h0 : h1;
+        const int r = rl & 63;
+        const int sc = (c >> 3) ^ ((r >> SH) & (CPR - 1));
+        u32x2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *(u32x2 *)(base + r * RS + sc * 16 + ((c >> 2) & 1) * 8) = o;
+    };
+    if (gated) {
+        const int F = N >> 1;
+        const uint16_t *b1 = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const uint16_t *b3 = routed
+            ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s3;
+        float bv1[2][4], bv3[2][4];
+        const int fb0 = (n0 >> 1) + 32 * wave + cq;
+        load_bias4<2>(b1, fb0, &bv1[0][0]);
+        load_bias4<2>(b3, fb0, &bv3[0][0]);
+        // blocks 0, 1: gate rows, 2, 3: up rows of features 16 jj + ...
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                float h[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    h[t] = silu_f(acc[i][jj][t] + bv1[jj][t]) *
+                           (acc[i][2 + jj][t] + bv3[jj][t]);
+                put(i * 16 + l16, 16 * jj + cq, h);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
+        float bv[4][4];
+        load_bias4<4>(bg, n0 + 64 * wave + cq, &bv[0][0]);
+        auto convert = [&](auto fn) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
+                    put(i * 16 + l16, 16 * j + cq, v);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (act == ACT_GELU)
+            convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
+        else if (act == ACT_SILU)
+            convert([](float z) __attribute__((always_inline)) { return silu_f(z); });
+        else
+            convert([](float z) __attribute__((always_inline)) { return z; });
+    }
+    // the wave reads back only what it wrote: LDS keeps a wave's order
+    const int rpp = 64 / CPR;                 // rows per pass
+    const int rr = lane / CPR, cc = lane % CPR;
+    uint16_t *out = (uint16_t *)p.out + (gated ? (n0 >> 1) + 32 * wave : n0 + 64 * wave) + cc * 8;
+    for (int r0 = 0; r0 < BM; r0 += rpp) {
+        const int row = r0 + rr;
+        const char *base = row < 64 ? h0 : h1;
+        const int r = row & 63;
+        const u32x4 v = *(const u32x4 *)(base + r * RS + ((cc ^ ((r >> SH) & (CPR - 1))) * 16));
+        if (row < nrows) *(u32x4 *)(out + (size_t)(row0 + row) * p.ldo) = v;
+    }
+}
+
+template <bool UP>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_x2(GemmParams p) {
+    using namespace x2;
+    __shared__ __attribute__((aligned(16))) char slot0[SLOT], slot1[SLOT], slot2[SLOT];
+    __shared__ TileTable tt;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int NTN = p.N / BN;
+    const int G = p.E + p.n_shared;
+    build_tile_table(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T, BM, NTN);
+    const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
+    // XCD-aware order: the blocks of one XCD take consecutive tiles, which
+    // are the row tiles of one (group, 256-column) weight panel
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    for (int r = 0;; ++r) {
+        const int L = r * nb + xcd * per + loc;
+        if (L >= total) break;
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tt, G, L));
+        const int local = L - __builtin_amdgcn_readfirstlane(tt.base[g]);
+        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
+        const int n_tile = local / mt;
+        const int m_tile = local - n_tile * mt;
+        const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) + m_tile * BM;
+        const int nrows = min(BM, __builtin_amdgcn_readfirstlane(tt.rows[g]) - m_tile * BM);
+        x2_tile<UP>(p, slot0, slot1, slot2, g, row0, nrows, n_tile * BN,
+                    g < p.E, wave);
+    }
+}
+
 // Finishing the split tails: for each group whose last 1..128 rows ran as
 // split units, out[row] = epilogue(sum over ks in order of the fp32 partial
 // rows + bias), 8 outputs per thread and step.  Block (group, 128-column
@@ -1909,6 +2152,7 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
     case GEMM_BF16_W4_256x256: return {256, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_X2_128x256: return {128, 256, 256, 3 * 384 * 64};
     case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
     case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
     case GEMM_BF16_RING2_16x16: return {16, 16, 256, 4 * 16 * 1024};
@@ -1953,6 +2197,12 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_W4_128x256:
         return up ? launch_w4<true, 128>(p, grid, s)
                   : launch_w4<false, 128>(p, grid, s);
+    case GEMM_BF16_X2_128x256:
+        if (up)
+            hipLaunchKernelGGL(gemm_bf16_x2<true>, dim3(grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(gemm_bf16_x2<false>, dim3(grid), dim3(256), 0, s, p);
+        return hipGetLastError();
 
     case GEMM_BF16_RING_16x16:
         if (up)

@@ -82,6 +82,7 @@ enum GemmVariant {
     GEMM_FP8_RING_16x16 = 17,
     GEMM_BF16_RING2_16x16 = 18,    // 1 KB row runs, two blocks per CU
     GEMM_FP8_RING2_16x16 = 19,
+    GEMM_BF16_X2_128x256 = 20,     // two blocks per CU, 32-deep stages, K % 32 == 0
 };
 
 // Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),

@@ -239,6 +239,14 @@ bool w4_fits(const moe_desc *d, bool up) {
     return K >= 128 && K % 128 == 0 && rows * K * 2 < (1ll << 32);
 }
 
+// The two-block kernel walks K in 32-deep stages, with the same 32-bit A
+// offsets.
+bool x2_fits(const moe_desc *d, bool up) {
+    const long long K = up ? d->d : d->d_ff;
+    const long long rows = up ? d->T : routed_rows(d) + (long long)d->n_shared * d->T;
+    return K >= 32 && K % 32 == 0 && rows * K * 2 < (1ll << 32);
+}
+
 // The weight-ring kernels take K in stages of whole row runs and stage
 // the routed slots' token indices in LDS.
 bool ring_fits(const moe_desc *d, bool up, int variant) {
@@ -259,13 +267,14 @@ int variant_override(bool up, const moe_desc *d, int N) {
                         id == GEMM_FP8_RING_16x16 || id == GEMM_FP8_RING2_16x16;
     if (ring_variant(id) && !ring_fits(d, up, id)) return -1;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_FP8_RING2_16x16 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_X2_128x256 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
     if ((id == GEMM_BF16_W4_256x256 || id == GEMM_BF16_W4_128x256) &&
         !w4_fits(d, up))
         return -1;
+    if (id == GEMM_BF16_X2_128x256 && !x2_fits(d, up)) return -1;
     // the streaming kernels split K in four quarters of whole load batches
     // (4 x 32 deep for 32-column units, 2 x 32 for 64-column ones)
     if (id == GEMM_BF16_STREAM_32x64 && (d->d % 512 != 0 || d->d_ff % 512 != 0))

@@ -302,3 +302,13 @@ def test_gemm_variant_override_is_validated(monkeypatch):
     # the FP8 ring needs FP8 weights
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "17")
     assert moe.moe_gemm_variant(d, False) == 14
+    # the two-block kernel takes K in 32-deep stages
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "20")
+    assert moe.moe_gemm_variant(d, True) == 20
+    assert moe.moe_gemm_variant(_desc_of(w), True) == 20
+    # (K % 32 != 0: refused; no tile kernel takes such a K at all)
+    w3 = dataclasses.replace(workloads.WORKLOADS["mixtral_prefill"], d=4096 + 16)
+    try:
+        assert moe.moe_gemm_variant(_desc_of(w3), True) != 20
+    except moe.MoeError:
+        pass

@@ -61,7 +61,7 @@ def test_activation_small_full_parity(name):
 
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "5", "6", "8", "9", "11",
-                                     "13", "14", "15", "16"])
+                                     "13", "14", "15", "16", "20"])
 def test_swiglu_every_gate_capable_variant(variant, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", variant)
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", variant)

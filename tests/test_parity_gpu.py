@@ -69,7 +69,7 @@ def test_small_full_parity(name):
 
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7", "8",
-                                     "9", "11", "13", "14", "15", "16"])
+                                     "9", "11", "13", "14", "15", "16", "20"])
 def test_every_gemm_variant(variant, monkeypatch):
     """Each bf16 tile variant forced on a shape with groups of 0 to ~100
     rows (several row chunks for the small-tile kernels)."""
@@ -82,7 +82,7 @@ def test_every_gemm_variant(variant, monkeypatch):
     say(f"[variant {variant}] {rep}")
 
 
-@pytest.mark.parametrize("variant", ["13", "14", "15"])
+@pytest.mark.parametrize("variant", ["13", "14", "15", "20"])
 def test_large_tile_variants_multi_tile_groups(variant, monkeypatch):
     """The 320- and four-wave 256-row kernels on groups of ~600 rows (three
     row tiles, the last ragged), eight column tiles and 16 stages of K,
