@@ -31,9 +31,15 @@ namespace {
 constexpr int RT = MOE_ROUTER_TOKENS;
 constexpr int RW = 16;            // waves per router block
 
+// LG_PAD: the logit planes staged in LDS have rows of EP + 1 floats.  The
+// expert-choice score pass reads them token-minor (a column of 32 tokens at
+// one expert per 32 lanes), which with EP-float rows put every lane of a
+// column on one bank; the MFMA result writes (two token rows 4 apart per
+// instruction) and the one-lane-per-token reads of the small-E path share
+// banks the same way.
 // Softmax + top-k phase over logits staged in LDS (KS partial planes).
 template <int EP, int KS>
-__device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP],
+__device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP + 1],
                                              const RouterParams &p,
                                              float (*pp)[EP]) {
     static_assert(RT % RW == 0, "tokens per wave");
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
 // renormalised (the softmax denominator cancels).  lg: the block's summed
 // logits; addv / subv: the router and balancing biases (0 where absent).
 template <int EP>
-__device__ __forceinline__ void route_lanes(const float (*lg)[EP],
+__device__ __forceinline__ void route_lanes(const float (*lg)[EP + 1],
                                             const RouterParams &p,
                                             const float *addv,
                                             const float *subv,
@@ -465,7 +471,7 @@ __device__ __forceinline__ void route_lanes(const float (*lg)[EP],
 template <int EP>
 __global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterParams p) {
     constexpr bool SMALL = EP <= 32;
-    __shared__ float lg[1][RT][EP];
+    __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
     __shared__ float pp[SMALL ? 1 : RW][EP];
     __shared__ float pr[SMALL ? RT : 1][EP + 1];
     __shared__ float zh[RT][2];
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(RW * 64) void router_fused(RouterParams p) {
     constexpr int NTE = EP / 32;                  // 32-expert tiles
     constexpr int KS = NTE >= RW ? 1 : RW / NTE;  // k-splits across waves
     constexpr int TPW = NTE >= RW ? NTE / RW : 1; // tiles per wave
-    __shared__ float lg[KS][RT][EP];
+    __shared__ float lg[KS][RT][EP + 1];  // rows of EP + 1 floats (LG_PAD)
     __shared__ float pp[RW][EP];
 
     const int lane = threadIdx.x & 63;
@@ -577,7 +583,7 @@ __global__ __launch_bounds__(RW * 64) void router_fused(RouterParams p) {
 // fp32 logits with plain FMA (sequential over d).
 template <int EP>
 __global__ __launch_bounds__(RW * 64) void router_f32(RouterParams p) {
-    __shared__ float lg[1][RT][EP];
+    __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
     __shared__ float pp[RW][EP];
     const int t0 = blockIdx.x * RT;
     const float *x = (const float *)p.x;
