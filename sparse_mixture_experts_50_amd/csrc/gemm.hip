@@ -1649,9 +1649,10 @@ __global__ __launch_bounds__(256, 2) void gemm_stream(GemmParams p) {
 // (past the last stage they re-read one line), so the waits are fixed
 // counts.  The four waves split each stage's k range in quarters; a unit's
 // partial sums are added through LDS (the slot its last stage leaves) in a
-// fixed order.  Each LDS row of a stage is padded by one 16-byte chunk, so
-// that the fragment reads (16 rows, one chunk) fall in distinct bank groups
-// while every sub-step's read is at a fixed offset from one address.
+// fixed order.  Each LDS row of a stage is padded by four 16-byte chunks
+// and its chunks XOR-swizzled by the row, so that the fragment reads (16
+// rows, one chunk) fall in distinct bank groups while every sub-step's
+// read is at a fixed offset from one address.
 namespace ring {
 constexpr int MAXTOK = MOE_RING_MAXTOK;
 
@@ -1671,7 +1672,11 @@ __device__ __forceinline__ void dma4(const char *src, u32x4 *lds) {
 template <bool UP, bool FP8, int CB, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_ring(GemmParams p) {
     constexpr int CPR = CB / 16;          // 16-byte chunks of a row per stage
-    constexpr int RS = CPR + 1;           // LDS row stride (chunks)
+    // LDS rows of CPR + 4 chunks, and chunk c of row r at c ^ ((r / 2) % 4)
+    // (low two bits): the fragment reads (16 rows at one chunk) then run
+    // without bank conflicts on gfx950, which rows padded by one chunk did
+    // not (two passes a read, rocprof counters)
+    constexpr int RS = CPR + 4;           // LDS row stride (chunks)
     constexpr int CPS = 16 * RS;          // chunks per stage
     constexpr int EPI = 32;               // epilogue chunks per slot
     constexpr int NI = CB / 256;          // 1 KB weight loads per wave
@@ -1794,11 +1799,13 @@ __global__ __launch_bounds__(256, OCC) void gemm_ring(GemmParams p) {
         ring::dma4(e0, ep);
         ring::dma4(e1, ep + 16);
         const char *wb = wr[RG] + (size_t)ikc * CB + 4 * wave * rowb;
-        const uint32_t loff = (uint32_t)lane * 16 * (uint32_t)real;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            // 1 KB of row 4 wave + jr (half h of a 2 KB run)
+            // 1 KB of row 4 wave + jr (half h of a 2 KB run); the lane
+            // fetches the chunk that the row's swizzle puts at its position
             const int jr = NI == 8 ? j >> 1 : j, h = NI == 8 ? (j & 1) : 0;
+            const int sw = ((4 * wave + jr) >> 1) & 3;
+            const uint32_t loff = (uint32_t)(lane ^ sw) * 16 * (uint32_t)real;
             ring::dma16nt(wb + jr * rowb + h * 1024 + loff,
                           slot + (4 * wave + jr) * RS + h * 64);
         }
@@ -1898,7 +1905,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_ring(GemmParams p) {
 
     auto compute = [&](auto rgc, const u32x4 *slot, const u32x4 (&ab)[NA]) __attribute__((always_inline)) {
         constexpr int RG = decltype(rgc)::value;
-        const u32x4 *brow = slot + l16 * RS + (CPR / 4) * wave + q;
+        const u32x4 *brow = slot + l16 * RS + (CPR / 4) * wave + (q ^ ((l16 >> 1) & 3));
 #pragma unroll
         for (int s = 0; s < SS; ++s) {
             // this lane's 16 weight bytes: row l16, chunk 4 s + q of the
