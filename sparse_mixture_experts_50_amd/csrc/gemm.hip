@@ -666,21 +666,27 @@ __device__ __forceinline__ void load_bias4(const uint16_t *bias, int f0,
 // loads of the stage after next spread over the MFMAs.
 // PART: write the fp32 sums over stages kt0 .. kt0 + KT - 1 to the tail
 // partial buffer (plane ks) instead of finishing the tile.
-template <bool UP, bool HALF, bool PART>
+// WR: rows of a wave's part of a full tile, 128 (256-row tiles) or 112
+// (224-row tiles of evenly split groups: seven MFMA row blocks a wave).
+template <bool UP, bool HALF, bool PART, int WR = 128>
 __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                                         u32x4 *slot1, int g, int row0,
                                         int nrows, int n0, bool routed,
                                         int wave, int lane, int kt0, int KT,
                                         int ks) {
     using namespace w4;
+    static_assert(WR == 128 || (WR == 112 && !HALF), "wave rows");
     constexpr int TN = HALF ? 4 : 8;          // 16-column blocks per wave
     constexpr int WC = HALF ? 64 : 128;       // columns per wave
-    constexpr int LA = HALF ? LPW / 2 : LPW;  // A loads per wave and stage
+    constexpr int RB = HALF ? 8 : WR / 16;    // 16-row blocks per wave
+    constexpr int TR = HALF ? 128 : 2 * WR;   // tile rows
+    constexpr int LA = TR / 32;               // A loads per wave and stage
     constexpr int NL = LA + LPW;              // loads per wave and stage
-    constexpr int NF = 8 + TN;                // fragment reads per sub-step
-    constexpr int NM = 8 * TN;                // MFMAs per sub-step
+    constexpr int NF = RB + TN;               // fragment reads per sub-step
+    constexpr int NM = RB * TN;               // MFMAs per sub-step
     constexpr int RD = HALF ? 2 : 3;          // a read after every RD MFMAs
-    constexpr int DM = HALF ? 2 : 4;          // a load after every DM MFMAs
+    constexpr int DM = HALF ? 2 : WR == 128 ? 4 : 3;  // a load after every DM MFMAs
+    static_assert(RD * (NF - 1) < NM && DM * (NL - 1) + 1 < NM, "issue slots");
     // The lane index is made opaque here, once per tile, so that the
     // per-lane addresses below are recomputed for each tile instead of
     // being hoisted out of the kernel's tile loop, where ~100 of them stay
@@ -729,22 +735,22 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                    st + BM * CPR + (wave + 4 * (q - LA)) * 64);
     };
     // fragment q (q < 8: A block q, else B block q - 8), sub-step kk
-    auto frag_one = [&](bf16x8 (&fa)[8], bf16x8 (&fb)[TN], const u32x4 *st,
+    auto frag_one = [&](bf16x8 (&fa)[RB], bf16x8 (&fb)[TN], const u32x4 *st,
                         int kk, int q) __attribute__((always_inline)) {
         const int c = (kk * 4 + (lane >> 4)) ^ sw;
-        if (q < 8)
-            fa[q] = as_bf16x8(st[(wm * 128 + q * 16 + l16) * CPR + c]);
+        if (q < RB)
+            fa[q] = as_bf16x8(st[(wm * WR + q * 16 + l16) * CPR + c]);
         else
-            fb[q - 8] = as_bf16x8(
-                st[BM * CPR + (wn * WC + (q - 8) * 16 + l16) * CPR + c]);
+            fb[q - RB] = as_bf16x8(
+                st[BM * CPR + (wn * WC + (q - RB) * 16 + l16) * CPR + c]);
     };
 
-    floatx4 acc[8][TN];
+    floatx4 acc[RB][TN];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 fa0[8], fb0[TN], fa1[8], fb1[TN];
+    bf16x8 fa0[RB], fb0[TN], fa1[RB], fb1[TN];
 
     // every wave is done with both slots (previous tile) before the first
     // loads of this one
@@ -802,7 +808,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         float *dst = p.part + ((size_t)ks * G + g) * 128 * N;
         __builtin_amdgcn_s_waitcnt(0);   // re-loads landed before the next tile
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RB; ++i) {
             const int r = i * 16 + l16;
             if (r >= nrows) continue;
 #pragma unroll
@@ -825,10 +831,12 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     // segments with 16-byte stores.
     __builtin_amdgcn_s_waitcnt(0);   // re-loads landed, own reads done
     __builtin_amdgcn_s_barrier();    // and every wave's
-    char *stg = (char *)(wm ? slot1 : slot0);
     const int cq = 4 * (lane >> 4);
-    // 4 values at staging row rl (0..127), output column c (c % 4 == 0)
-    auto put = [&](int rl, int c, const float (&v)[4]) __attribute__((always_inline)) {
+    // 4 values at tile row R (0..TR-1), output column c (c % 4 == 0); R < 128
+    // is uniform for a row block, so the slot choice is too
+    auto put = [&](int R, int c, const float (&v)[4]) __attribute__((always_inline)) {
+        char *stg = (char *)(R < 128 ? slot0 : slot1);
+        const int rl = R & 127;
         const int sc = (c >> 3) ^ (rl & 15);
         u32x2 o;
         o.x = pack_bf16x2(v[0], v[1]);
@@ -855,7 +863,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         load_bias4<NC * 2>(b1, fb, &bv1[0][0][0]);
         load_bias4<NC * 2>(b3, fb, &bv3[0][0][0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RB; ++i) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -867,7 +875,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                         const float uv = acc[i][4 * c + 2 + jj][t] + bv3[c][jj][t];
                         h[t] = silu_f(gv) * uv;
                     }
-                    put(i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
+                    put(wm * WR + i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
                 }
             // one row block at a time: the accumulators are read as they
             // are converted, not all at once
@@ -884,13 +892,13 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         load_bias4<TN>(bg, n0 + wn * WC + cq, &bv[0][0]);
         auto convert = [&](auto fn) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < RB; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
-                    put(i * 16 + l16, wn * WC + j * 16 + cq, v);
+                    put(wm * WR + i * 16 + l16, wn * WC + j * 16 + cq, v);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -909,7 +917,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     const int rpp = 256 / cpr;                 // rows per block pass
     const int rr = tid / cpr, cc = tid % cpr;
     uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
-    for (int r0 = 0; r0 < (HALF ? 128 : BM); r0 += rpp) {
+    for (int r0 = 0; r0 < TR; r0 += rpp) {
         const int row = r0 + rr;
         if (row < nrows) {
             const char *sb = (const char *)(row < 128 ? slot0 : slot1);
@@ -930,6 +938,18 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
 // stay in group order, where the half tiles spread over the last round
 // (the Mixtral down GEMM's 2.25 rounds: 5 % faster that way).
 // TM_ROWS = 128: every tile half-height (for groups of up to ~128 rows).
+// Even split (TM_ROWS = 256, tails not split over K): a group whose last
+// 256-row block would hold 1..128 rows and that needs m >= 3 tiles, if m
+// tiles of 224 rows hold it, runs as those m tiles instead.  The m tiles
+// take the same time, so all of a weight panel's row tiles run side by
+// side and share it through L2; the half tiles instead come after every
+// full tile, and by then their panels have left L2 (the Mixtral up GEMM
+// fetched ~0.9 GB more than its weights and rows for them).
+__device__ __forceinline__ bool w4_even_group(int rows) {
+    const int m = (rows + 255) >> 8, rem = rows & 255;
+    return m >= 3 && rem >= 1 && rem <= 128 && m * 224 >= rows;
+}
+
 template <bool UP, int TM_ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     using namespace w4;
@@ -945,13 +965,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
                          128, NTN);
     } else {
         // full-height tiles: whole 256-row blocks and a last block of more
-        // than 128 rows; half tiles: a last block of 1..128 rows
+        // than 128 rows (or an evenly split group's 224-row tiles); half
+        // tiles: a last block of 1..128 rows
+        const bool ev = p.tail_split <= 1;
         build_tile_table_by(tf, p.offsets, p.E, p.n_shared, p.shared_base,
-                            p.T, NTN, [](int rows) {
+                            p.T, NTN, [ev](int rows) {
+                                if (ev && w4_even_group(rows)) return (rows + 255) >> 8;
                                 return (rows >> 8) + ((rows & 255) > 128);
                             });
         build_tile_table_by(th, p.offsets, p.E, p.n_shared, p.shared_base,
-                            p.T, NTN, [](int rows) {
+                            p.T, NTN, [ev](int rows) {
+                                if (ev && w4_even_group(rows)) return 0;
                                 const int rem = rows & 255;
                                 return rem > 0 && rem <= 128 ? 1 : 0;
                             });
@@ -1001,10 +1025,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
             m_tile = first ? local - n_tile * mt
                            : __builtin_amdgcn_readfirstlane(tf.mt[g]);
         }
-        const int row0 = __builtin_amdgcn_readfirstlane(tf.start[g]) +
-                         m_tile * TM_ROWS;
-        const int nrows = min(TM_ROWS, __builtin_amdgcn_readfirstlane(tf.rows[g]) -
-                                           m_tile * TM_ROWS);
+        const int grows = __builtin_amdgcn_readfirstlane(tf.rows[g]);
+        const int tm = TM_ROWS == 256 && S == 1 && w4_even_group(grows) ? 224 : TM_ROWS;
+        const int row0 = __builtin_amdgcn_readfirstlane(tf.start[g]) + m_tile * tm;
+        const int nrows = min(tm, grows - m_tile * tm);
         const int n0 = n_tile * BN;
         const bool routed = g < p.E;
         if (S > 1 && L >= total_f)
@@ -1014,6 +1038,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         else if (TM_ROWS == 128 || nrows <= 128)
             w4_tile<UP, true, false>(p, slot0, slot1, g, row0, nrows, n0,
                                      routed, wave, lane, 0, KT, 0);
+        else if (tm == 224)
+            w4_tile<UP, false, false, 112>(p, slot0, slot1, g, row0, nrows, n0,
+                                           routed, wave, lane, 0, KT, 0);
         else
             w4_tile<UP, false, false>(p, slot0, slot1, g, row0, nrows, n0,
                                       routed, wave, lane, 0, KT, 0);
