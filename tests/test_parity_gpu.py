@@ -18,8 +18,8 @@ import sparse_mixture_experts_50_amd as moe
 import workloads
 from workloads import scaled
 
-from parity import (check_layer, device, gpu_forward, inputs_on,
-                    sample_tokens)
+from parity import (check_expert_choice, check_layer, device, gpu_forward,
+                    inputs_on, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -251,3 +251,21 @@ def test_zero_tokens():
     y, r = layer.forward(inp["x"][:0])
     torch.cuda.synchronize()
     assert y.shape == (0, 256)
+
+
+@pytest.mark.parametrize("C", [513, 640, 700, 257])
+def test_four_wave_even_split_group_sizes(C, monkeypatch):
+    """Expert-Choice routing gives every expert exactly C rows.  Without
+    split tails, 513 and 640 rows run as three 224-row tiles (the last of
+    65 / 192 rows); 700 rows (a 188-row last block) and 257 rows (two
+    tiles) keep 256-row and half-height tiles."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+    monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
+    w = scaled(W["expert_choice_c2"], T=2 * C, d=256, E=2, k=2, d_ff=512,
+               capacity_factor=1.0)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    # (expert choice: every expert keeps exactly C rows)
+    assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
+    say(f"[even split C={C}] {check_expert_choice(w, inp, gpu)}")
