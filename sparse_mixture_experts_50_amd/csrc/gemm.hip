@@ -27,11 +27,16 @@
 //   gemm_bf16_w4  256 x 256 tiles, one wave per SIMD holding 128 x 128 in
 //                 256 accumulators (16x16x32 MFMAs issued in a fixed
 //                 order), half-height tiles for a group's last <= 128 rows,
-//                 optionally split over K;
+//                 optionally split over K, or 224-row tiles for groups
+//                 split evenly;
+//   gemm_bf16_x2  128 x 256 tiles, two blocks per CU (selectable only:
+//                 slower than gemm_bf16_w4 on every measured shape);
 //   gemm_f32_simt the fp32 layer on the vector ALUs.
 // Common to the tiled kernels: 16-byte-chunk XOR swizzles that keep the
-// fragment reads conflict-free, the A operand of the up pass gathered on
-// load through slot_token[], bias and activation in the epilogue.
+// fragment reads free of bank conflicts (checked with rocprof's LDS
+// conflict counter on gfx950, whose ds_read_b128 passes do not follow a
+// plain 64-bank model), the A operand of the up pass gathered on load
+// through slot_token[], bias and activation in the epilogue.
 #include "kernels.h"
 
 namespace {
@@ -862,25 +867,35 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         const int fb = (n0 >> 1) + (WC / 2) * wn + cq;
         load_bias4<NC * 2>(b1, fb, &bv1[0][0][0]);
         load_bias4<NC * 2>(b3, fb, &bv3[0][0][0]);
+        // BIAS is a compile-time flag: x + 0.0f is not folded away
+        auto swiglu = [&](auto bias) __attribute__((always_inline)) {
+            constexpr bool BIAS = decltype(bias)::value;
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
+            for (int i = 0; i < RB; ++i) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
+                for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    float h[4];
+                    for (int jj = 0; jj < 2; ++jj) {
+                        float h[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float gv = acc[i][4 * c + jj][t] + bv1[c][jj][t];
-                        const float uv = acc[i][4 * c + 2 + jj][t] + bv3[c][jj][t];
-                        h[t] = silu_f(gv) * uv;
+                        for (int t = 0; t < 4; ++t) {
+                            float gv = acc[i][4 * c + jj][t];
+                            float uv = acc[i][4 * c + 2 + jj][t];
+                            if (BIAS) {
+                                gv += bv1[c][jj][t];
+                                uv += bv3[c][jj][t];
+                            }
+                            h[t] = silu_f(gv) * uv;
+                        }
+                        put(wm * WR + i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
                     }
-                    put(wm * WR + i * 16 + l16, (WC / 2) * wn + 32 * c + 16 * jj + cq, h);
-                }
-            // one row block at a time: the accumulators are read as they
-            // are converted, not all at once
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                // one row block at a time: the accumulators are read as they
+                // are converted, not all at once
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (b1 || b3) swiglu(std::true_type{});
+        else swiglu(std::false_type{});
     } else {
         const uint16_t *bg = routed
             ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
@@ -890,25 +905,34 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
         float bv[TN][4];
         load_bias4<TN>(bg, n0 + wn * WC + cq, &bv[0][0]);
-        auto convert = [&](auto fn) __attribute__((always_inline)) {
+        // BIAS is a compile-time flag: x + 0.0f is not folded away
+        auto convert = [&](auto fn, auto bias) __attribute__((always_inline)) {
+            constexpr bool BIAS = decltype(bias)::value;
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     float v[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = fn(acc[i][j][t] + bv[j][t]);
+                    for (int t = 0; t < 4; ++t)
+                        v[t] = fn(BIAS ? acc[i][j][t] + bv[j][t] : acc[i][j][t]);
                     put(wm * WR + i * 16 + l16, wn * WC + j * 16 + cq, v);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if (act == ACT_GELU)
-            convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); });
-        else if (act == ACT_SILU)
-            convert([](float z) __attribute__((always_inline)) { return silu_f(z); });
-        else
-            convert([](float z) __attribute__((always_inline)) { return z; });
+        auto with_act = [&](auto bias) __attribute__((always_inline)) {
+            if (act == ACT_GELU)
+                convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); }, bias);
+            else if (act == ACT_SILU)
+                convert([](float z) __attribute__((always_inline)) { return silu_f(z); }, bias);
+            else
+                convert([](float z) __attribute__((always_inline)) { return z; }, bias);
+        };
+        // (only for the up GEMM: in the down GEMM's epilogue the second
+        // copy made the compiler spill)
+        if (!UP || bg) with_act(std::true_type{});
+        else with_act(std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
