@@ -146,12 +146,21 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         }
     }
     __syncthreads();
+    // 4a. inclusive scan of the segment counts over the segments, per
+    // expert: log2(S) steps through LDS instead of a loop over up to S - 1
+    // earlier segments per thread (S = 128 at E = 8)
+    for (int d = 1; d < S; d <<= 1) {
+        int v = 0;
+        if (active && seg >= d) v = seg_i[(seg - d) * p.E + e];
+        __syncthreads();
+        if (active) seg_i[seg * p.E + e] += v;
+        __syncthreads();
+    }
     // 4. rank bases: the segment's base plus a running count over its
     // chunks, 32 counts loaded before any base is written (one memory round
     // trip per 32 chunks rather than per chunk)
     if (active && p.n_chunks > 0) {
-        int run = 0;
-        for (int q = 0; q < seg; ++q) run += seg_i[q * p.E + e];
+        int run = seg_i[seg * p.E + e] - part;   // earlier segments' counts
         int b = c0;
         for (; b + 32 <= c1; b += 32) {
             int v[32];
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         if (p.scores) {
             cnt = p.T;                    // expert choice: every token
         } else {
-            for (int q = 0; q < S; ++q) cnt += seg_i[q * p.E + tid];
+            cnt = seg_i[(S - 1) * p.E + tid];   // inclusive over every segment
         }
         float ps = 0.0f;
         for (int q = 0; q < S; ++q) ps += seg_f[q * p.E + tid];
