@@ -724,3 +724,111 @@ def test_swiglu_shared_expert_and_fp8_up_projection():
                   deq(inp["ws2"], inp["ws2_scale"]), None,
                   deq(inp["ws3"], inp["ws3_scale"]), None, "swiglu")
     assert np.allclose(out["y"], ref, rtol=1e-10, atol=1e-10)
+
+
+# ---------------------------------------------- selection-conditioned path
+# A checker that adopts the GPU's choice at a near-tie re-runs the layer on
+# a given selection: the weights are then the renormalised probabilities of
+# the chosen experts ("MoE architecture deep dive", sec. 1.3 steps 2-3) and
+# everything after is the ordinary dispatch, FFN and combine.
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 9).flatmap(lambda E: st.tuples(
+    st.just(E), st.integers(1, E),
+    st.lists(st.integers(1, 6), min_size=E, max_size=E))))
+def test_renorm_selection_of_own_topk_is_topk_weights(args):
+    E, k, ints = args
+    p = np.array(ints, np.float64) / 64.0
+    idx, w, _ = oracle.topk(p[None, :], k)
+    assert np.array_equal(oracle.renorm_selection(p[None, :], idx), w)
+
+
+def test_renorm_selection_golden_figure_and_non_top_pairs():
+    g = golden("renorm_figure")
+    p = np.array(g["probs"], np.float64)[None, :]
+    # the figure's pair, in either order: the weights follow the selection
+    w = oracle.renorm_selection(p, np.array([g["topk_idx"]], np.int32))
+    assert np.allclose(w[0], g["topk_w"], rtol=1e-15, atol=1e-15)
+    w = oracle.renorm_selection(p, np.array([[5, 1]], np.int32))
+    assert np.allclose(w[0], [0.4, 0.6], rtol=1e-15, atol=1e-15)
+    # a pair that is not the top-2: renormalised over the chosen two only
+    # (dividing by the sum over all E would give 0.1 each)
+    w = oracle.renorm_selection(p, np.array([[0, 2]], np.int32))
+    assert np.array_equal(w[0], [0.5, 0.5])
+    w = oracle.renorm_selection(p, np.array([[2, 6]], np.int32))
+    assert np.allclose(w[0], [2 / 3, 1 / 3], rtol=1e-15)
+    # one expert: weight 1 whatever its probability
+    w = oracle.renorm_selection(p, np.array([[7]], np.int32))
+    assert w[0, 0] == 1.0
+
+
+def test_forward_with_own_selection_is_bit_equal():
+    for cf in (None, 0.75):
+        w, inp = tiny_inputs(E=5, T=40)
+        a = oracle.forward(inp, k=2, capacity_factor=cf)
+        b = oracle.forward(inp, k=2, capacity_factor=cf,
+                           selection=a["topk_idx"])
+        for key in ("topk_idx", "topk_w", "counts", "kept", "offsets",
+                    "slot_token", "slot_of", "f", "p", "y"):
+            assert np.array_equal(a[key], b[key]), (cf, key)
+        assert a["l_aux"] == b["l_aux"]
+
+
+def test_forward_with_foreign_selection_follows_definition():
+    # Every token takes experts (t mod E, (t + 2) mod E), mostly not its own
+    # top-2: y_t = sum_j p_sel_j / (sum p_sel) * FFN_sel_j(x_t) by torch's
+    # float64 Linear -> GELU -> Linear, and the counts follow the selection.
+    E, T = 5, 30
+    w, inp = tiny_inputs(E=E, T=T)
+    sel = np.stack([np.arange(T) % E, (np.arange(T) + 2) % E], 1).astype(
+        np.int32)
+    out = oracle.forward(inp, k=2, selection=sel)
+    logits = torch.nn.functional.linear(inp["x"].double(),
+                                        inp["wr"].double(),
+                                        inp["br"].double())
+    p = torch.softmax(logits, -1).numpy()
+    assert np.array_equal(out["counts"], np.bincount(sel.ravel(),
+                                                     minlength=E))
+    for t in range(T):
+        ps = p[t, sel[t]]
+        ref = 0
+        for j in range(2):
+            e = sel[t, j]
+            ref = ref + ps[j] / ps.sum() * dense_ffn_torch(
+                inp["x"][t:t + 1], inp["w1"][e], inp["b1"][e], inp["w2"][e],
+                inp["b2"][e])[0]
+        assert np.allclose(out["topk_w"][t], ps / ps.sum(), rtol=1e-13)
+        assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_expert_choice_with_own_selection_is_bit_equal():
+    w, inp = tiny_inputs(E=4, T=24)
+    a = oracle.forward_expert_choice(inp, capacity=5)
+    b = oracle.forward_expert_choice(inp, capacity=5,
+                                     selection=a["slot_token"])
+    for key in ("slot_token", "slot_of", "gate", "picks", "y"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_expert_choice_with_foreign_selection_follows_definition():
+    # Expert e picks tokens e, e+4, e+8 (ascending): y_t sums p[t,e] *
+    # FFN_e(x_t) over the experts that picked t, unrenormalised.
+    E, T, C = 4, 20, 3
+    w, inp = tiny_inputs(E=E, T=T)
+    sel = np.concatenate([np.arange(C) * E + e for e in range(E)]).astype(
+        np.int32)
+    out = oracle.forward_expert_choice(inp, capacity=C, selection=sel)
+    logits = torch.nn.functional.linear(inp["x"].double(),
+                                        inp["wr"].double(),
+                                        inp["br"].double())
+    p = torch.softmax(logits, -1).numpy()
+    ref = np.zeros((T, inp["x"].shape[1]))
+    for e in range(E):
+        toks = sel[e * C:(e + 1) * C]
+        ref[toks] += p[toks, e:e + 1] * dense_ffn_torch(
+            inp["x"][toks], inp["w1"][e], inp["b1"][e], inp["w2"][e],
+            inp["b2"][e])
+        for r, t in enumerate(toks):
+            assert out["slot_of"][t, e] == e * C + r
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(out["picks"], (np.arange(T) < E * C).astype(
+        np.int32))
