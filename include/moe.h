@@ -49,10 +49,22 @@
  *   - Pointers named in the structs and arguments are DEVICE pointers unless
  *     stated otherwise; arrays are row-major and contiguous.
  *   - The caller owns every buffer, including the workspace sized by
- *     moe_workspace_size().  The library allocates nothing, keeps no state
- *     between calls, and only enqueues work on `stream` (a hipStream_t;
- *     NULL is the default stream).  No call synchronises the device or
- *     reads device data back to the host.
+ *     moe_workspace_size().  The library allocates nothing and only
+ *     enqueues work on `stream` (a hipStream_t; NULL is the default
+ *     stream).  No call synchronises the device or reads device data back
+ *     to the host.  The one piece of state kept between calls is a
+ *     per-device cache of the compute-unit count (filled on first use,
+ *     atomically, with a value that never changes).
+ *   - Tuning variables.  The environment variables MOE_ROUTER_SPLIT (0 / 1:
+ *     fused or split bf16 router), MOE_TAIL_SPLIT (1..8: cap of the
+ *     four-wave GEMM's K split of half-height tiles) and
+ *     MOE_GEMM_VARIANT_UP / MOE_GEMM_VARIANT_DOWN (a tile variant id,
+ *     used only where valid for the shape) are read at every call.  The
+ *     first two change the workspace layout, so they are part of the
+ *     workspace contract: keep them unchanged between moe_workspace_size()
+ *     and the calls that use that workspace (a call whose workspace is then
+ *     too small returns MOE_ERR_WORKSPACE).  Unset, every choice is a
+ *     function of the descriptor and the device.
  *   - Arguments are validated on the host before any HIP call; a failed
  *     check returns a negative moe_status and enqueues nothing.  A failed
  *     kernel launch returns MOE_ERR_HIP.  T == 0 is valid: once the
@@ -205,8 +217,9 @@ int32_t moe_capacity(int32_t T, int32_t E, double cf);
 
 /* Host.  Bytes of workspace the calls below need for this shape, or 0 if
  * the descriptor is invalid; a function of the descriptor alone (and of the
- * MOE_ROUTER_SPLIT tuning variable, when set; a call whose workspace is
- * then too small returns MOE_ERR_WORKSPACE).  One workspace serves every entry point;
+ * MOE_ROUTER_SPLIT and MOE_TAIL_SPLIT tuning variables, when set; a call
+ * whose workspace is then too small returns MOE_ERR_WORKSPACE).  One
+ * workspace serves every entry point;
  * moe_router_topk writes router partial sums into it that moe_permute reads,
  * and moe_grouped_ffn writes the expert outputs that moe_combine reads, so
  * run a sequence of calls with one workspace. */
@@ -218,6 +231,14 @@ size_t moe_workspace_size(const moe_desc *desc);
  * status if the descriptor is invalid.  Depends on the descriptor, the
  * device's CU count and the MOE_GEMM_VARIANT_UP / _DOWN tuning variables. */
 int moe_gemm_variant(const moe_desc *desc, int up);
+
+/* Host.  Number of K ranges S the four-wave 256-row grouped GEMM splits
+ * each half-height (last <= 128 rows of a group) tile into for moe_ffn_up
+ * (up != 0) or moe_ffn_down: 1 when there is no split or another variant
+ * runs, else 2..8 with (K / 64) divisible by 2 S, so every unit covers a
+ * whole number of 64-deep stage pairs.  A negative status if the
+ * descriptor is invalid.  For diagnostics and tests. */
+int moe_gemm_tail_split(const moe_desc *desc, int up);
 
 /* Router GEMM with bias, softmax, top-k and renormalisation (layer steps
  * 1-2); bf16 layers run it as one kernel or, for deep or few-token shapes,

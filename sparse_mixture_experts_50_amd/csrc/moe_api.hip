@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -128,14 +130,16 @@ int tail_split(const moe_desc *d, bool up) {
     if (H < 1.0) return 1;
     int S = (int)floor(256.0 / H);
     if (S > 8) S = 8;
-    while (S > 1 && (K / 64) % (2 * S) != 0) --S;   // whole stage pairs
-    if (S > 1 && (double)S * (d->E + d->n_shared) * 128.0 * N * 4.0 > 512e6)
-        S = 1;
     // tuning and test knob: MOE_TAIL_SPLIT=1..8 caps the split (1: none);
-    // read here, so the workspace size follows it
+    // read here, so the workspace size follows it.  The cap comes first:
+    // the unit ranges below must still be whole stage pairs.
     const char *v = getenv("MOE_TAIL_SPLIT");
     if (v && v[0] >= '1' && v[0] <= '8' && v[1] == 0 && S > v[0] - '0')
         S = v[0] - '0';
+    // each unit walks KT / S 64-deep stages, two per loop trip
+    while (S > 1 && (K / 64) % (2 * S) != 0) --S;
+    if (S > 1 && (double)S * (d->E + d->n_shared) * 128.0 * N * 4.0 > 512e6)
+        S = 1;
     return S;
 }
 
@@ -205,18 +209,21 @@ char *at(void *ws, size_t off) { return (char *)ws + off; }
 int to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Compute units of the current device (host query, cached per device).
+// The cache is the library's one piece of state kept between calls: a
+// per-device constant, written with relaxed atomics, so concurrent first
+// calls at worst both query the device and store the same value.
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
                                   dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Tuning override: MOE_GEMM_VARIANT_UP / MOE_GEMM_VARIANT_DOWN name a
@@ -498,6 +505,10 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
     if (variant == GEMM_BF16_W4_256x256) {
         GemmParams q = p;
         q.tail_split = tail_split(d, up);
+        // a split unit covers KT / S stages in whole stage pairs; any other
+        // split would drop or repeat part of K
+        if (q.tail_split > 1 && (q.K / 64) % (2 * q.tail_split) != 0)
+            return MOE_ERR_UNSUPPORTED;
         if (q.tail_split > 1) q.part = (float *)at(ws, layout(d).tpart);
         return to_status(launch_gemm(q, variant, up, grid, s));
     }
@@ -525,6 +536,17 @@ int moe_gemm_variant(const moe_desc *desc, int up) {
     int v = variant_override(up != 0, desc, N);
     if (v < 0) v = pick_variant(desc, N, up != 0);
     return v;
+}
+
+int moe_gemm_tail_split(const moe_desc *desc, int up) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    const int N = up ? (desc->activation == MOE_ACT_SWIGLU ? 2 * desc->d_ff
+                                                           : desc->d_ff)
+                     : desc->d;
+    int v = variant_override(up != 0, desc, N);
+    if (v < 0) v = pick_variant(desc, N, up != 0);
+    return v == GEMM_BF16_W4_256x256 ? tail_split(desc, up != 0) : 1;
 }
 
 size_t moe_workspace_size(const moe_desc *desc) {

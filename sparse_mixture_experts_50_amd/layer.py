@@ -98,6 +98,14 @@ def moe_gemm_variant(desc: MoeDesc, up: bool) -> int:
     return v
 
 
+def moe_gemm_tail_split(desc: MoeDesc, up: bool) -> int:
+    """K ranges per half-height tile of the four-wave 256-row GEMM for the
+    up (or down) projection (1: no split, or another kernel runs)."""
+    v = _lib.lib().moe_gemm_tail_split(ctypes.byref(desc), 1 if up else 0)
+    check("moe_gemm_tail_split", min(v, 0))
+    return v
+
+
 def _codes(t):
     """float8_e4m3fn tensors are passed as their uint8 codes."""
     if t is not None and t.dtype == torch.float8_e4m3fn:

@@ -312,3 +312,45 @@ def test_gemm_variant_override_is_validated(monkeypatch):
         assert moe.moe_gemm_variant(_desc_of(w3), True) != 20
     except moe.MoeError:
         pass
+
+
+@pytest.mark.parametrize("shape", [
+    dict(name="mixtral_prefill"),                          # K 4096 / 14336
+    dict(name="mixtral_prefill", T=2400, d=1024, d_ff=2048),   # K 1024 / 2048
+    dict(name="mixtral_prefill", T=1200, d=2048, d_ff=1536),   # K 2048 / 1536
+    dict(name="deepseek_v3", T=600, d=512, E=16, k=4, d_ff=512,
+         expert_bias="none", linear_biases=True),
+])
+def test_tail_split_covers_whole_stage_pairs(shape, monkeypatch):
+    # A split unit walks KT / S 64-deep stages two at a time: every cap of
+    # MOE_TAIL_SPLIT must leave (K / 64) divisible by 2 S, or the units
+    # would drop (or repeat) the last stages of K.
+    import workloads
+    shape = dict(shape)
+    w = workloads.WORKLOADS[shape.pop("name")]
+    if shape:
+        w = workloads.scaled(w, **shape)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+    d = _desc_of(w)
+    seen = set()
+    for cap in [None] + [str(c) for c in range(1, 9)]:
+        if cap is None:
+            monkeypatch.delenv("MOE_TAIL_SPLIT", raising=False)
+        else:
+            monkeypatch.setenv("MOE_TAIL_SPLIT", cap)
+        for up in (True, False):
+            K = w.d if up else w.d_ff
+            S = moe.moe_gemm_tail_split(d, up)
+            assert 1 <= S <= 8
+            assert (K // 64) % (2 * S) == 0 or S == 1, (cap, up, K, S)
+            if cap is not None:
+                assert S <= int(cap)
+            seen.add((up, S))
+    # the Mixtral down projection (K = 14336, 224 stages) splits its 64
+    # half tiles four ways by default; a cap of 3 must fall back to 2
+    if w.name == "mixtral_prefill" and w.d_ff == 14336:
+        monkeypatch.delenv("MOE_TAIL_SPLIT", raising=False)
+        assert moe.moe_gemm_tail_split(d, False) == 4
+        monkeypatch.setenv("MOE_TAIL_SPLIT", "3")
+        assert moe.moe_gemm_tail_split(d, False) == 2

@@ -8,7 +8,9 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
+import sparse_mixture_experts_50_amd as moe
 import workloads
 from workloads import scaled
 
@@ -31,6 +33,9 @@ CASES = {
     # gated experts, same group sizes
     "swiglu_600": scaled(W["mixtral_prefill_swiglu"], T=2400, d=1024,
                          d_ff=2048),
+    # K = 1536 (24 stages): splits of 2, 3 and 4 all cover whole stage
+    # pairs, so a cap of 3 really runs three units per half tile
+    "gelu_k1536": scaled(W["mixtral_prefill"], T=2400, d=1536, d_ff=1536),
     # shared expert (T = 600 rows: 2 full + an 88-row tail) and Linear
     # biases, top-4 of 16
     "shared_biases": scaled(W["deepseek_v3"], T=600, d=512, E=16, k=4,
@@ -39,18 +44,23 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("split", ["8", "1"])
+@pytest.mark.parametrize("split", ["8", "3", "1"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_tail_split_parity(name, split, monkeypatch):
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
     monkeypatch.setenv("MOE_TAIL_SPLIT", split)
     w = CASES[name]
+    d = moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, torch.bfloat16,
+                      n_shared=w.n_shared, activation=w.activation)
+    S = (moe.moe_gemm_tail_split(d, True), moe.moe_gemm_tail_split(d, False))
+    if name == "gelu_k1536" and split == "3":
+        assert S == (3, 3), S
     inp = inputs_on(w, device())
     gpu = gpu_forward(w, inp)
     tokens = sample_tokens(w.T, 64, seed=5)
     rep = check_layer(w, inp, gpu, tokens=tokens)
-    say(f"[tail split <= {split}] {name}: {rep}")
+    say(f"[tail split <= {split}, S up/down {S}] {name}: {rep}")
 
 
 @pytest.mark.parametrize("name", ["gelu_600", "swiglu_600"])
