@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shaped leg of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (a kernel of "
                          "known traffic for scaling HBM byte counters)")
@@ -158,6 +160,106 @@ def cpu_baseline(wl, inp, budget_s):
                        f"layer (router to combine) in fp64, {dt:.1f} s")
 
 
+def time_layer(wl, layer, weights, xs, steps, warmup, stream):
+    """Run ``warmup`` untimed and ``steps`` timed layer calls (call i on
+    xs[i % len(xs)]) through the five entry points on ``stream``; HIP events
+    around each call and around each up-projection GEMM launch."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_50_amd as moe
+    desc, r, ws, y = layer.buffers(wl.T)
+    n_x = len(xs)
+    up_ev = []
+    step_ev = []
+
+    def step(i, timed):
+        x = xs[i % n_x]
+        if timed:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+        moe.moe_router_topk(desc, x, weights, r, ws)
+        moe.moe_permute(desc, r, ws)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        moe.moe_ffn_up(desc, x, weights, r, ws)
+        if timed:
+            e1.record(stream)
+            up_ev.append((e0, e1))
+        moe.moe_ffn_down(desc, weights, r, ws)
+        moe.moe_combine(desc, r, y, ws)
+        if timed:
+            s1.record(stream)
+            step_ev.append((s0, s1))
+
+    log(f"[bench] {wl.name}: warmup {warmup}")
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: timing {steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    counts = r.counts.cpu().numpy()
+    kept = r.kept.cpu().numpy()
+    assert int(counts.sum()) == wl.T * wl.k
+    return dict(desc=desc, total_ms=total_ms, wall=wall,
+                ms_per_step=total_ms / steps,
+                step_ms=[a.elapsed_time(b) for a, b in step_ev],
+                up_avg_ms=float(np.mean([a.elapsed_time(b)
+                                         for a, b in up_ev])),
+                counts=counts, kept=kept)
+
+
+def decode_leg(weights, dev, stream, warmup=10):
+    """The Mixtral-shaped decode layer (32 tokens per call, the same expert
+    weights as the prefill layer), timed over its 200 calls with distinct
+    x: per-call time, tokens/s and the whole layer's algorithmic HBM bytes
+    per call against the HBM peak, plus the up GEMM's own rate."""
+    import numpy as np
+
+    import sparse_mixture_experts_50_amd as moe
+    import workloads
+    wl = workloads.get("mixtral_decode")
+    xs = [workloads.make_x(wl, dev, c) for c in range(wl.calls)]
+    layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha,
+                         routing=wl.routing, activation=wl.activation)
+    m = time_layer(wl, layer, weights, xs, wl.calls, warmup, stream)
+    # touched experts and kept rows vary by call: every one of the 200
+    # calls touches all 8 experts of this workload (checked on the last)
+    alg = algorithmic(wl, m["counts"], m["kept"])
+    ms = m["ms_per_step"]
+    layer_gbs = alg["bytes"] / (ms * 1e6)
+    up_gbs = alg["up_bytes"] / (m["up_avg_ms"] * 1e6)
+    return {
+        "workload": wl.name, "calls": wl.calls, "warmup": warmup,
+        "tokens_per_call": wl.T,
+        "ms_per_call": ms,
+        "ms_per_call_median": float(np.median(m["step_ms"])),
+        "tokens_per_s": wl.T / (ms / 1e3),
+        "layer_bytes_per_call": alg["bytes"],
+        "layer_hbm_gbs": layer_gbs,
+        "layer_hbm_frac": layer_gbs / HBM_PEAK_GBS,
+        "up_gemm_ms": m["up_avg_ms"],
+        "up_gemm_gbs": up_gbs,
+        "up_gemm_frac": up_gbs / HBM_PEAK_GBS,
+        "experts_touched_last_call": int(np.sum(m["kept"] > 0)),
+        "gemm_variants": [moe.moe_gemm_variant(m["desc"], True),
+                          moe.moe_gemm_variant(m["desc"], False)],
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -200,61 +302,15 @@ def main():
     weights = moe.Weights.from_dict(inp)
     layer = moe.MoeLayer(weights, wl.k, wl.capacity_factor, wl.alpha,
                          routing=wl.routing, activation=wl.activation)
-    desc, r, ws, y = layer.buffers(wl.T)
     stream = torch.cuda.current_stream(dev)
-
-    up_ev = []
-    step_ev = []
-
-    def step(i, timed):
-        x = xs[i % n_x]
-        if timed:
-            s0 = torch.cuda.Event(enable_timing=True)
-            s1 = torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-        moe.moe_router_topk(desc, x, weights, r, ws)
-        moe.moe_permute(desc, r, ws)
-        if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        moe.moe_ffn_up(desc, x, weights, r, ws)
-        if timed:
-            e1.record(stream)
-            up_ev.append((e0, e1))
-        moe.moe_ffn_down(desc, weights, r, ws)
-        moe.moe_combine(desc, r, y, ws)
-        if timed:
-            s1.record(stream)
-            step_ev.append((s0, s1))
-
-    log(f"[bench] warmup {warmup}")
-    for i in range(warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        step(i, True)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    up_ms = [a.elapsed_time(b) for a, b in up_ev]
-    up_avg_ms = float(np.mean(up_ms))
-    ms_per_step = total_ms / steps
-    step_ms = [a.elapsed_time(b) for a, b in step_ev]
-
-    # algorithmic work of the last call (counts of each call are similar;
-    # decode calls differ, so average their touched/row counts)
-    counts = r.counts.cpu().numpy()
-    kept = r.kept.cpu().numpy()
+    m = time_layer(wl, layer, weights, xs, steps, warmup, stream)
+    desc = m["desc"]
+    total_ms, wall = m["total_ms"], m["wall"]
+    up_avg_ms = m["up_avg_ms"]
+    ms_per_step = m["ms_per_step"]
+    step_ms = m["step_ms"]
+    counts, kept = m["counts"], m["kept"]
     alg = algorithmic(wl, counts, kept)
-    assert int(counts.sum()) == wl.T * wl.k
     tokens_per_s = wl.T * steps / (total_ms / 1e3)
     if float(np.sum(kept)) / wl.E <= 48:       # rows per routed expert
         roof = dict(bound="hbm", achieved=alg["up_bytes"] / (up_avg_ms * 1e6),
@@ -277,6 +333,12 @@ def main():
     roof["gemm_variants"] = [moe.moe_gemm_variant(desc, True),
                              moe.moe_gemm_variant(desc, False)]
     roof["kernel_ms"] = up_avg_ms
+
+    decode = None
+    if wl.name == "mixtral_prefill" and not args.no_decode:
+        # the metric's second half: the decode-shaped layer's HBM fraction,
+        # on the same weights, in the same process
+        decode = decode_leg(weights, dev, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -309,6 +371,7 @@ def main():
         "wall_s": wall,
         "measured_hbm_copy_gbs": copy_gbs,
         "roofline": roof,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

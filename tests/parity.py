@@ -70,6 +70,49 @@ def sample_tokens(T: int, n: int, seed: int = 0, must=()) -> np.ndarray:
     return np.array(sorted(base | set(extra.tolist())), dtype=np.int32)
 
 
+# Row-tile heights of the grouped-GEMM variants (internal ids reported by
+# moe_gemm_variant), with the wave-row boundaries inside a tile.  The
+# four-wave 256-row kernel (14) also runs 224-row tiles (evenly split
+# groups, waves of 112 rows) and 128-row half tiles.
+TILE_ROWS = {0: (256,), 1: (128,), 2: (32,), 3: (64,), 5: (256,), 6: (128,),
+             8: (256,), 9: (128,), 13: (320,), 14: (256, 224, 128),
+             15: (128,), 20: (128,)}
+
+
+def tile_cover_tokens(w: workloads.Workload, gpu: dict, variants) -> \
+        np.ndarray:
+    """Tokens whose rows touch every row tile that the GEMM variants run:
+    for each expert group (and the shared expert's group of all T tokens)
+    its first and last row and, for every tile height of the variants, each
+    tile's first, middle pair and last row, plus rows 111/112 and 127/128
+    of the four-wave kernel's tiles (its wave-row and half-tile edges).
+    Slot rows map to tokens through the GPU's slot_token, which the checker
+    separately requires to equal the oracle's."""
+    off = gpu["offsets"].reshape(-1)
+    st = gpu["slot_token"].reshape(-1)
+    heights = sorted({h for v in variants for h in TILE_ROWS.get(v, (16,))})
+    four_wave = any(v in (14, 15) for v in variants)
+
+    def rows_of(R):
+        rows = {0, R - 1}
+        for h in heights:
+            for s0 in range(0, R, h):
+                rows |= {s0, s0 + h // 2 - 1, s0 + h // 2,
+                         min(s0 + h, R) - 1}
+                if four_wave:
+                    rows |= {s0 + 111, s0 + 112, s0 + 127, s0 + 128}
+        return sorted(r for r in rows if 0 <= r < R)
+
+    toks = set()
+    for e in range(len(off) - 1):
+        R = int(off[e + 1] - off[e])
+        if R > 0:
+            toks.update(int(st[off[e] + r]) for r in rows_of(R))
+    if w.n_shared:
+        toks.update(rows_of(w.T))
+    return np.array(sorted(toks), dtype=np.int32)
+
+
 def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
                 tokens=None) -> dict:
     """Oracle on the same inputs; assert every rule; return a report."""
@@ -132,7 +175,7 @@ def check_layer(w: workloads.Workload, inp: dict, gpu: dict,
     # outputs on the checked rows
     y_ref = cond["y"]
     y_gpu = gpu["y"][tokens]
-    scale = np.max(np.abs(y_ref))
+    scale = np.max(np.abs(y_ref)) if y_ref.size else 0.0
     err = np.max(np.abs(y_gpu - y_ref)) if y_ref.size else 0.0
     tol = TOL[w.dtype] * scale
     # rows whose every assignment overflowed are exactly zero
