@@ -263,6 +263,18 @@ int moe_router_topk(const moe_desc *desc, const void *x,
 int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
                 size_t ws_bytes, void *stream);
 
+/* moe_router_topk followed by moe_permute (layer steps 1-3 and 6), with
+ * the same arguments, checks and results.  Where a decode-sized step
+ * allows (bf16, top-k routing, E <= 32, T <= 32, T*k <= 256) the routing
+ * and the dispatch run in one workgroup after the partial logits: two
+ * kernel launches instead of three, with results equal to the two calls'
+ * bit for bit.  The pages give fewer kernel launches as the reason for
+ * fused MoE kernels in serving ("MoE inference with vLLM";
+ * "AI-Research-SKILLs MoE training guide", sec. 9.2). */
+int moe_route_dispatch(const moe_desc *desc, const void *x,
+                       const moe_weights *w, moe_routing *r, void *ws,
+                       size_t ws_bytes, void *stream);
+
 /* Grouped expert FFNs (layer step 4): for every kept slot s of expert e,
  *   Yp[s] = W2_e GELU(W1_e x[slot_token[s]] + b1_e) + b2_e,
  * and, with a shared expert, Yp[R + t] = Shared(x[t]) for every token,
@@ -292,8 +304,8 @@ int moe_ffn_down(const moe_desc *desc, const moe_weights *w,
 int moe_combine(const moe_desc *desc, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
-/* The whole forward: moe_router_topk, moe_permute, moe_grouped_ffn and
- * moe_combine on one stream. */
+/* The whole forward: moe_route_dispatch (= moe_router_topk and
+ * moe_permute), moe_grouped_ffn and moe_combine on one stream. */
 int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
                 moe_routing *r, void *y, void *ws, size_t ws_bytes,
                 void *stream);

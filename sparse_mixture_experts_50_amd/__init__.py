@@ -9,7 +9,8 @@ from .layer import (MoeLayer, Routing, Weights, make_desc,  # noqa: F401
                     moe_bias_update, moe_capacity, moe_combine,
                     moe_ffn_down, moe_ffn_up, moe_forward, moe_gemm_tail_split,
                     moe_gemm_variant,
-                    moe_grouped_ffn, moe_permute, moe_router_topk,
+                    moe_grouped_ffn, moe_permute, moe_route_dispatch,
+                    moe_router_topk,
                     moe_workspace_size)
 
 __version__ = "0.1.0"

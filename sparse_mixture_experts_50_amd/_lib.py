@@ -66,6 +66,10 @@ SIGNATURES = {
                                        ctypes.POINTER(MoeWeights),
                                        ctypes.POINTER(MoeRouting), c_vp,
                                        ctypes.c_size_t, c_vp]),
+    "moe_route_dispatch": (ctypes.c_int, [ctypes.POINTER(MoeDesc), c_vp,
+                                          ctypes.POINTER(MoeWeights),
+                                          ctypes.POINTER(MoeRouting), c_vp,
+                                          ctypes.c_size_t, c_vp]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(MoeDesc),
                                    ctypes.POINTER(MoeRouting), c_vp,
                                    ctypes.c_size_t, c_vp]),

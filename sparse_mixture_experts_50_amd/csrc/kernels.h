@@ -119,6 +119,13 @@ GemmVariantInfo gemm_variant_info(int variant);
 
 hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s);
 hipError_t launch_permute(const PermuteParams &p, hipStream_t s);
+// Router and permute of a decode-sized step in two launches instead of
+// three (bf16 split router plan, E <= 32, T <= 32, T*k <= 256, top-k
+// routing): the partial logits, then routing and dispatch in one block;
+// the same results as launch_router followed by launch_permute.
+bool route_permute_small_ok(const RouterParams &p);
+hipError_t launch_route_permute_small(const RouterParams &p,
+                                      const PermuteParams &q, hipStream_t s);
 hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
                        hipStream_t s);

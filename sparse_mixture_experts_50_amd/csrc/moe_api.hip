@@ -444,6 +444,74 @@ int check_routing_combine(const moe_routing *r) {
     return MOE_OK;
 }
 
+RouterParams router_params(const moe_desc *desc, const void *x,
+                           const moe_weights *w, moe_routing *r, void *ws) {
+    const WsLayout L = layout(desc);
+    RouterParams p;
+    p.x = x;
+    p.wr = w->w_router;
+    p.add = w->b_router;
+    p.sub = w->expert_bias;
+    p.topk_idx = r->topk_idx;
+    p.topk_w = r->topk_w;
+    p.p_part = (float *)at(ws, L.p_part);
+    p.zh_part = (float *)at(ws, L.zh_part);
+    p.scores = expert_choice(desc) ? (float *)at(ws, L.scores) : nullptr;
+    p.slot_of = r->slot_of;
+    const RouterPlan rp = plan(desc);
+    p.part = (float *)at(ws, L.rpart);
+    p.S = rp.split ? rp.S : 0;
+    p.kc = rp.kc;
+    p.T = desc->T;
+    p.d = desc->d;
+    p.E = desc->E;
+    p.k = desc->k;
+    return p;
+}
+
+PermuteParams permute_params(const moe_desc *desc, moe_routing *r, void *ws) {
+    const WsLayout L = layout(desc);
+    PermuteParams p;
+    p.topk_idx = r->topk_idx;
+    p.p_part = (const float *)at(ws, L.p_part);
+    p.zh_part = (const float *)at(ws, L.zh_part);
+    p.blk = (int32_t *)at(ws, L.blk);
+    p.scores = expert_choice(desc) ? (const float *)at(ws, L.scores) : nullptr;
+    p.counts = r->counts;
+    p.kept = r->kept;
+    p.offsets = r->offsets;
+    p.slot_token = r->slot_token;
+    p.slot_of = r->slot_of;
+    p.f = r->f;
+    p.p = r->p;
+    p.l_aux = r->l_aux;
+    p.monitor = r->monitor;
+    p.T = desc->T;
+    p.E = desc->E;
+    p.k = desc->k;
+    p.capacity = desc->capacity;
+    p.n_rtiles = L.n_rtiles;
+    p.n_chunks = L.n_chunks;
+    p.alpha = desc->aux_alpha;
+    return p;
+}
+
+// moe_router_topk then moe_permute, as one launch where a decode-sized
+// step allows it (the same results either way).  Arguments checked by the
+// caller.
+int route_and_permute(const moe_desc *desc, const void *x,
+                      const moe_weights *w, moe_routing *r, void *ws,
+                      size_t ws_bytes, void *stream) {
+    const RouterParams rp = router_params(desc, x, w, r, ws);
+    if (desc->dtype == MOE_BF16 && !expert_choice(desc) &&
+        route_permute_small_ok(rp))
+        return to_status(launch_route_permute_small(
+            rp, permute_params(desc, r, ws), (hipStream_t)stream));
+    int st = moe_router_topk(desc, x, w, r, ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_permute(desc, r, ws, ws_bytes, stream);
+}
+
 GemmParams gemm_params(const moe_desc *d, const moe_weights *w,
                        const moe_routing *r, bool up, const void *x, void *ws) {
     const WsLayout L = layout(d);
@@ -563,26 +631,7 @@ int moe_router_topk(const moe_desc *desc, const void *x, const moe_weights *w,
     if ((st = check_weights_router(w)) != MOE_OK) return st;
     if ((st = check_routing_router(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
-    const WsLayout L = layout(desc);
-    RouterParams p;
-    p.x = x;
-    p.wr = w->w_router;
-    p.add = w->b_router;
-    p.sub = w->expert_bias;
-    p.topk_idx = r->topk_idx;
-    p.topk_w = r->topk_w;
-    p.p_part = (float *)at(ws, L.p_part);
-    p.zh_part = (float *)at(ws, L.zh_part);
-    p.scores = expert_choice(desc) ? (float *)at(ws, L.scores) : nullptr;
-    p.slot_of = r->slot_of;
-    const RouterPlan rp = plan(desc);
-    p.part = (float *)at(ws, L.rpart);
-    p.S = rp.split ? rp.S : 0;
-    p.kc = rp.kc;
-    p.T = desc->T;
-    p.d = desc->d;
-    p.E = desc->E;
-    p.k = desc->k;
+    const RouterParams p = router_params(desc, x, w, r, ws);
     return to_status(launch_router(p, desc->dtype, (hipStream_t)stream));
 }
 
@@ -593,32 +642,24 @@ int moe_permute(const moe_desc *desc, moe_routing *r, void *ws,
     if (desc->T == 0) return MOE_OK;
     if ((st = check_routing_permute(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
-    const WsLayout L = layout(desc);
-    PermuteParams p;
-    p.topk_idx = r->topk_idx;
-    p.p_part = (const float *)at(ws, L.p_part);
-    p.zh_part = (const float *)at(ws, L.zh_part);
-    p.blk = (int32_t *)at(ws, L.blk);
-    p.scores = expert_choice(desc) ? (const float *)at(ws, L.scores) : nullptr;
-    p.counts = r->counts;
-    p.kept = r->kept;
-    p.offsets = r->offsets;
-    p.slot_token = r->slot_token;
-    p.slot_of = r->slot_of;
-    p.f = r->f;
-    p.p = r->p;
-    p.l_aux = r->l_aux;
-    p.monitor = r->monitor;
-    p.T = desc->T;
-    p.E = desc->E;
-    p.k = desc->k;
-    p.capacity = desc->capacity;
-    p.n_rtiles = L.n_rtiles;
-    p.n_chunks = L.n_chunks;
-    p.alpha = desc->aux_alpha;
+    const PermuteParams p = permute_params(desc, r, ws);
     if (expert_choice(desc))
         return to_status(launch_expert_choice(p, (hipStream_t)stream));
     return to_status(launch_permute(p, (hipStream_t)stream));
+}
+
+int moe_route_dispatch(const moe_desc *desc, const void *x,
+                       const moe_weights *w, moe_routing *r, void *ws,
+                       size_t ws_bytes, void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    if (!x) return MOE_ERR_INVALID_ARG;
+    if ((st = check_weights_router(w)) != MOE_OK) return st;
+    if ((st = check_routing_router(desc, r)) != MOE_OK) return st;
+    if ((st = check_routing_permute(desc, r)) != MOE_OK) return st;
+    if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
+    return route_and_permute(desc, x, w, r, ws, ws_bytes, stream);
 }
 
 int moe_ffn_up(const moe_desc *desc, const void *x, const moe_weights *w,
@@ -688,9 +729,8 @@ int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
     if ((st = check_routing_router(desc, r)) != MOE_OK) return st;
     if ((st = check_routing_permute(desc, r)) != MOE_OK) return st;
     if ((st = check_ws(desc, ws, ws_bytes)) != MOE_OK) return st;
-    if ((st = moe_router_topk(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
+    if ((st = route_and_permute(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
         return st;
-    if ((st = moe_permute(desc, r, ws, ws_bytes, stream)) != MOE_OK) return st;
     if ((st = moe_grouped_ffn(desc, x, w, r, ws, ws_bytes, stream)) != MOE_OK)
         return st;
     return moe_combine(desc, r, y, ws, ws_bytes, stream);

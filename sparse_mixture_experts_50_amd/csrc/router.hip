@@ -25,6 +25,7 @@
 // (32 consecutive tokens per expert row), the layout in which each expert
 // later ranks its column.
 #include "kernels.h"
+#include "permute_block.h"
 
 namespace {
 
@@ -464,25 +465,13 @@ __device__ __forceinline__ void route_lanes(const float (*lg)[EP + 1],
     zh[tl][1] = h;
 }
 
-// Sum the S partial logit planes of 32 tokens in order, then route them:
-// one lane per token in a 256-thread block (E <= 32: a handful of logits
-// per lane beats a chain of 64-lane reductions), or 2 tokens per wave in a
-// 1024-thread block.
+// Sum the S partial logit planes of this block's 32 tokens in order into
+// lg (tokens past T take the last token's sums; they are never routed).
 template <int EP>
-__global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterParams p) {
-    constexpr bool SMALL = EP <= 32;
-    __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
-    __shared__ float pp[SMALL ? 1 : RW][EP];
-    __shared__ float pr[SMALL ? RT : 1][EP + 1];
-    __shared__ float zh[RT][2];
-    __shared__ float addv[SMALL ? EP : 1], subv[SMALL ? EP : 1];
+__device__ __forceinline__ void sum_partials(const RouterParams &p,
+                                             float (*lg)[EP + 1]) {
     const int t0 = blockIdx.x * RT;
     const size_t plane = (size_t)p.T * p.E;
-    if (SMALL && threadIdx.x < EP) {
-        const int e = threadIdx.x;
-        addv[e] = (e < p.E && p.add) ? p.add[e] : 0.0f;
-        subv[e] = (e < p.E && p.sub) ? p.sub[e] : 0.0f;
-    }
     for (int i = threadIdx.x; i < RT * p.E; i += blockDim.x) {
         const int tl = i / p.E, e = i - tl * p.E;
         const int t = min(t0 + tl, p.T - 1);
@@ -496,14 +485,29 @@ __global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterP
 #pragma unroll
         for (int k = 1; k < MOE_ROUTER_MAX_SPLITS; ++k)
             if (k < p.S) s += a[k];
-        lg[0][tl][e] = s;
+        lg[tl][e] = s;
     }
+}
+
+// Route 32 tokens from their split partial logits, one lane per token
+// (E <= 32: a handful of logits per lane beats a chain of 64-lane
+// reductions), in a 256-thread block; then the block's probability column
+// sums and lse^2 / entropy sums in token order.
+template <int EP>
+__device__ __forceinline__ void route_tile_lanes(const RouterParams &p) {
+    static_assert(EP <= 32, "one lane per token");
+    __shared__ float lg[RT][EP + 1];      // rows of EP + 1 floats (LG_PAD)
+    __shared__ float pr[RT][EP + 1];
+    __shared__ float zh[RT][2];
+    __shared__ float addv[EP], subv[EP];
+    if (threadIdx.x < EP) {
+        const int e = threadIdx.x;
+        addv[e] = (e < p.E && p.add) ? p.add[e] : 0.0f;
+        subv[e] = (e < p.E && p.sub) ? p.sub[e] : 0.0f;
+    }
+    sum_partials<EP>(p, lg);
     __syncthreads();
-    if (!SMALL) {
-        route_tokens<EP, 1>(lg, p, pp);
-        return;
-    }
-    if (threadIdx.x < RT) route_lanes<EP>(lg[0], p, addv, subv, pr, zh);
+    if (threadIdx.x < RT) route_lanes<EP>(lg, p, addv, subv, pr, zh);
     __syncthreads();
     // block sums in token order: probability columns, then lse^2, entropy
     for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
@@ -517,6 +521,38 @@ __global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterP
         for (int tl = 1; tl < RT; ++tl) s += zh[tl][c];
         p.zh_part[(size_t)blockIdx.x * 2 + c] = s;
     }
+}
+
+// Sum the S partial logit planes of 32 tokens in order, then route them:
+// one lane per token in a 256-thread block (E <= 32), or 2 tokens per wave
+// in a 1024-thread block.
+template <int EP>
+__global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterParams p) {
+    if constexpr (EP <= 32) {
+        route_tile_lanes<EP>(p);
+    } else {
+        __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
+        __shared__ float pp[RW][EP];
+        sum_partials<EP>(p, lg[0]);
+        __syncthreads();
+        route_tokens<EP, 1>(lg, p, pp);
+    }
+}
+
+// A decode-sized step's routing and dispatch in one launch (bf16 split
+// router, E <= 32, one 32-token tile, T*k <= 256): router_route's work for
+// the tile, then the single-block permute on the picks it wrote, so the
+// results equal router_route + permute_small bit for bit.  The logits stay
+// spread over the partial-logit kernel's blocks (one block pulling every
+// token and router row through its CU took 22 us against 5).
+template <int EP>
+__global__ __launch_bounds__(256) void route_permute_small(RouterParams p,
+                                                           PermuteParams q) {
+    route_tile_lanes<EP>(p);
+    // the picks and sums this block wrote to global memory are visible to
+    // the whole block after the barrier
+    __syncthreads();
+    permute_one_block<256>(q);
 }
 
 // bf16, fused: one block (16 waves) computes and routes 32 tokens.  The
@@ -689,5 +725,20 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
     case 128: hipLaunchKernelGGL(router_f32<128>, grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL(router_f32<256>, grid, block, 0, s, p); break;
     }
+    return hipGetLastError();
+}
+
+bool route_permute_small_ok(const RouterParams &p) {
+    return p.S > 0 && p.S <= MOE_ROUTER_MAX_SPLITS && p.E <= 32 &&
+           p.T <= RT && p.T * p.k <= MOE_PERMUTE_CHUNK && !p.scores;
+}
+
+hipError_t launch_route_permute_small(const RouterParams &p,
+                                      const PermuteParams &q, hipStream_t s) {
+    const dim3 lgrid(1, p.S);
+    hipLaunchKernelGGL(router_logits<32>, lgrid, dim3(256), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_permute_small<32>, dim3(1), dim3(256), 0, s, p, q);
     return hipGetLastError();
 }

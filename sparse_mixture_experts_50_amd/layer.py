@@ -249,6 +249,16 @@ def moe_permute(desc, r: Routing, ws) -> None:
         ctypes.byref(desc), ctypes.byref(rs), p, n, _stream(ws)))
 
 
+def moe_route_dispatch(desc, x, w: Weights, r: Routing, ws) -> None:
+    """moe_router_topk + moe_permute (one launch for decode-sized steps)."""
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    p, n = _ws(desc, ws)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_route_dispatch", _lib.lib().moe_route_dispatch(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), p, n, _stream(x)))
+
+
 def moe_grouped_ffn(desc, x, w: Weights, r: Routing, ws) -> None:
     _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
     p, n = _ws(desc, ws)

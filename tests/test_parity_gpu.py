@@ -109,6 +109,43 @@ def test_step_entry_points_match_forward():
     check_layer(w, inp, b)
 
 
+# Decode-sized steps (bf16, E <= 32, T <= 32, T*k <= 256): moe_forward runs
+# the router and the permute as one launch; the separate entry points run
+# the split router (logits over S depth ranges, then routing) and the
+# single-launch permute.  Both must agree bit for bit, and with the oracle.
+FUSED_ROUTE = {
+    "mixtral_decode": W["mixtral_decode"],                      # S = 8
+    "ragged_e16_k4": scaled(W["mixtral_decode"], T=20, d=1024, E=16, k=4,
+                            d_ff=512),                          # S = 2
+    "e32_k8_whole_chunk": scaled(W["mixtral_decode"], T=32, d=512, E=32,
+                                 k=8, d_ff=256),                # S = 1
+    "capacity_skew": scaled(W["switch_top1_cap"], T=32, d=768, E=8,
+                            d_ff=512, capacity_factor=1.0),     # C = 4
+    "zipf_shared_d7168": scaled(W["deepseek_v3"], T=16, d=7168, E=32, k=4,
+                                d_ff=256),                      # kc = 896
+    "uneven_ranges": scaled(W["mixtral_decode"], T=24, d=4160, E=8,
+                            d_ff=256),       # last range shorter than kc
+    "single_token": scaled(W["mixtral_decode"], T=1, d=1024, E=8,
+                           d_ff=256),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_ROUTE))
+def test_fused_decode_routing_matches_entry_points(name):
+    w = FUSED_ROUTE[name]
+    say(f"[fused route] {name}: {w}")
+    inp = inputs_on(w, device())
+    a = gpu_forward(w, inp, steps=False)
+    b = gpu_forward(w, inp, steps=True)
+    for key in ("topk_idx", "topk_w", "counts", "kept", "offsets",
+                "slot_token", "slot_of", "f", "p", "l_aux", "monitor", "y"):
+        assert np.array_equal(a[key], b[key]), key
+    rep = check_layer(w, inp, a)
+    if w.capacity_factor is not None:
+        assert np.any(a["slot_of"] < 0)
+    say(f"[fused route] {name}: {rep}")
+
+
 # Full workload sizes, in the launch configuration the benchmark times.
 # Where the oracle finishes the whole layer in well under a minute on the
 # host cores every output row is checked; the DeepSeek-shaped layer (257
