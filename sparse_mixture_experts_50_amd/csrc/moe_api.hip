@@ -110,6 +110,22 @@ TileCount group_tiles(const moe_desc *d, int bm) {
     return c;
 }
 
+int variant_override(bool up, const moe_desc *d, int N);
+bool w4_fits(const moe_desc *d, bool up);
+
+// Whether the four-wave 256-row kernel may run this GEMM: forced by the
+// tuning variable, or inside the range where pick_variant weighs it
+// against the eight-wave kernels (a function of the descriptor only; the
+// device-dependent cost comparison may still pick another kernel).
+bool w4_256_possible(const moe_desc *d, bool up, int N) {
+    const int forced = variant_override(up, d, N);
+    if (forced >= 0) return forced == GEMM_BF16_W4_256x256;
+    const double avg = (double)routed_rows(d) / d->E;
+    const int K = up ? d->d : d->d_ff;
+    return N % 256 == 0 && avg >= 768.0 && K >= 2048 &&
+           w4_fits(d, up);
+}
+
 // How many K ranges the four-wave 256-row kernel splits each half-height
 // tile into (1: none).  When the full tiles fill whole rounds and the half
 // tiles would run as a sparse extra round (the Mixtral down GEMM: 512 full
@@ -123,6 +139,9 @@ int tail_split(const moe_desc *d, bool up) {
                      : d->d;
     const int K = up ? d->d : d->d_ff;
     if (N % 256 != 0 || K % 128 != 0 || K < 256) return 1;
+    // no split (and no partials in the workspace) where the four-wave
+    // 256-row kernel cannot be the pick
+    if (!w4_256_possible(d, up, N)) return 1;
     const TileCount g = group_tiles(d, 256);
     const int rem = d->T & 255;
     const double shared_half = (double)d->n_shared * (rem > 0 && rem <= 128);
