@@ -92,7 +92,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k out of range */
     MOE_ERR_UNSUPPORTED = -2, /* shape or dtype this library cannot run */
     MOE_ERR_WORKSPACE = -3,   /* workspace missing or too small */
-    MOE_ERR_HIP = -4          /* a HIP launch failed */
+    MOE_ERR_HIP = -4,         /* a HIP launch failed */
+    MOE_ERR_SCRATCH = -5      /* moe_forward_noalloc: the shape needs more
+                                 than MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -309,6 +311,28 @@ int moe_combine(const moe_desc *desc, const moe_routing *r, void *y,
 int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
                 moe_routing *r, void *y, void *ws, size_t ws_bytes,
                 void *stream);
+
+/* Bytes of the static device scratch moe_forward_noalloc uses (16 MiB per
+ * GPU the library runs on, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments and results as
+ * moe_forward, minus ws / ws_bytes: the scratch (router partials, dispatch
+ * histograms, hidden activations, expert outputs) lives in a file-scope
+ * device array of MOE_NOALLOC_SCRATCH_BYTES per GPU, whose address is
+ * looked up once per device on the first call there.  Allocates nothing:
+ * no hipMalloc, hipFree or allocating library call.  Returns
+ * MOE_ERR_SCRATCH, enqueuing nothing, when moe_workspace_size(desc)
+ * exceeds the buffer (decode-sized layers fit: the Mixtral-shaped T = 32
+ * step needs 2.4 MB).  No part of the scratch has to start at zero.  Every
+ * call on one GPU shares that GPU's buffer, which keeps the last call's
+ * contents: calls that overlap on one GPU (distinct streams, or host
+ * threads) race and must be serialised by the caller. */
+int moe_forward_noalloc(const moe_desc *desc, const void *x,
+                        const moe_weights *w, moe_routing *r, void *y,
+                        void *stream);
 
 /* Balancing-bias step (layer step 7), in place on fp32 state:
  * bias[e] = bias[e] + gamma * sign(counts[e] - target), sign(0) = 0, one

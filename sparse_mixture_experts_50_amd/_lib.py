@@ -21,6 +21,8 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_ROUTE_TOPK = 0
@@ -92,6 +94,10 @@ SIGNATURES = {
                                    ctypes.POINTER(MoeWeights),
                                    ctypes.POINTER(MoeRouting), c_vp, c_vp,
                                    ctypes.c_size_t, c_vp]),
+    "moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeDesc), c_vp,
+                                           ctypes.POINTER(MoeWeights),
+                                           ctypes.POINTER(MoeRouting), c_vp,
+                                           c_vp]),
     "moe_bias_update": (ctypes.c_int, [c_i32, c_vp, ctypes.c_float,
                                        ctypes.c_float, c_vp, c_vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -602,6 +602,38 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
     return to_status(launch_gemm(p, variant, up, grid, s));
 }
 
+// ---------------------------------------------------------------------
+// Static scratch of moe_forward_noalloc: a file-scope device array that
+// each GPU the library runs on holds until the process ends.  In host code
+// `scratch` is only a host-side stand-in for the symbol: its device
+// address on the current device comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device (nullptr and the
+// failing status on error).  The lookup runs once per device; concurrent
+// first calls may both look it up and store the same address.
+void *static_scratch(int *status) {
+    static std::atomic<void *> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *status = MOE_ERR_HIP;
+        return nullptr;
+    }
+    void *ptr = addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess ||
+            !ptr) {
+            *status = MOE_ERR_HIP;
+            return nullptr;
+        }
+        addr[dev].store(ptr, std::memory_order_release);
+    }
+    *status = MOE_OK;
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -755,6 +787,19 @@ int moe_forward(const moe_desc *desc, const void *x, const moe_weights *w,
     return moe_combine(desc, r, y, ws, ws_bytes, stream);
 }
 
+int moe_forward_noalloc(const moe_desc *desc, const void *x,
+                        const moe_weights *w, moe_routing *r, void *y,
+                        void *stream) {
+    int st = check_desc(desc);
+    if (st != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    const size_t need = layout(desc).total;
+    if (need > kStaticScratchBytes) return MOE_ERR_SCRATCH;
+    void *ws = static_scratch(&st);
+    if (st != MOE_OK) return st;
+    return moe_forward(desc, x, w, r, y, ws, kStaticScratchBytes, stream);
+}
+
 int moe_bias_update(int32_t E, const int32_t *counts, float target,
                     float gamma, float *expert_bias, void *stream) {
     if (E < 1 || E > MOE_MAX_E || !counts || !expert_bias)
@@ -770,6 +815,8 @@ const char *moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+        return "layer needs more scratch than the static buffer holds";
     default: return "unknown status";
     }
 }

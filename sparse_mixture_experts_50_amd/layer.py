@@ -304,6 +304,18 @@ def moe_forward(desc, x, w: Weights, r: Routing, y, ws) -> None:
         ctypes.byref(rs), y.data_ptr(), p, n, _stream(x)))
 
 
+def moe_forward_noalloc(desc, x, w: Weights, r: Routing, y) -> None:
+    """moe_forward with the library's static device scratch instead of a
+    workspace (no allocation; raises MoeError with MOE_ERR_SCRATCH when the
+    shape needs more than the static buffer)."""
+    _need(x, "x", (desc.T, desc.d), w.dtype, w.device)
+    _need(y, "y", (desc.T, desc.d), w.dtype, w.device)
+    rs, wsct = r.struct(), w.struct()
+    check("moe_forward_noalloc", _lib.lib().moe_forward_noalloc(
+        ctypes.byref(desc), x.data_ptr(), ctypes.byref(wsct),
+        ctypes.byref(rs), y.data_ptr(), _stream(x)))
+
+
 def moe_bias_update(counts, target: float, gamma: float,
                     expert_bias) -> None:
     E = expert_bias.numel()
