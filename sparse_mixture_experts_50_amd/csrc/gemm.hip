@@ -79,16 +79,20 @@ __device__ __forceinline__ void tile_sstore(const u32x4 (&ra)[AC],
 
 // LDS -> registers: the MFMA fragments of sub-step kk (16 k values) of one
 // stage for this wave's TM row tiles (A) and TN column tiles (B).
-template <int BM, int BN, int WM, int WN, int TM, int TN>
+// BMX: rows of the tile being computed, at most the BM rows the stage
+// holds (the eight-wave kernel runs a group of <= 256 rows in its 320-row
+// stages as a 256-row tile).
+template <int BM, int BN, int WM, int WN, int TM, int TN, int BMX = BM>
 __device__ __forceinline__ void load_frags(bf16x8 (&af)[TM], bf16x8 (&bf)[TN],
                                            const u32x4 *stage, int wm, int wn,
                                            int lane, int kk) {
+    static_assert(BMX <= BM && TM * 32 * WM == BMX, "tile rows");
     const u32x4 *sA = stage;
     const u32x4 *sB = stage + BM * 8;
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int ar = wm * (BM / WM) + i * 32 + (lane & 31);
+        const int ar = wm * (BMX / WM) + i * 32 + (lane & 31);
         af[i] = as_bf16x8(sA[ar * 8 + (c ^ ((ar >> 1) & 7))]);
     }
 #pragma unroll
@@ -568,38 +572,49 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
                 dma16(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
         };
 
-        floatx16 acc[TM][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
         wait_vmcnt<0>();   // previous tile's stores are done
         issue(0);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        bf16x8 fa[2][TM], fb[2][TN];
-        for (int kt = 0; kt < KT; ++kt) {
-            // the other slot was last read in step kt-1, before its barrier
-            if (kt + 1 < KT) issue(kt + 1);
-            const u32x4 *stage = smem + (kt & 1) * STAGE;
-            load_frags<BM, BN, WM, WN, TM, TN>(fa[0], fb[0], stage, wm, wn,
-                                               lane, 0);
+        // The tile's MFMAs over BMX rows (BMX = BM, or 256 for a group of
+        // at most 256 rows in 320-row stages: 8 instead of 10 row blocks per
+        // SIMD, the DeepSeek-shaped groups being 256 +- 17 rows).  Each
+        // height has its own accumulators, live only in its own branch.
+        auto compute = [&](auto bmx) __attribute__((always_inline)) {
+            constexpr int BMX = decltype(bmx)::value;
+            constexpr int TMX = BMX / (WM * 32);
+            floatx16 acc[TMX][TN];
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                if (kk + 1 < BK / 16)
-                    load_frags<BM, BN, WM, WN, TM, TN>(
-                        fa[(kk + 1) & 1], fb[(kk + 1) & 1], stage, wm, wn, lane,
-                        kk + 1);
-                mfma_block<TM, TN>(acc, fa[kk & 1], fb[kk & 1]);
+            for (int i = 0; i < TMX; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            bf16x8 fa[2][TMX], fb[2][TN];
+            for (int kt = 0; kt < KT; ++kt) {
+                // the other slot was last read in step kt-1, before its barrier
+                if (kt + 1 < KT) issue(kt + 1);
+                const u32x4 *stage = smem + (kt & 1) * STAGE;
+                load_frags<BM, BN, WM, WN, TMX, TN, BMX>(fa[0], fb[0], stage,
+                                                         wm, wn, lane, 0);
+#pragma unroll
+                for (int kk = 0; kk < BK / 16; ++kk) {
+                    if (kk + 1 < BK / 16)
+                        load_frags<BM, BN, WM, WN, TMX, TN, BMX>(
+                            fa[(kk + 1) & 1], fb[(kk + 1) & 1], stage, wm, wn,
+                            lane, kk + 1);
+                    mfma_block<TMX, TN>(acc, fa[kk & 1], fb[kk & 1]);
+                }
+                wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
             }
-            wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        store_tile<BM, BN, WM, WN, TM, TN, UP>(p, acc, routed, g, row0, nrows,
-                                               n0, wm, wn, lane);
+            store_tile<BMX, BN, WM, WN, TMX, TN, UP>(p, acc, routed, g, row0,
+                                                     nrows, n0, wm, wn, lane);
+        };
+        if (BM == 320 && nrows <= 256)
+            compute(std::integral_constant<int, BM == 320 ? 256 : BM>{});
+        else
+            compute(std::integral_constant<int, BM>{});
     }
 }
 
