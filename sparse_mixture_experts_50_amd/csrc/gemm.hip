@@ -695,7 +695,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                                         int wave, int lane, int kt0, int KT,
                                         int ks) {
     using namespace w4;
-    static_assert(WR == 128 || (WR == 112 && !HALF), "wave rows");
+    static_assert(WR == 128 || ((WR == 112 || WR == 96 || WR == 80) && !HALF),
+                  "wave rows");
     constexpr int TN = HALF ? 4 : 8;          // 16-column blocks per wave
     constexpr int WC = HALF ? 64 : 128;       // columns per wave
     constexpr int RB = HALF ? 8 : WR / 16;    // 16-row blocks per wave
@@ -984,9 +985,18 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
 // side and share it through L2; the half tiles instead come after every
 // full tile, and by then their panels have left L2 (the Mixtral up GEMM
 // fetched ~0.9 GB more than its weights and rows for them).
-__device__ __forceinline__ bool w4_even_group(int rows) {
+// Two-tile groups (257..384 rows) split the same way: two tiles of 160 or
+// 192 rows instead of a full tile and a half tile, the half tile being the
+// one that would re-read the weight panel long after (DeepSeek-shaped
+// groups of 256 +- 17 rows: about half of them).
+__device__ __forceinline__ int w4_even_rows(int rows) {
     const int m = (rows + 255) >> 8, rem = rows & 255;
-    return m >= 3 && rem >= 1 && rem <= 128 && m * 224 >= rows;
+    if (rem < 1 || rem > 128) return 0;
+    if (m == 2) return rows <= 320 ? 160 : 192;
+    return m >= 3 && m * 224 >= rows ? 224 : 0;
+}
+__device__ __forceinline__ bool w4_even_group(int rows) {
+    return w4_even_rows(rows) != 0;
 }
 
 template <bool UP, int TM_ROWS>
@@ -1065,7 +1075,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
                            : __builtin_amdgcn_readfirstlane(tf.mt[g]);
         }
         const int grows = __builtin_amdgcn_readfirstlane(tf.rows[g]);
-        const int tm = TM_ROWS == 256 && S == 1 && w4_even_group(grows) ? 224 : TM_ROWS;
+        const int ev_rows = TM_ROWS == 256 && S == 1 ? w4_even_rows(grows) : 0;
+        const int tm = ev_rows ? ev_rows : TM_ROWS;
         const int row0 = __builtin_amdgcn_readfirstlane(tf.start[g]) + m_tile * tm;
         const int nrows = min(tm, grows - m_tile * tm);
         const int n0 = n_tile * BN;
@@ -1080,6 +1091,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         else if (tm == 224)
             w4_tile<UP, false, false, 112>(p, slot0, slot1, g, row0, nrows, n0,
                                            routed, wave, lane, 0, KT, 0);
+        else if (tm == 192)
+            w4_tile<UP, false, false, 96>(p, slot0, slot1, g, row0, nrows, n0,
+                                          routed, wave, lane, 0, KT, 0);
+        else if (tm == 160)
+            w4_tile<UP, false, false, 80>(p, slot0, slot1, g, row0, nrows, n0,
+                                          routed, wave, lane, 0, KT, 0);
         else
             w4_tile<UP, false, false>(p, slot0, slot1, g, row0, nrows, n0,
                                       routed, wave, lane, 0, KT, 0);

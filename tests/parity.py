@@ -72,11 +72,11 @@ def sample_tokens(T: int, n: int, seed: int = 0, must=()) -> np.ndarray:
 
 # Row-tile heights of the grouped-GEMM variants (internal ids reported by
 # moe_gemm_variant), with the wave-row boundaries inside a tile.  The
-# four-wave 256-row kernel (14) also runs 224-row tiles (evenly split
-# groups, waves of 112 rows) and 128-row half tiles.  The eight-wave 320-row
+# four-wave 256-row kernel (14) also runs 224-, 192- and 160-row tiles
+# (evenly split groups) and 128-row half tiles.  The eight-wave 320-row
 # kernel (13) runs a group of at most 256 rows as a 256-row tile.
 TILE_ROWS = {0: (256,), 1: (128,), 2: (32,), 3: (64,), 5: (256,), 6: (128,),
-             8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 128),
+             8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 192, 160, 128),
              15: (128,), 20: (128,)}
 
 

@@ -258,11 +258,11 @@ PICKS = {
     "switch_top1_cap": (2, 15),
     "mixtral_prefill": (14, 14),
     "mixtral_decode": (18, 18),
-    "deepseek_v3": (13, 13),
+    "deepseek_v3": (13, 14),
     "mixtral_decode_fp8": (19, 19),
     "mixtral_prefill_swiglu": (14, 14),
     "mixtral_decode_swiglu": (11, 18),
-    "expert_choice_c2": (8, 8),
+    "expert_choice_c2": (8, 14),
 }
 
 

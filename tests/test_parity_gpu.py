@@ -344,12 +344,13 @@ def test_zero_tokens():
     assert y.shape == (0, 256)
 
 
-@pytest.mark.parametrize("C", [513, 640, 700, 257])
+@pytest.mark.parametrize("C", [513, 640, 700, 257, 300, 320, 321, 384, 385])
 def test_four_wave_even_split_group_sizes(C, monkeypatch):
     """Expert-Choice routing gives every expert exactly C rows.  Without
     split tails, 513 and 640 rows run as three 224-row tiles (the last of
-    65 / 192 rows); 700 rows (a 188-row last block) and 257 rows (two
-    tiles) keep 256-row and half-height tiles."""
+    65 / 192 rows); 700 rows (a 188-row last block) keep 256-row tiles;
+    257..320 rows run as two 160-row tiles and 321..384 as two 192-row
+    tiles; 385 rows (a 129-row last block) as two full-height tiles."""
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
     monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
