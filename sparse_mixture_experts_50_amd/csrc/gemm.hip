@@ -1104,6 +1104,480 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------
+// The four-wave 256 x 256 tile with v_mfma_f32_32x32x16_bf16 instead of
+// 16x16x32.  Same LDS stages (64-deep, two slots, the same direct loads and
+// swizzle), the same one wave per SIMD with 256 AGPR accumulators, but a
+// wave's 128 x 128 quarter is 4 x 4 blocks of 32 x 32, half as many MFMA
+// instructions for the same work.  Measured on gfx950 with one wave per
+// SIMD and fragment reads prefetched a step ahead: 16x16x32 with one
+// ds_read_b128 per four MFMAs issues at 18.4 clocks per 16-clock MFMA,
+// 32x32x16 with one read per two MFMAs (the same bytes per FLOP) at 32.9
+// per 32-clock MFMA.  A 64-deep stage is four 16-deep steps; the fragments
+// of steps 2 and 3 are read during step 1, so that after the mid-stage
+// barrier nothing reads the slot any more and the loads of the stage after
+// next go into it during steps 2 and 3 while step 2 reads the next stage's
+// first fragments from the other slot.  Tile heights are multiples of 64
+// (32-row MFMA blocks, two wave rows): 256, 192 and 128 full-width tiles
+// and the 128 x 256 half tile (the waves then split the columns).
+namespace w4x {
+using w4::BM;
+using w4::BN;
+using w4::CPR;
+using w4::LPW;
+using w4::SK;
+
+__device__ __forceinline__ void mfma32_agpr(floatx16 &acc, const bf16x8 &a,
+                                            const bf16x8 &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+}
+}  // namespace w4x
+
+// bias[f0 + 8 q + t] (q, t < 4) into v[q][t] as bf16 -> f32 (zeros without
+// a bias): the 16 columns a lane of a 32 x 32 output block holds.
+__device__ __forceinline__ void load_bias_q4(const uint16_t *bias, int f0,
+                                             float (&v)[4][4]) {
+    if (bias) {
+        u32x2 bb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bb[q] = *(const u32x2 *)(bias + f0 + 8 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[q][0] = bf16_lo(bb[q].x);
+            v[q][1] = bf16_hi(bb[q].x);
+            v[q][2] = bf16_lo(bb[q].y);
+            v[q][3] = bf16_hi(bb[q].y);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[q][t] = 0.0f;
+    }
+}
+
+// One tile.  HALF: at most 128 rows, waves 128 x 64.  Otherwise 2 WR rows,
+// waves 2 x 2 quarters of WR x 128.  PART: fp32 sums of stages kt0 ..
+// kt0 + KT - 1 into the tail partial buffer (plane ks), as w4_tile.
+template <bool UP, bool HALF, bool PART, int WR = 128>
+__device__ __forceinline__ void w4x_tile(const GemmParams &p, u32x4 *slot0,
+                                         u32x4 *slot1, int g, int row0,
+                                         int nrows, int n0, bool routed,
+                                         int wave, int lane, int kt0, int KT,
+                                         int ks) {
+    using namespace w4x;
+    static_assert(WR == 128 || ((WR == 96 || WR == 64) && !HALF), "wave rows");
+    constexpr int TN = HALF ? 2 : 4;          // 32-column blocks per wave
+    constexpr int WC = HALF ? 64 : 128;       // columns per wave
+    constexpr int RB = HALF ? 4 : WR / 32;    // 32-row blocks per wave
+    constexpr int WRR = HALF ? 128 : WR;      // rows per wave
+    constexpr int TR = HALF ? 128 : 2 * WR;   // tile rows
+    constexpr int LA = TR / 32;               // A loads per wave and stage
+    constexpr int NL = LA + LPW;              // loads per wave and stage
+    constexpr int NF = RB + TN;               // fragment reads per step
+    constexpr int NM = RB * TN;               // MFMAs per step
+    constexpr int DM = (2 * NM) / NL;         // a load every DM MFMAs
+    static_assert(DM >= 1 && DM * NL <= 2 * NM, "load slots");
+    // the lane index made opaque once per tile (addresses recomputed per
+    // tile, not hoisted out of the tile loop and spilled)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    const int wm = HALF ? 0 : wave >> 1;
+    const int wn = HALF ? wave : wave & 1;
+    const int N = p.N, K = p.K;
+    const char *A = (const char *)p.A;
+    const int lr = lane >> 3;
+    const int ch = (lane & 7) ^ ((4 * wave + (lr >> 1)) & 7);
+    const uint32_t b_lane = (uint32_t)(lr * K + ch * 8) * 2u;
+    const int l32 = lane & 31;
+    const int hk = lane >> 5;                 // k half of a 16-deep step
+    const int sw = (l32 >> 1) & 7;            // row swizzle of l32's rows
+
+    uint32_t a_off[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        int rr = (wave + 4 * j) * 8 + lr;
+        if (rr >= nrows) rr = 0;
+        const int slot = row0 + rr;
+        int src = slot;
+        if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
+        a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
+    }
+    const char *bbase[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+        bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
+
+    auto dma_one = [&](int kl, u32x4 *st, int q) __attribute__((always_inline)) {
+        const size_t ko = (size_t)(kt0 + kl) * SK * 2;
+        if (q < LA)
+            w4::dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
+        else
+            w4::dma16b(bbase[q - LA] + ko + b_lane,
+                       st + BM * CPR + (wave + 4 * (q - LA)) * 64);
+    };
+    // fragment q (q < RB: A block q, else B block q - RB) of 16-deep step t
+    auto frag_one = [&](bf16x8 (&fa)[RB], bf16x8 (&fb)[TN], const u32x4 *st,
+                        int t, int q) __attribute__((always_inline)) {
+        const int c = (t * 2 + hk) ^ sw;
+        if (q < RB)
+            fa[q] = as_bf16x8(st[(wm * WRR + q * 32 + l32) * CPR + c]);
+        else
+            fb[q - RB] = as_bf16x8(
+                st[BM * CPR + (wn * WC + (q - RB) * 32 + l32) * CPR + c]);
+    };
+
+    floatx16 acc[RB][TN];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    bf16x8 a0[RB], b0[TN], a1[RB], b1[TN], a2[RB], b2[TN], a3[RB], b3[TN];
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < NL; ++q) dma_one(0, slot0, q);
+#pragma unroll
+    for (int q = 0; q < NL; ++q) dma_one(min(1, KT - 1), slot1, q);
+    wait_vmcnt<NL>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < NF; ++q) frag_one(a0, b0, slot0, 0, q);
+
+    // MFMAs of one step on (fa, fb), with R reads (index r: r < NF the
+    // fragments of ra/rb at step rt, else of rc/rd at step rt + 1, all from
+    // rs) spread over them, and (LD) loads d0 .. of the stage after next.
+    auto step = [&](const bf16x8 (&fa)[RB], const bf16x8 (&fb)[TN],
+                    auto nreads, bf16x8 (&ra)[RB], bf16x8 (&rb)[TN],
+                    bf16x8 (&rc)[RB], bf16x8 (&rd)[TN], const u32x4 *rs,
+                    int rt, auto ld, int d0, int kload, u32x4 *lslot)
+                    __attribute__((always_inline)) {
+        constexpr int R = decltype(nreads)::value;
+        constexpr bool LD = decltype(ld)::value;
+#pragma unroll
+        for (int x = 0; x < NM; ++x) {
+            mfma32_agpr(acc[x / TN][x % TN], fb[x % TN], fa[x / TN]);
+#pragma unroll
+            for (int r = (x * R) / NM; r < ((x + 1) * R) / NM; ++r) {
+                if (r < NF) frag_one(ra, rb, rs, rt, r);
+                else frag_one(rc, rd, rs, rt + 1, r - NF);
+            }
+            if (LD && x % DM == 0 && d0 + x / DM < NL && x / DM < (NM + DM - 1) / DM)
+                dma_one(kload, lslot, d0 + x / DM);
+        }
+    };
+    constexpr int LD2 = (NM + DM - 1) / DM;   // loads issued in step 2
+    auto stage = [&](int s, u32x4 *cur, u32x4 *nxt) __attribute__((always_inline)) {
+        const int nx = min(s + 2, KT - 1);
+        // step 0 (fragments a0/b0): read step 1's from cur
+        step(a0, b0, std::integral_constant<int, NF>{}, a1, b1, a1, b1, cur, 1,
+             std::false_type{}, 0, nx, cur);
+        // step 1: read steps 2 and 3 from cur
+        step(a1, b1, std::integral_constant<int, 2 * NF>{}, a2, b2, a3, b3, cur,
+             2, std::false_type{}, 0, nx, cur);
+        // own reads done, stage s+1 landed (this wave's part), then every
+        // wave's part: nothing reads cur after this barrier
+        __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4));
+        __builtin_amdgcn_s_barrier();
+        // step 2: read the next stage's step 0 from nxt, load stage s+2
+        step(a2, b2, std::integral_constant<int, NF>{}, a0, b0, a0, b0, nxt, 0,
+             std::true_type{}, 0, nx, cur);
+        // step 3: the rest of the loads
+        step(a3, b3, std::integral_constant<int, 0>{}, a0, b0, a0, b0, nxt, 0,
+             std::true_type{}, LD2, nx, cur);
+    };
+    for (int s = 0; s < KT; s += 2) {
+        asm volatile("s_nop 4");
+        stage(s, slot0, slot1);
+        stage(s + 1, slot1, slot0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    }
+    // lane l holds, for row l32 of each 32 x 32 block, output columns
+    // 8 q + 4 hk + 0..3 (q = 0..3): acc[i][j][4 q + t]
+    if (PART) {
+        const int G = p.E + p.n_shared;
+        float *dst = p.part + ((size_t)ks * G + g) * 128 * N;
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int r = wm * WRR + i * 32 + l32;
+            if (r >= nrows) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = n0 + wn * WC + j * 32 + 8 * q + 4 * hk;
+                    *(float4 *)(dst + (size_t)r * N + c) =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                    acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                }
+        }
+        return;
+    }
+    // Epilogue through LDS, as w4_tile: bias and activation (or SwiGLU) to
+    // bf16 into a staging copy of the output tile in the idle slots (rows
+    // 0-127 in slot0, 128-255 in slot1, 512-byte rows with 16-byte chunks
+    // XOR-swizzled by the row), then whole row segments with 16-byte stores.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    auto put = [&](int R, int c, const float (&v)[4]) __attribute__((always_inline)) {
+        char *stg = (char *)(R < 128 ? slot0 : slot1);
+        const int rl = R & 127;
+        const int sc = (c >> 3) ^ (rl & 15);
+        u32x2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *(u32x2 *)(stg + rl * 512 + sc * 16 + ((c >> 2) & 1) * 8) = o;
+    };
+    const bool gated = UP && p.gated;
+    if (gated) {
+        // wave columns are whole 64-column chunks of the virtual panel:
+        // block 2c the gate rows and 2c + 1 the up rows of output features
+        // WC wn / 2 + 32 c + 8 q + 4 hk + t
+        constexpr int NC = WC / 64;
+        const int F = N >> 1;
+        const uint16_t *bp1 = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const uint16_t *bp3 = routed
+            ? (p.bias3 ? (const uint16_t *)p.bias3 + (size_t)g * F : nullptr)
+            : (const uint16_t *)p.bias_s3;
+        const int fb0 = (n0 >> 1) + (WC / 2) * wn + 4 * hk;
+        float bv1[NC][4][4], bv3[NC][4][4];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            load_bias_q4(bp1 ? bp1 + 32 * c : nullptr, fb0, bv1[c]);
+            load_bias_q4(bp3 ? bp3 + 32 * c : nullptr, fb0, bv3[c]);
+        }
+        auto swiglu = [&](auto bias) __attribute__((always_inline)) {
+            constexpr bool BIAS = decltype(bias)::value;
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float h[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            float gv = acc[i][2 * c][4 * q + t];
+                            float uv = acc[i][2 * c + 1][4 * q + t];
+                            if (BIAS) {
+                                gv += bv1[c][q][t];
+                                uv += bv3[c][q][t];
+                            }
+                            h[t] = silu_f(gv) * uv;
+                        }
+                        put(wm * WRR + i * 32 + l32,
+                            (WC / 2) * wn + 32 * c + 8 * q + 4 * hk, h);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (bp1 || bp3) swiglu(std::true_type{});
+        else swiglu(std::false_type{});
+    } else {
+        const uint16_t *bg = routed
+            ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
+            : (const uint16_t *)p.bias_s;
+        const int act = !UP ? -1 : p.act == ACT_SILU ? ACT_SILU : ACT_GELU;
+        // bias of columns wn WC + 32 j + 8 q + 4 hk + t
+        float bv[TN][4][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            load_bias_q4(bg ? bg + 32 * j : nullptr, n0 + wn * WC + 4 * hk, bv[j]);
+        auto convert = [&](auto fn, auto bias) __attribute__((always_inline)) {
+            constexpr bool BIAS = decltype(bias)::value;
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[t] = fn(BIAS ? acc[i][j][4 * q + t] + bv[j][q][t]
+                                           : acc[i][j][4 * q + t]);
+                        put(wm * WRR + i * 32 + l32, wn * WC + j * 32 + 8 * q + 4 * hk, v);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto with_act = [&](auto bias) __attribute__((always_inline)) {
+            if (act == ACT_GELU)
+                convert([](float z) __attribute__((always_inline)) { return gelu_erf(z); }, bias);
+            else if (act == ACT_SILU)
+                convert([](float z) __attribute__((always_inline)) { return silu_f(z); }, bias);
+            else
+                convert([](float z) __attribute__((always_inline)) { return z; }, bias);
+        };
+        if (!UP || bg) with_act(std::true_type{});
+        else with_act(std::false_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    const int cpr = gated ? 16 : 32;
+    const int rpp = 256 / cpr;
+    const int rr = tid / cpr, cc = tid % cpr;
+    uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
+    for (int r0 = 0; r0 < TR; r0 += rpp) {
+        const int row = r0 + rr;
+        if (row < nrows) {
+            const char *sb = (const char *)(row < 128 ? slot0 : slot1);
+            const int rl = row & 127;
+            const u32x4 v = *(const u32x4 *)(sb + rl * 512 + ((cc ^ (rl & 15)) * 16));
+            *(u32x4 *)(out + (size_t)(row0 + row) * p.ldo) = v;
+        }
+    }
+}
+
+// Row tiles of a group of `rows` rows for the 32x32 four-wave kernel
+// without split tails: m = ceil(rows / 256) tiles whose heights (256, 192
+// or 128, in that order) hold the group with the least padding; a group of
+// at most 128 rows is one half tile instead (counted in th, not here).
+struct W4xSplit {
+    int n256, n192, n128;
+};
+__device__ __forceinline__ W4xSplit w4x_split(int rows) {
+    W4xSplit s = {0, 0, 0};
+    if (rows <= 128) return s;
+    const int m = (rows + 255) >> 8;
+    const int x = (256 * m - rows) >> 6;      // 64-row reductions
+    s.n128 = max(0, x - m);
+    s.n192 = x - 2 * s.n128;
+    s.n256 = m - s.n192 - s.n128;
+    return s;
+}
+
+template <bool UP, int TM_ROWS>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4x(GemmParams p) {
+    using namespace w4;
+    __shared__ u32x4 slot0[STAGE], slot1[STAGE];
+    __shared__ TileTable tf, th;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KT = p.K / SK;
+    const int NTN = p.N / BN;
+    const int G = p.E + p.n_shared;
+    // S > 1: the half tiles run as S units each over a 1/S range of K, and
+    // full tiles are whole 256-row blocks; S == 1: mixed heights
+    const int S = TM_ROWS == 256 && p.tail_split > 1 ? p.tail_split : 1;
+    if (TM_ROWS == 128) {
+        build_tile_table(tf, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
+                         128, NTN);
+    } else {
+        build_tile_table_by(tf, p.offsets, p.E, p.n_shared, p.shared_base,
+                            p.T, NTN, [S](int rows) {
+                                if (S > 1) return (rows >> 8) + ((rows & 255) > 128);
+                                const W4xSplit w = w4x_split(rows);
+                                return w.n256 + w.n192 + w.n128;
+                            });
+        build_tile_table_by(th, p.offsets, p.E, p.n_shared, p.shared_base,
+                            p.T, NTN, [S](int rows) {
+                                if (S > 1) {
+                                    const int rem = rows & 255;
+                                    return rem > 0 && rem <= 128 ? 1 : 0;
+                                }
+                                return rows > 0 && rows <= 128 ? 1 : 0;
+                            });
+    }
+    const int total_f = __builtin_amdgcn_readfirstlane(tf.base[G]);
+    const int total = total_f + (TM_ROWS == 128
+                                     ? 0
+                                     : S * __builtin_amdgcn_readfirstlane(th.base[G]));
+    const int nb = gridDim.x, per = nb >> 3;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const bool halves_last = TM_ROWS == 256 && (S > 1 || total >= 4 * nb);
+    for (int r = 0;; ++r) {
+        const int L = r * nb + xcd * per + loc;
+        if (L >= total) break;
+        int g, n_tile, m_tile, ks = 0;
+        bool half;
+        if (!halves_last) {
+            int lo = 0, hi = G;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (tf.base[mid] + (TM_ROWS == 256 ? th.base[mid] : 0) <= L) lo = mid;
+                else hi = mid;
+            }
+            g = __builtin_amdgcn_readfirstlane(lo);
+            const int base = tf.base[g] + (TM_ROWS == 256 ? th.base[g] : 0);
+            const int mt = tf.mt[g] + (TM_ROWS == 256 ? th.mt[g] : 0);
+            const int local = __builtin_amdgcn_readfirstlane(L - base);
+            n_tile = local / mt;
+            m_tile = local - n_tile * mt;
+            half = TM_ROWS == 128 || m_tile >= tf.mt[g];
+        } else {
+            const bool first = L < total_f;
+            const TileTable &tt = first ? tf : th;
+            int Lg = first ? L : L - total_f;
+            if (!first) {
+                ks = Lg % S;
+                Lg /= S;
+            }
+            g = __builtin_amdgcn_readfirstlane(find_group(tt, G, Lg));
+            const int local = Lg - __builtin_amdgcn_readfirstlane(tt.base[g]);
+            const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
+            n_tile = local / mt;
+            m_tile = first ? local - n_tile * mt
+                           : __builtin_amdgcn_readfirstlane(tf.mt[g]);
+            half = !first;
+        }
+        const int grows = __builtin_amdgcn_readfirstlane(tf.rows[g]);
+        const int gstart = __builtin_amdgcn_readfirstlane(tf.start[g]);
+        int tm = TM_ROWS, off = m_tile * TM_ROWS;
+        if (TM_ROWS == 256 && !half) {
+            if (S > 1) {
+                tm = 256;
+                off = m_tile * 256;
+            } else {
+                const W4xSplit w = w4x_split(grows);
+                if (m_tile < w.n256) {
+                    tm = 256;
+                    off = m_tile * 256;
+                } else if (m_tile < w.n256 + w.n192) {
+                    tm = 192;
+                    off = w.n256 * 256 + (m_tile - w.n256) * 192;
+                } else {
+                    tm = 128;
+                    off = w.n256 * 256 + w.n192 * 192 + (m_tile - w.n256 - w.n192) * 128;
+                }
+            }
+        } else if (TM_ROWS == 256 && half) {
+            // the group's rows after its full tiles
+            off = S > 1 ? (tf.mt[g]) * 256 : 0;
+            tm = 128;
+        }
+        const int row0 = gstart + off;
+        const int nrows = min(tm, grows - off);
+        const int n0 = n_tile * BN;
+        const bool routed = g < p.E;
+        if (S > 1 && L >= total_f)
+            w4x_tile<UP, true, true>(p, slot0, slot1, g, row0, nrows, n0,
+                                     routed, wave, lane, ks * (KT / S), KT / S,
+                                     ks);
+        else if (half || TM_ROWS == 128)
+            w4x_tile<UP, true, false>(p, slot0, slot1, g, row0, nrows, n0,
+                                      routed, wave, lane, 0, KT, 0);
+        else if (tm == 256)
+            w4x_tile<UP, false, false, 128>(p, slot0, slot1, g, row0, nrows, n0,
+                                            routed, wave, lane, 0, KT, 0);
+        else if (tm == 192)
+            w4x_tile<UP, false, false, 96>(p, slot0, slot1, g, row0, nrows, n0,
+                                           routed, wave, lane, 0, KT, 0);
+        else
+            w4x_tile<UP, false, false, 64>(p, slot0, slot1, g, row0, nrows, n0,
+                                           routed, wave, lane, 0, KT, 0);
+    }
+}
+
+// ---------------------------------------------------------------------
 // Two blocks per CU: 128 x 256 tiles, four waves of 128 x 64 (8 x 4
 // v_mfma_f32_16x16x32_bf16 blocks, 128 accumulators as AGPR operands, as in
 // the four-wave kernel).  With one wave per SIMD the four-wave kernel's
@@ -2199,9 +2673,12 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool UP, int TM_ROWS>
+template <bool UP, int TM_ROWS, bool X32 = false>
 hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
+    if (X32)
+        hipLaunchKernelGGL((gemm_bf16_w4x<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
     if (TM_ROWS == 256 && p.tail_split > 1) {
         const int G = p.E + p.n_shared;
         const int oc = UP && p.gated ? p.N / 2 : p.N;
@@ -2242,6 +2719,8 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_DMA64_320x256: return {320, 256, 512, 2 * 576 * 128};
     case GEMM_BF16_W4_256x256: return {256, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_W4X_256x256: return {256, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_W4X_128x256: return {128, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_X2_128x256: return {128, 256, 256, 3 * 384 * 64};
     case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
     case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
@@ -2287,6 +2766,12 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_W4_128x256:
         return up ? launch_w4<true, 128>(p, grid, s)
                   : launch_w4<false, 128>(p, grid, s);
+    case GEMM_BF16_W4X_256x256:
+        return up ? launch_w4<true, 256, true>(p, grid, s)
+                  : launch_w4<false, 256, true>(p, grid, s);
+    case GEMM_BF16_W4X_128x256:
+        return up ? launch_w4<true, 128, true>(p, grid, s)
+                  : launch_w4<false, 128, true>(p, grid, s);
     case GEMM_BF16_X2_128x256:
         if (up)
             hipLaunchKernelGGL(gemm_bf16_x2<true>, dim3(grid), dim3(256), 0, s, p);

@@ -83,6 +83,8 @@ enum GemmVariant {
     GEMM_BF16_RING2_16x16 = 18,    // 1 KB row runs, two blocks per CU
     GEMM_FP8_RING2_16x16 = 19,
     GEMM_BF16_X2_128x256 = 20,     // two blocks per CU, 32-deep stages, K % 32 == 0
+    GEMM_BF16_W4X_256x256 = 21,    // variant 14 with 32x32x16 MFMAs, mixed tile heights
+    GEMM_BF16_W4X_128x256 = 22,    // variant 15 with 32x32x16 MFMAs
 };
 
 // Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),

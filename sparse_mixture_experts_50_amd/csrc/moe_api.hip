@@ -111,6 +111,12 @@ TileCount group_tiles(const moe_desc *d, int bm) {
 }
 
 int variant_override(bool up, const moe_desc *d, int N);
+
+// The four-wave 256-row kernels (16x16x32 and 32x32x16 MFMA forms), the
+// ones with split tails.
+bool w4_256(int v) {
+    return v == GEMM_BF16_W4_256x256 || v == GEMM_BF16_W4X_256x256;
+}
 bool w4_fits(const moe_desc *d, bool up);
 
 // Whether the four-wave 256-row kernel may run this GEMM: forced by the
@@ -119,7 +125,7 @@ bool w4_fits(const moe_desc *d, bool up);
 // device-dependent cost comparison may still pick another kernel).
 bool w4_256_possible(const moe_desc *d, bool up, int N) {
     const int forced = variant_override(up, d, N);
-    if (forced >= 0) return forced == GEMM_BF16_W4_256x256;
+    if (forced >= 0) return w4_256(forced);
     const double avg = (double)routed_rows(d) / d->E;
     const int K = up ? d->d : d->d_ff;
     const bool small_down = !up && avg > 192.0 && avg <= 384.0;
@@ -295,11 +301,11 @@ int variant_override(bool up, const moe_desc *d, int N) {
                         id == GEMM_FP8_RING_16x16 || id == GEMM_FP8_RING2_16x16;
     if (ring_variant(id) && !ring_fits(d, up, id)) return -1;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_X2_128x256 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4X_128x256 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
-    if ((id == GEMM_BF16_W4_256x256 || id == GEMM_BF16_W4_128x256) &&
+    if ((w4_256(id) || id == GEMM_BF16_W4_128x256 || id == GEMM_BF16_W4X_128x256) &&
         !w4_fits(d, up))
         return -1;
     if (id == GEMM_BF16_X2_128x256 && !x2_fits(d, up)) return -1;
@@ -599,7 +605,7 @@ int run_gemm(const moe_desc *d, const moe_weights *w, const moe_routing *r,
     // never lands on a variant that cannot pair gate and up columns
     if (gated_up(d, up) && !gate_capable(variant)) return MOE_ERR_UNSUPPORTED;
     const int grid = gemm_grid(d, variant, p.N);
-    if (variant == GEMM_BF16_W4_256x256) {
+    if (w4_256(variant)) {
         GemmParams q = p;
         q.tail_split = tail_split(d, up);
         // a split unit covers KT / S stages in whole stage pairs; any other
@@ -675,7 +681,7 @@ int moe_gemm_tail_split(const moe_desc *desc, int up) {
                      : desc->d;
     int v = variant_override(up != 0, desc, N);
     if (v < 0) v = pick_variant(desc, N, up != 0);
-    return v == GEMM_BF16_W4_256x256 ? tail_split(desc, up != 0) : 1;
+    return w4_256(v) ? tail_split(desc, up != 0) : 1;
 }
 
 size_t moe_workspace_size(const moe_desc *desc) {

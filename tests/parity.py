@@ -76,7 +76,8 @@ def sample_tokens(T: int, n: int, seed: int = 0, must=()) -> np.ndarray:
 # (evenly split groups) and 128-row half tiles.  The eight-wave 320-row
 # kernel (13) runs a group of at most 256 rows as a 256-row tile.
 TILE_ROWS = {0: (256,), 1: (128,), 2: (32,), 3: (64,), 5: (256,), 6: (128,),
-             8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 192, 160, 128),
+             8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 192, 160, 128), 21: (256, 192, 128),
+             22: (128,),
              15: (128,), 20: (128,)}
 
 

@@ -70,7 +70,8 @@ def test_small_full_parity(name):
 
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7", "8",
-                                     "9", "11", "13", "14", "15", "16", "20"])
+                                     "9", "11", "13", "14", "15", "16", "20",
+                                     "21", "22"])
 def test_every_gemm_variant(variant, monkeypatch):
     """Each bf16 tile variant forced on a shape with groups of 0 to ~100
     rows (several row chunks for the small-tile kernels)."""
@@ -83,7 +84,7 @@ def test_every_gemm_variant(variant, monkeypatch):
     say(f"[variant {variant}] {rep}")
 
 
-@pytest.mark.parametrize("variant", ["13", "14", "15", "20"])
+@pytest.mark.parametrize("variant", ["13", "14", "15", "20", "21", "22"])
 def test_large_tile_variants_multi_tile_groups(variant, monkeypatch):
     """The 320- and four-wave 256-row kernels on groups of ~600 rows (three
     row tiles, the last ragged), eight column tiles and 16 stages of K,
@@ -344,15 +345,20 @@ def test_zero_tokens():
     assert y.shape == (0, 256)
 
 
-@pytest.mark.parametrize("C", [513, 640, 700, 257, 300, 320, 321, 384, 385])
-def test_four_wave_even_split_group_sizes(C, monkeypatch):
+@pytest.mark.parametrize("kernel", ["14", "21"])
+@pytest.mark.parametrize("C", [513, 640, 700, 257, 300, 320, 321, 384, 385,
+                               129, 192, 193, 1049])
+def test_four_wave_even_split_group_sizes(C, kernel, monkeypatch):
     """Expert-Choice routing gives every expert exactly C rows.  Without
-    split tails, 513 and 640 rows run as three 224-row tiles (the last of
-    65 / 192 rows); 700 rows (a 188-row last block) keep 256-row tiles;
-    257..320 rows run as two 160-row tiles and 321..384 as two 192-row
-    tiles; 385 rows (a 129-row last block) as two full-height tiles."""
-    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
-    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+    split tails, the 16x16x32 four-wave kernel (14) runs 513 and 640 rows
+    as three 224-row tiles (the last of 65 / 192 rows); 700 rows (a 188-row
+    last block) keep 256-row tiles; 257..320 rows run as two 160-row tiles
+    and 321..384 as two 192-row tiles; 385 rows (a 129-row last block) as
+    two full-height tiles.  The 32x32x16 form (21) mixes 256-, 192- and
+    128-row tiles: 129..192 rows one 192-row tile, 257 rows 192 + 128, 385
+    rows 256 + 192, 1049 rows 2 x 256 + 3 x 192."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", kernel)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", kernel)
     monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
     w = scaled(W["expert_choice_c2"], T=2 * C, d=256, E=2, k=2, d_ff=512,
                capacity_factor=1.0)
@@ -360,4 +366,4 @@ def test_four_wave_even_split_group_sizes(C, monkeypatch):
     gpu = gpu_forward(w, inp)
     # (expert choice: every expert keeps exactly C rows)
     assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
-    say(f"[even split C={C}] {check_expert_choice(w, inp, gpu)}")
+    say(f"[even split C={C}, kernel {kernel}] {check_expert_choice(w, inp, gpu)}")

@@ -44,11 +44,16 @@ CASES = {
 }
 
 
+# the four-wave kernel in its two MFMA forms: 16x16x32 (14), 32x32x16 (21)
+FOUR_WAVE = ["14", "21"]
+
+
+@pytest.mark.parametrize("kernel", FOUR_WAVE)
 @pytest.mark.parametrize("split", ["8", "3", "1"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_tail_split_parity(name, split, monkeypatch):
-    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
-    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+def test_tail_split_parity(name, split, kernel, monkeypatch):
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", kernel)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", kernel)
     monkeypatch.setenv("MOE_TAIL_SPLIT", split)
     w = CASES[name]
     d = moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, torch.bfloat16,
@@ -60,15 +65,16 @@ def test_tail_split_parity(name, split, monkeypatch):
     gpu = gpu_forward(w, inp)
     tokens = sample_tokens(w.T, 64, seed=5)
     rep = check_layer(w, inp, gpu, tokens=tokens)
-    say(f"[tail split <= {split}, S up/down {S}] {name}: {rep}")
+    say(f"[tail split <= {split}, S up/down {S}, kernel {kernel}] {name}: {rep}")
 
 
+@pytest.mark.parametrize("kernel", FOUR_WAVE)
 @pytest.mark.parametrize("name", ["gelu_600", "swiglu_600"])
-def test_tail_split_matches_unsplit(name, monkeypatch):
+def test_tail_split_matches_unsplit(name, kernel, monkeypatch):
     w = CASES[name]
     inp = inputs_on(w, device())
-    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
-    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", kernel)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", kernel)
     out = {}
     for split in ("8", "1"):
         monkeypatch.setenv("MOE_TAIL_SPLIT", split)
