@@ -117,6 +117,10 @@ int variant_override(bool up, const moe_desc *d, int N);
 bool w4_256(int v) {
     return v == GEMM_BF16_W4_256x256 || v == GEMM_BF16_W4X_256x256;
 }
+// Any four-wave kernel (256-row or every tile 128 rows).
+bool w4_any(int v) {
+    return w4_256(v) || v == GEMM_BF16_W4_128x256 || v == GEMM_BF16_W4X_128x256;
+}
 bool w4_fits(const moe_desc *d, bool up);
 
 // Whether the four-wave 256-row kernel may run this GEMM: forced by the
@@ -305,8 +309,7 @@ int variant_override(bool up, const moe_desc *d, int N) {
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
-    if ((w4_256(id) || id == GEMM_BF16_W4_128x256 || id == GEMM_BF16_W4X_128x256) &&
-        !w4_fits(d, up))
+    if (w4_any(id) && !w4_fits(d, up))
         return -1;
     if (id == GEMM_BF16_X2_128x256 && !x2_fits(d, up)) return -1;
     // the streaming kernels split K in four quarters of whole load batches
