@@ -688,7 +688,9 @@ __device__ __forceinline__ void load_bias4(const uint16_t *bias, int f0,
 // partial buffer (plane ks) instead of finishing the tile.
 // WR: rows of a wave's part of a full tile, 128 (256-row tiles) or 112
 // (224-row tiles of evenly split groups: seven MFMA row blocks a wave).
-template <bool UP, bool HALF, bool PART, int WR = 128>
+// BN: tile columns, 256 or 192 (ungated only: a wave's 48 or 96 columns
+// are not whole 64-column gate/up chunks); the slots keep room for 256.
+template <bool UP, bool HALF, bool PART, int WR = 128, int BN = 256>
 __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                                         u32x4 *slot1, int g, int row0,
                                         int nrows, int n0, bool routed,
@@ -697,16 +699,21 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     using namespace w4;
     static_assert(WR == 128 || ((WR == 112 || WR == 96 || WR == 80) && !HALF),
                   "wave rows");
-    constexpr int TN = HALF ? 4 : 8;          // 16-column blocks per wave
-    constexpr int WC = HALF ? 64 : 128;       // columns per wave
+    static_assert(BN == 256 || BN == 192, "tile columns");
+    constexpr int TN = HALF ? BN / 64 : BN / 32;  // 16-column blocks per wave
+    constexpr int WC = TN * 16;               // columns per wave
     constexpr int RB = HALF ? 8 : WR / 16;    // 16-row blocks per wave
     constexpr int TR = HALF ? 128 : 2 * WR;   // tile rows
     constexpr int LA = TR / 32;               // A loads per wave and stage
-    constexpr int NL = LA + LPW;              // loads per wave and stage
+    constexpr int LB = BN / 32;               // B loads per wave and stage
+    constexpr int NL = LA + LB;               // loads per wave and stage
     constexpr int NF = RB + TN;               // fragment reads per sub-step
     constexpr int NM = RB * TN;               // MFMAs per sub-step
-    constexpr int RD = HALF ? 2 : 3;          // a read after every RD MFMAs
-    constexpr int DM = HALF ? 2 : WR == 128 ? 4 : 3;  // a load after every DM MFMAs
+    // a read after every RD MFMAs, a load after every DM (192 columns: as
+    // densely as the fewer MFMAs need)
+    constexpr int RD = BN == 192 ? 2 : HALF ? 2 : 3;
+    constexpr int DM = BN == 192 ? (NM - 2) / (NL - 1)
+                                 : HALF ? 2 : WR == 128 ? 4 : 3;
     static_assert(RD * (NF - 1) < NM && DM * (NL - 1) + 1 < NM, "issue slots");
     // The lane index is made opaque here, once per tile, so that the
     // per-lane addresses below are recomputed for each tile instead of
@@ -741,9 +748,9 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         if (UP) src = routed ? p.slot_token[slot] : slot - p.shared_base;
         a_off[j] = (uint32_t)(src * K + ch * 8) * 2u;
     }
-    const char *bbase[LPW];
+    const char *bbase[LB];
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
+    for (int j = 0; j < LB; ++j)
         bbase[j] = weight_row(p, routed, g, n0 + (wave + 4 * j) * 8, 2);
 
     // load q (q < LA: A rows, else B rows) of stage kt0 + kl into a slot
@@ -864,8 +871,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         o.y = pack_bf16x2(v[2], v[3]);
         *(u32x2 *)(stg + rl * 512 + sc * 16 + ((c >> 2) & 1) * 8) = o;
     };
-    const bool gated = UP && p.gated;
-    if (gated) {
+    const bool gated = BN == 256 && UP && p.gated;
+    if (gated) if constexpr (BN == 256) {
         // a wave's columns are whole 64-column chunks of the virtual panel:
         // blocks 4c, 4c+1 are the gate rows and 4c+2, 4c+3 the up rows of
         // the tile's output features WC wn / 2 + 32 c + 16 jj + ...
@@ -912,7 +919,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         };
         if (b1 || b3) swiglu(std::true_type{});
         else swiglu(std::false_type{});
-    } else {
+    }
+    if (!gated) {
         const uint16_t *bg = routed
             ? (p.bias ? (const uint16_t *)p.bias + (size_t)g * N : nullptr)
             : (const uint16_t *)p.bias_s;
@@ -952,14 +960,15 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     }
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    // 16-byte chunks per output row: 32 (256 columns) or 16 (gated)
-    const int cpr = gated ? 16 : 32;
+    // 16-byte chunks per output row: BN / 8 (32 or 24), or 16 (gated)
+    const int cpr = gated ? 16 : BN / 8;
     const int rpp = 256 / cpr;                 // rows per block pass
     const int rr = tid / cpr, cc = tid % cpr;
     uint16_t *out = (uint16_t *)p.out + (gated ? n0 >> 1 : n0) + cc * 8;
     for (int r0 = 0; r0 < TR; r0 += rpp) {
         const int row = r0 + rr;
-        if (row < nrows) {
+        // (24 chunks a row: the last 16 threads have no row in a pass)
+        if (row < nrows && (BN == 256 || rr < rpp)) {
             const char *sb = (const char *)(row < 128 ? slot0 : slot1);
             const int rl = row & 127;
             const u32x4 v = *(const u32x4 *)(sb + rl * 512 + ((cc ^ (rl & 15)) * 16));
@@ -988,9 +997,14 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
 // Two-tile groups (257..384 rows) split the same way: two tiles of 160 or
 // 192 rows instead of a full tile and a half tile, the half tile being the
 // one that would re-read the weight panel long after (DeepSeek-shaped
-// groups of 256 +- 17 rows: about half of them).
+// groups of 256 +- 17 rows: about half of them).  A one-tile group of
+// 129..224 rows runs as one tile of 160, 192 or 224 rows (fewer padded
+// MFMA rows than a 256-row tile).
 __device__ __forceinline__ int w4_even_rows(int rows) {
     const int m = (rows + 255) >> 8, rem = rows & 255;
+    // a group of 129..224 rows, one tile: trimmed to its height
+    if (m == 1 && rem > 128)
+        return rows <= 160 ? 160 : rows <= 192 ? 192 : rows <= 224 ? 224 : 0;
     if (rem < 1 || rem > 128) return 0;
     if (m == 2) return rows <= 320 ? 160 : 192;
     return m >= 3 && m * 224 >= rows ? 224 : 0;
@@ -999,7 +1013,9 @@ __device__ __forceinline__ bool w4_even_group(int rows) {
     return w4_even_rows(rows) != 0;
 }
 
-template <bool UP, int TM_ROWS>
+// TN_COLS: tile columns (256, or 192 for an ungated GEMM with N a multiple
+// of 192).
+template <bool UP, int TM_ROWS, int TN_COLS = 256>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     using namespace w4;
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
@@ -1007,7 +1023,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KT = p.K / SK;
-    const int NTN = p.N / BN;
+    const int NTN = p.N / TN_COLS;
     const int G = p.E + p.n_shared;
     if (TM_ROWS == 128) {
         build_tile_table(tf, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
@@ -1079,26 +1095,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         const int tm = ev_rows ? ev_rows : TM_ROWS;
         const int row0 = __builtin_amdgcn_readfirstlane(tf.start[g]) + m_tile * tm;
         const int nrows = min(tm, grows - m_tile * tm);
-        const int n0 = n_tile * BN;
+        const int n0 = n_tile * TN_COLS;
         const bool routed = g < p.E;
         if (S > 1 && L >= total_f)
-            w4_tile<UP, true, true>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, true, true, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                     routed, wave, lane, ks * (KT / S), KT / S,
                                     ks);
         else if (TM_ROWS == 128 || nrows <= 128)
-            w4_tile<UP, true, false>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, true, false, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                      routed, wave, lane, 0, KT, 0);
         else if (tm == 224)
-            w4_tile<UP, false, false, 112>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 112, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                            routed, wave, lane, 0, KT, 0);
         else if (tm == 192)
-            w4_tile<UP, false, false, 96>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 96, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                           routed, wave, lane, 0, KT, 0);
         else if (tm == 160)
-            w4_tile<UP, false, false, 80>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 80, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                           routed, wave, lane, 0, KT, 0);
         else
-            w4_tile<UP, false, false>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
                                       routed, wave, lane, 0, KT, 0);
     }
 }
@@ -2673,12 +2689,13 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool UP, int TM_ROWS, bool X32 = false>
+template <bool UP, int TM_ROWS, bool X32 = false, int TN_COLS = 256>
 hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
     if (X32)
         hipLaunchKernelGGL((gemm_bf16_w4x<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS, TN_COLS>), dim3(grid),
+                           dim3(256), 0, s, p);
     if (TM_ROWS == 256 && p.tail_split > 1) {
         const int G = p.E + p.n_shared;
         const int oc = UP && p.gated ? p.N / 2 : p.N;
@@ -2721,6 +2738,7 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_W4_128x256: return {128, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4X_256x256: return {256, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4X_128x256: return {128, 256, 256, 2 * 512 * 128};
+    case GEMM_BF16_W4_256x192: return {256, 192, 256, 2 * 512 * 128};
     case GEMM_BF16_X2_128x256: return {128, 256, 256, 3 * 384 * 64};
     case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
     case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
@@ -2772,6 +2790,9 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
     case GEMM_BF16_W4X_128x256:
         return up ? launch_w4<true, 128, true>(p, grid, s)
                   : launch_w4<false, 128, true>(p, grid, s);
+    case GEMM_BF16_W4_256x192:
+        return up ? launch_w4<true, 256, false, 192>(p, grid, s)
+                  : launch_w4<false, 256, false, 192>(p, grid, s);
     case GEMM_BF16_X2_128x256:
         if (up)
             hipLaunchKernelGGL(gemm_bf16_x2<true>, dim3(grid), dim3(256), 0, s, p);

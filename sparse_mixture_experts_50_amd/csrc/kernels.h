@@ -85,6 +85,7 @@ enum GemmVariant {
     GEMM_BF16_X2_128x256 = 20,     // two blocks per CU, 32-deep stages, K % 32 == 0
     GEMM_BF16_W4X_256x256 = 21,    // variant 14 with 32x32x16 MFMAs, mixed tile heights
     GEMM_BF16_W4X_128x256 = 22,    // variant 15 with 32x32x16 MFMAs
+    GEMM_BF16_W4_256x192 = 23,     // variant 14 with 192-column tiles (ungated, N % 192 == 0)
 };
 
 // Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),

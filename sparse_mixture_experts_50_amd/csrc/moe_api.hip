@@ -117,9 +117,11 @@ int variant_override(bool up, const moe_desc *d, int N);
 bool w4_256(int v) {
     return v == GEMM_BF16_W4_256x256 || v == GEMM_BF16_W4X_256x256;
 }
-// Any four-wave kernel (256-row or every tile 128 rows).
+// Any four-wave kernel (256-row or every tile 128 rows, 256 or 192
+// columns).
 bool w4_any(int v) {
-    return w4_256(v) || v == GEMM_BF16_W4_128x256 || v == GEMM_BF16_W4X_128x256;
+    return w4_256(v) || v == GEMM_BF16_W4_128x256 ||
+           v == GEMM_BF16_W4X_128x256 || v == GEMM_BF16_W4_256x192;
 }
 bool w4_fits(const moe_desc *d, bool up);
 
@@ -266,7 +268,7 @@ bool gated_up(const moe_desc *d, bool up) {
 // Variants whose waves hold whole 64-column chunks of the gated panel.
 bool gate_capable(int v) {
     return v != GEMM_BF16_64x64 && v != GEMM_BF16_STREAM_32x64 &&
-           v != GEMM_FP8_STREAM_32x64;
+           v != GEMM_FP8_STREAM_32x64 && v != GEMM_BF16_W4_256x192;
 }
 
 // The four-wave kernel walks K in pairs of 64-deep stages and addresses
@@ -305,7 +307,7 @@ int variant_override(bool up, const moe_desc *d, int N) {
                         id == GEMM_FP8_RING_16x16 || id == GEMM_FP8_RING2_16x16;
     if (ring_variant(id) && !ring_fits(d, up, id)) return -1;
     if (d->expert_fp8) return fp8_id ? id : -1;
-    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4X_128x256 ||
+    if (id < GEMM_BF16_256x256 || id > GEMM_BF16_W4_256x192 ||
         id == GEMM_F32_64x64 || fp8_id)
         return -1;
     if (N % gemm_variant_info(id).bn != 0) return -1;
@@ -389,6 +391,20 @@ int pick_variant(const moe_desc *d, int N, bool up) {
             return GEMM_BF16_32x256;
         if (avg > 96.0 && avg <= 192.0) return GEMM_BF16_DMA64_256x256;
     }
+    // Expert choice with 129..256 rows per expert, no shared expert, K >=
+    // 2048 and N a multiple of 192: every group is one full (or trimmed)
+    // tile of the four-wave kernel, so E (N / 256) tiles fill only part of
+    // the CUs' one round; with 192-column tiles, if E (N / 192) still fit
+    // one round, each tile has three quarters of the work (the
+    // Expert-Choice-shaped down GEMM: 64 x 4 = 256 tiles instead of 192,
+    // layer 0.326 -> 0.318 ms).  Not for groups of up to 128 rows: the
+    // Switch-shaped down GEMM (0-160 rows, mostly half tiles) ran 7 us
+    // slower than on 128 x 256 tiles.
+    if (!up && !gated_up(d, up) && N % 192 == 0 && K >= 2048 &&
+        expert_choice(d) && d->capacity > 128 && d->capacity <= 256 &&
+        d->n_shared == 0 && w4_fits(d, up) &&
+        (long long)d->E * (N / 192) <= device_cus())
+        return GEMM_BF16_W4_256x192;
     if (avg <= 128.0)
         return w4_fits(d, up) ? GEMM_BF16_W4_128x256 : GEMM_BF16_DMA64_256x256;
     if (avg <= 192.0) return GEMM_BF16_DMA64_256x256;

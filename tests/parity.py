@@ -77,7 +77,7 @@ def sample_tokens(T: int, n: int, seed: int = 0, must=()) -> np.ndarray:
 # kernel (13) runs a group of at most 256 rows as a 256-row tile.
 TILE_ROWS = {0: (256,), 1: (128,), 2: (32,), 3: (64,), 5: (256,), 6: (128,),
              8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 192, 160, 128), 21: (256, 192, 128),
-             22: (128,),
+             22: (128,), 23: (256, 224, 192, 160, 128),
              15: (128,), 20: (128,)}
 
 
@@ -93,7 +93,7 @@ def tile_cover_tokens(w: workloads.Workload, gpu: dict, variants) -> \
     off = gpu["offsets"].reshape(-1)
     st = gpu["slot_token"].reshape(-1)
     heights = sorted({h for v in variants for h in TILE_ROWS.get(v, (16,))})
-    four_wave = any(v in (14, 15) for v in variants)
+    four_wave = any(v in (14, 15, 23) for v in variants)
 
     def rows_of(R):
         rows = {0, R - 1}

@@ -252,7 +252,8 @@ def _desc_of(w):
 # (up, down) grouped-GEMM kernel ids the host picks on a 256-CU device
 # (host side only: no GPU needed).  4: fp32 SIMT; 8 / 13: eight-wave
 # 256- / 320-row tiles; 11 / 12: bf16 / FP8 weight streaming; 14: four-wave
-# 256-row tiles with half-height tails; 15: four-wave 128-row tiles.
+# 256-row tiles with half-height tails; 15: four-wave 128-row tiles; 23:
+# four-wave 256-row tiles of 192 columns.
 PICKS = {
     "tiny_top2_f32": (4, 4),
     "switch_top1_cap": (2, 15),
@@ -262,7 +263,7 @@ PICKS = {
     "mixtral_decode_fp8": (19, 19),
     "mixtral_prefill_swiglu": (14, 14),
     "mixtral_decode_swiglu": (11, 18),
-    "expert_choice_c2": (8, 14),
+    "expert_choice_c2": (8, 23),
 }
 
 

@@ -345,6 +345,45 @@ def test_zero_tokens():
     assert y.shape == (0, 256)
 
 
+@pytest.mark.parametrize("C", [100, 128, 129, 160, 161, 200, 224, 225, 256,
+                               300, 513])
+def test_four_wave_192_column_tiles(C, monkeypatch):
+    """The four-wave kernel with 192-column tiles (23) on Expert-Choice
+    groups of exactly C rows, d = 768 and d_ff = 1536 (both GEMMs' N a
+    multiple of 192): up to 128 rows a half tile, 129..224 rows one tile
+    of 160, 192 or 224 rows, 225..256 a full tile, 300 rows two 192-row
+    tiles, 513 rows three 224-row tiles."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "23")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "23")
+    monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
+    w = scaled(W["expert_choice_c2"], T=2 * C, d=768, E=2, k=2, d_ff=1536,
+               capacity_factor=1.0)
+    d = moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, torch.bfloat16,
+                      capacity=C, routing="expert_choice")
+    assert (moe.moe_gemm_variant(d, True), moe.moe_gemm_variant(d, False)) \
+        == (23, 23)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
+    say(f"[192 columns C={C}] {check_expert_choice(w, inp, gpu)}")
+
+
+def test_switch_down_192_column_tiles(monkeypatch):
+    """A Switch-shaped layer (capacity 160 rows: groups of 0..160 rows, half
+    tiles and trimmed 160-row tiles; N = 768 for the down GEMM) with the
+    192-column four-wave kernel forced on its down GEMM; every output row
+    against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "23")
+    w = scaled(W["switch_top1_cap"], T=2048, E=16)
+    d = moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, torch.bfloat16,
+                      capacity=moe.moe_capacity(w.T, w.E, w.capacity_factor))
+    assert moe.moe_gemm_variant(d, False) == 23
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    rep = check_layer(w, inp, gpu)
+    say(f"[switch 192 columns] {rep}")
+
+
 @pytest.mark.parametrize("kernel", ["14", "21"])
 @pytest.mark.parametrize("C", [513, 640, 700, 257, 300, 320, 321, 384, 385,
                                129, 192, 193, 1049])
@@ -356,7 +395,8 @@ def test_four_wave_even_split_group_sizes(C, kernel, monkeypatch):
     and 321..384 as two 192-row tiles; 385 rows (a 129-row last block) as
     two full-height tiles.  The 32x32x16 form (21) mixes 256-, 192- and
     128-row tiles: 129..192 rows one 192-row tile, 257 rows 192 + 128, 385
-    rows 256 + 192, 1049 rows 2 x 256 + 3 x 192."""
+    rows 256 + 192, 1049 rows 2 x 256 + 3 x 192.  (A one-tile group of
+    129..224 rows runs as one tile of 160, 192 or 224 rows in form 14.)"""
     monkeypatch.setenv("MOE_GEMM_VARIANT_UP", kernel)
     monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", kernel)
     monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
