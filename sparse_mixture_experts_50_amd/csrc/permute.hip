@@ -86,18 +86,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         for (; b < c1; ++b) part += p.blk[(size_t)b * p.E + e];
         seg_i[seg * p.E + e] = part;
     }
-    // 2. probability column sums over this segment's router blocks
+    // 2. probability column sums over this segment's router blocks, in
+    // block order; the loads of 32 blocks are issued before any is added
+    // (past the end a batch re-reads the last block and adds zero instead,
+    // which is exact: the sums are of probabilities, never -0)
     if (active) {
         float ps = 0.0f;
-        int b = seg;
-        for (; b + 31 * S < p.n_rtiles; b += 32 * S) {
+        for (int b = seg; b < p.n_rtiles; b += 32 * S) {
             float v[32];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) v[u] = p.p_part[(size_t)(b + u * S) * p.E + e];
+            for (int u = 0; u < 32; ++u) {
+                const int bu = b + u * S;
+                const float x = p.p_part[(size_t)min(bu, p.n_rtiles - 1) * p.E + e];
+                v[u] = bu < p.n_rtiles ? x : 0.0f;
+            }
 #pragma unroll
             for (int u = 0; u < 32; ++u) ps += v[u];
         }
-        for (; b < p.n_rtiles; b += S) ps += p.p_part[(size_t)b * p.E + e];
         seg_f[seg * p.E + e] = ps;
     }
     // 3. router z / entropy partials: all threads, then waves in order
