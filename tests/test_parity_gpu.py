@@ -345,6 +345,23 @@ def test_zero_tokens():
     assert y.shape == (0, 256)
 
 
+@pytest.mark.parametrize("C", [129, 192, 193, 257, 321, 513])
+def test_four_wave_trimmed_tiles_swiglu(C, monkeypatch):
+    """The gated (SwiGLU) epilogue on the four-wave kernel's shorter tiles:
+    one-tile groups of 129..224 rows (160-, 192- and 224-row tiles), the
+    two-tile even split (257 rows: 2 x 160, 321 rows: 2 x 192) and three
+    224-row tiles (513 rows), Expert-Choice groups of exactly C rows."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "14")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "14")
+    monkeypatch.setenv("MOE_TAIL_SPLIT", "1")
+    w = scaled(W["expert_choice_c2"], T=2 * C, d=256, E=2, k=2, d_ff=512,
+               capacity_factor=1.0, activation="swiglu")
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
+    say(f"[trimmed swiglu C={C}] {check_expert_choice(w, inp, gpu)}")
+
+
 @pytest.mark.parametrize("C", [100, 128, 129, 160, 161, 200, 224, 225, 256,
                                300, 513])
 def test_four_wave_192_column_tiles(C, monkeypatch):
