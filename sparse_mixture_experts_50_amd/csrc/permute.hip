@@ -317,11 +317,20 @@ __global__ __launch_bounds__(EC_THREADS) void ec_select(PermuteParams p) {
     const int s1 = min(T, s0 + L);
     const int n_i = L / 64;
     const int n_r = min(n_i, EC_KR);      // 64-token steps staged in LDS
-    // LDS slot of step i of this lane (wave-private, so no barrier needed)
+    // LDS slot of step i of this lane (wave-private, so no barrier needed).
+    // The EC_KR loads are issued together (addresses clamped into the
+    // row, the values past the segment then replaced by 0) rather than one
+    // wait per step.
     unsigned *kw = keys + wave * (EC_KR * 64) + lane;
-    for (int i = 0; i < n_r; ++i) {
-        const int t = s0 + 64 * i + lane;
-        kw[64 * i] = t < s1 ? order_key(sc[t]) : 0u;
+    {
+        float v[EC_KR];
+#pragma unroll
+        for (int i = 0; i < EC_KR; ++i) v[i] = sc[min(s0 + 64 * i + lane, T - 1)];
+#pragma unroll
+        for (int i = 0; i < EC_KR; ++i) {
+            const int t = s0 + 64 * i + lane;
+            if (i < n_r) kw[64 * i] = t < s1 ? order_key(v[i]) : 0u;
+        }
     }
 
     // thr = the C-th largest key; need = how many keys equal to thr are
