@@ -319,6 +319,7 @@ def main():
         roof["measured_dense_gemm_tflops"] = dense_gemm_tflops(
             alg["rows"], wl.d_ff * (2 if wl.activation == "swiglu" else 1),
             wl.d, dev)
+    roof["algorithmic_bytes"] = alg["up_bytes"]
     roof["traffic"] = recorded_traffic(wl.name)
     roof["kernel"] = "grouped GEMM up (moe_ffn_up)"
     # the library's kernel variant ids of the up and down GEMMs

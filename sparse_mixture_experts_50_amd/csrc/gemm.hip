@@ -330,6 +330,22 @@ __device__ __forceinline__ void dma16(const uint16_t *src, u32x4 *lds_row16) {
         (__attribute__((address_space(3))) void *)lds_row16, 16, 0, 0);
 }
 
+// The same load with the non-temporal hint, for weight panels that only
+// one row tile reads: their lines are not kept in the caches at the
+// expense of the gathered token rows, which every column tile of the group
+// reads again.  (Measured on the Expert-Choice-shaped layer, one 256-row
+// tile per expert: up GEMM 136 -> 131 us, 192-column down GEMM 124 -> 104,
+// layer 292 -> 272 us; DeepSeek-shaped up GEMM, 320-row tiles, 2.48 -> 2.41
+// ms.  Where two or more row tiles share a panel through L2 it is slower:
+// with every weight load non-temporal the DeepSeek-shaped down GEMM, whose
+// groups of 257..384 rows run as two tiles on one panel, took 2.44 -> 2.78
+// ms, and even there its one-tile groups alone gained nothing.)
+__device__ __forceinline__ void dma16_nt(const void *src, u32x4 *lds) {
+    __builtin_amdgcn_global_load_lds(
+        src, (__attribute__((address_space(3))) void *)lds, 16, 0,
+        2 /* non-temporal */);
+}
+
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -558,6 +574,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
             bp[j] = (const uint16_t *)weight_row(p, routed, g, n0 + rr, 2) +
                     ch * 8;
         }
+        // a weight panel that only this row tile reads is streamed
+        // non-temporally (uniform per tile)
+        const bool nt_b = mt == 1;
         // 8-row groups wholly past the group's end are not loaded (their
         // stale LDS rows only feed outputs that are never stored)
         auto issue = [&](int ks) __attribute__((always_inline)) {
@@ -567,9 +586,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
             for (int j = 0; j < IA; ++j)
                 if ((wave + j * NW) * 8 < nrows)
                     dma16(A + aoff[j] + ko, st + (wave + j * NW) * 64);
+            if (nt_b) {
 #pragma unroll
-            for (int j = 0; j < IB; ++j)
-                dma16(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+                for (int j = 0; j < IB; ++j)
+                    dma16_nt(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+            } else {
+#pragma unroll
+                for (int j = 0; j < IB; ++j)
+                    dma16(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+            }
         };
 
         wait_vmcnt<0>();   // previous tile's stores are done
@@ -690,7 +715,10 @@ __device__ __forceinline__ void load_bias4(const uint16_t *bias, int f0,
 // (224-row tiles of evenly split groups: seven MFMA row blocks a wave).
 // BN: tile columns, 256 or 192 (ungated only: a wave's 48 or 96 columns
 // are not whole 64-column gate/up chunks); the slots keep room for 256.
-template <bool UP, bool HALF, bool PART, int WR = 128, int BN = 256>
+// NT: weight rows loaded with the non-temporal hint (for GEMMs whose
+// groups are one row tile each).
+template <bool UP, bool HALF, bool PART, int WR = 128, int BN = 256,
+          bool NT = false>
 __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
                                         u32x4 *slot1, int g, int row0,
                                         int nrows, int n0, bool routed,
@@ -758,6 +786,9 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         const size_t ko = (size_t)(kt0 + kl) * SK * 2;
         if (q < LA)
             dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
+        else if (NT)
+            dma16_nt(bbase[q - LA] + ko + b_lane,
+                     st + BM * CPR + (wave + 4 * (q - LA)) * 64);
         else
             dma16b(bbase[q - LA] + ko + b_lane,
                    st + BM * CPR + (wave + 4 * (q - LA)) * 64);
@@ -1014,8 +1045,8 @@ __device__ __forceinline__ bool w4_even_group(int rows) {
 }
 
 // TN_COLS: tile columns (256, or 192 for an ungated GEMM with N a multiple
-// of 192).
-template <bool UP, int TM_ROWS, int TN_COLS = 256>
+// of 192).  NT: weights streamed with the non-temporal hint.
+template <bool UP, int TM_ROWS, int TN_COLS = 256, bool NT = false>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
     using namespace w4;
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
@@ -1098,23 +1129,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmParams p) {
         const int n0 = n_tile * TN_COLS;
         const bool routed = g < p.E;
         if (S > 1 && L >= total_f)
-            w4_tile<UP, true, true, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, true, true, 128, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                     routed, wave, lane, ks * (KT / S), KT / S,
                                     ks);
         else if (TM_ROWS == 128 || nrows <= 128)
-            w4_tile<UP, true, false, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, true, false, 128, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                      routed, wave, lane, 0, KT, 0);
         else if (tm == 224)
-            w4_tile<UP, false, false, 112, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 112, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                            routed, wave, lane, 0, KT, 0);
         else if (tm == 192)
-            w4_tile<UP, false, false, 96, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 96, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                           routed, wave, lane, 0, KT, 0);
         else if (tm == 160)
-            w4_tile<UP, false, false, 80, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 80, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                           routed, wave, lane, 0, KT, 0);
         else
-            w4_tile<UP, false, false, 128, TN_COLS>(p, slot0, slot1, g, row0, nrows, n0,
+            w4_tile<UP, false, false, 128, TN_COLS, NT>(p, slot0, slot1, g, row0, nrows, n0,
                                       routed, wave, lane, 0, KT, 0);
     }
 }
@@ -2689,12 +2720,13 @@ hipError_t launch_dma64(const GemmParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool UP, int TM_ROWS, bool X32 = false, int TN_COLS = 256>
+template <bool UP, int TM_ROWS, bool X32 = false, int TN_COLS = 256,
+          bool NT = false>
 hipError_t launch_w4(const GemmParams &p, int grid, hipStream_t s) {
     if (X32)
         hipLaunchKernelGGL((gemm_bf16_w4x<UP, TM_ROWS>), dim3(grid), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS, TN_COLS>), dim3(grid),
+        hipLaunchKernelGGL((gemm_bf16_w4<UP, TM_ROWS, TN_COLS, NT>), dim3(grid),
                            dim3(256), 0, s, p);
     if (TM_ROWS == 256 && p.tail_split > 1) {
         const int G = p.E + p.n_shared;
@@ -2791,8 +2823,10 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
         return up ? launch_w4<true, 128, true>(p, grid, s)
                   : launch_w4<false, 128, true>(p, grid, s);
     case GEMM_BF16_W4_256x192:
-        return up ? launch_w4<true, 256, false, 192>(p, grid, s)
-                  : launch_w4<false, 256, false, 192>(p, grid, s);
+        // picked where every group is one row tile (expert choice with at
+        // most 256 rows per expert): weights streamed non-temporally
+        return up ? launch_w4<true, 256, false, 192, true>(p, grid, s)
+                  : launch_w4<false, 256, false, 192, true>(p, grid, s);
     case GEMM_BF16_X2_128x256:
         if (up)
             hipLaunchKernelGGL(gemm_bf16_x2<true>, dim3(grid), dim3(256), 0, s, p);
