@@ -228,49 +228,3 @@ __device__ __forceinline__ const char *weight_row(const GemmParams &p,
     if (routed) base += (size_t)g * F * p.K * esz;
     return base + row * p.K * esz;
 }
-
-// ------------------------------------------------ loads and tile MFMAs
-// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
-// the wave's 64 lanes fill 1 KB of LDS from lds on, lane i at lds + 16 i.
-__device__ __forceinline__ void lds_load16(const void *src, u32x4 *lds) {
-    __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-// The same load with the non-temporal hint, for weight panels that only
-// one row tile reads: their lines are not kept in the caches at the
-// expense of the gathered token rows, which every column tile of the group
-// reads again.  (Measured on the Expert-Choice-shaped layer, one 256-row
-// tile per expert: up GEMM 136 -> 131 us, 192-column down GEMM 124 -> 104,
-// layer 292 -> 272 us; DeepSeek-shaped up GEMM, 320-row tiles, 2.48 -> 2.41
-// ms.  Where two or more row tiles share a panel through L2 it is slower:
-// with every weight load non-temporal the DeepSeek-shaped down GEMM, whose
-// groups of 257..384 rows run as two tiles on one panel, took 2.44 -> 2.78
-// ms, and even there its one-tile groups alone gained nothing.)
-__device__ __forceinline__ void lds_load16_nt(const void *src, u32x4 *lds) {
-    __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void *)lds, 16, 0,
-        2 /* non-temporal */);
-}
-
-// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) |
-                               (0xF << 8));
-}
-
-// One v_mfma_f32_16x16x32_bf16 accumulating into AGPRs, written as asm:
-// with the builtin, hipcc splits a wave's 256 accumulators between AGPRs
-// and VGPRs and copies them back and forth every step, and as volatile asm
-// the MFMAs keep the issue order they are written in.  With a = 16 rows of
-// one operand and b = 16 rows of the other (lane l: row l % 16, k-chunk
-// l / 16 of 8 values), lane l holds acc[t] = sum_k a[4 (l / 16) + t][k] *
-// b[l % 16][k].
-__device__ __forceinline__ void mfma16_agpr(floatx4 &acc, const bf16x8 &a,
-                                            const bf16x8 &b) {
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-                 : "+a"(acc)
-                 : "v"(a), "v"(b));
-}

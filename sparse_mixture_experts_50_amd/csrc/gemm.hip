@@ -330,7 +330,29 @@ __device__ __forceinline__ void dma16(const uint16_t *src, u32x4 *lds_row16) {
         (__attribute__((address_space(3))) void *)lds_row16, 16, 0, 0);
 }
 
+// The same load with the non-temporal hint, for weight panels that only
+// one row tile reads: their lines are not kept in the caches at the
+// expense of the gathered token rows, which every column tile of the group
+// reads again.  (Measured on the Expert-Choice-shaped layer, one 256-row
+// tile per expert: up GEMM 136 -> 131 us, 192-column down GEMM 124 -> 104,
+// layer 292 -> 272 us; DeepSeek-shaped up GEMM, 320-row tiles, 2.48 -> 2.41
+// ms.  Where two or more row tiles share a panel through L2 it is slower:
+// with every weight load non-temporal the DeepSeek-shaped down GEMM, whose
+// groups of 257..384 rows run as two tiles on one panel, took 2.44 -> 2.78
+// ms, and even there its one-tile groups alone gained nothing.)
+__device__ __forceinline__ void dma16_nt(const void *src, u32x4 *lds) {
+    __builtin_amdgcn_global_load_lds(
+        src, (__attribute__((address_space(3))) void *)lds, 16, 0,
+        2 /* non-temporal */);
+}
 
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) |
+                               (0xF << 8));
+}
 
 
 // LDS -> registers: both 16-deep sub-steps of one BKD = 32 stage.
@@ -567,7 +589,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_dma64(GemmParams p) 
             if (nt_b) {
 #pragma unroll
                 for (int j = 0; j < IB; ++j)
-                    lds_load16_nt(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
+                    dma16_nt(bp[j] + ko, st + BM * 8 + (wave + j * NW) * 64);
             } else {
 #pragma unroll
                 for (int j = 0; j < IB; ++j)
@@ -643,6 +665,18 @@ constexpr int CPR = 8;                   // 16-byte chunks per row and stage
 constexpr int STAGE = (BM + BN) * CPR;   // 16-byte units per stage (64 KB)
 constexpr int LPW = BM / 8 / 4;          // loads per wave, operand and stage
 
+__device__ __forceinline__ void dma16b(const char *src, u32x4 *lds_row8) {
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src,
+        (__attribute__((address_space(3))) void *)lds_row8, 16, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_agpr(floatx4 &acc, const bf16x8 &a,
+                                          const bf16x8 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+}
 }  // namespace w4
 
 // bias[f0 + 16 b + t] (t < 4) of NB 16-column blocks into v[4 b + t], as
@@ -751,12 +785,12 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
     auto dma_one = [&](int kl, u32x4 *st, int q) __attribute__((always_inline)) {
         const size_t ko = (size_t)(kt0 + kl) * SK * 2;
         if (q < LA)
-            lds_load16(A + ko + a_off[q], st + (wave + 4 * q) * 64);
+            dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
         else if (NT)
-            lds_load16_nt(bbase[q - LA] + ko + b_lane,
+            dma16_nt(bbase[q - LA] + ko + b_lane,
                      st + BM * CPR + (wave + 4 * (q - LA)) * 64);
         else
-            lds_load16(bbase[q - LA] + ko + b_lane,
+            dma16b(bbase[q - LA] + ko + b_lane,
                    st + BM * CPR + (wave + 4 * (q - LA)) * 64);
     };
     // fragment q (q < 8: A block q, else B block q - 8), sub-step kk
@@ -799,7 +833,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
-            mfma16_agpr(acc[q / TN][q % TN], fb0[q % TN], fa0[q / TN]);
+            mfma_agpr(acc[q / TN][q % TN], fb0[q % TN], fa0[q / TN]);
             if (q % RD == 0 && q / RD < NF) frag_one(fa1, fb1, cur, 1, q / RD);
         }
         // own reads done, stage s+1 landed (this wave's part), then every
@@ -809,7 +843,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams &p, u32x4 *slot0,
         const int nx = min(s + 2, KT - 1);
 #pragma unroll
         for (int q = 0; q < NM; ++q) {
-            mfma16_agpr(acc[q / TN][q % TN], fb1[q % TN], fa1[q / TN]);
+            mfma_agpr(acc[q / TN][q % TN], fb1[q % TN], fa1[q / TN]);
             if (q % RD == 0 && q / RD < NF) frag_one(fa0, fb0, nxt, 0, q / RD);
             if (q % DM == 1 && q / DM < NL) dma_one(nx, cur, q / DM);
         }
@@ -1226,9 +1260,9 @@ __device__ __forceinline__ void w4x_tile(const GemmParams &p, u32x4 *slot0,
     auto dma_one = [&](int kl, u32x4 *st, int q) __attribute__((always_inline)) {
         const size_t ko = (size_t)(kt0 + kl) * SK * 2;
         if (q < LA)
-            lds_load16(A + ko + a_off[q], st + (wave + 4 * q) * 64);
+            w4::dma16b(A + ko + a_off[q], st + (wave + 4 * q) * 64);
         else
-            lds_load16(bbase[q - LA] + ko + b_lane,
+            w4::dma16b(bbase[q - LA] + ko + b_lane,
                        st + BM * CPR + (wave + 4 * (q - LA)) * 64);
     };
     // fragment q (q < RB: A block q, else B block q - RB) of 16-deep step t
@@ -1653,10 +1687,10 @@ __device__ __forceinline__ void x2_tile(const GemmParams &p, char *s0,
         const size_t ko = (size_t)kt * SK * 2;
 #pragma unroll
         for (int j = 0; j < LA; ++j)
-            lds_load16(A + ko + a_off[j], (u32x4 *)(slot + (wave + 4 * j) * 1024));
+            w4::dma16b(A + ko + a_off[j], (u32x4 *)(slot + (wave + 4 * j) * 1024));
 #pragma unroll
         for (int j = 0; j < LB; ++j)
-            lds_load16(bbase[j] + ko + b_lane,
+            w4::dma16b(bbase[j] + ko + b_lane,
                        (u32x4 *)(slot + BM * ROWB + (wave + 4 * j) * 1024));
     };
     const int l16 = lane & 15;
@@ -1693,7 +1727,7 @@ __device__ __forceinline__ void x2_tile(const GemmParams &p, char *s0,
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mfma16_agpr(acc[i][j], fb[j], fa[i]);
+            for (int j = 0; j < 4; ++j) w4::mfma_agpr(acc[i][j], fb[j], fa[i]);
     };
     // wait states of the asm MFMAs: before the first (a VALU write of its
     // srcC) and after the last (a read of an 8-pass result)
