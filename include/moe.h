@@ -250,13 +250,15 @@ int moe_gemm_tail_split(const moe_desc *desc, int up);
  * the workspace (consumed by moe_permute for p_i).  Expert choice: writes
  * topk_idx = e and topk_w = p[t,e] for all E experts, sets every entry of
  * r->slot_of (required) to -1, and writes the logits, transposed to
- * [E][T], into the workspace for moe_permute. */
+ * [E][T], into the workspace for moe_permute.  Top-k: also writes each
+ * 32-token tile's count of picks per expert into the workspace. */
 int moe_router_topk(const moe_desc *desc, const void *x,
                     const moe_weights *w, moe_routing *r, void *ws,
                     size_t ws_bytes, void *stream);
 
 /* Counts, capacity, stable dispatch and statistics (layer steps 3 and 6).
- * Reads r->topk_idx and the router partial sums in the workspace; writes
+ * Reads r->topk_idx and what moe_router_topk left in the workspace (the
+ * probability partial sums and each 32-token tile's expert counts); writes
  * counts, kept, offsets, slot_token, slot_of, f, p, l_aux and, if
  * r->monitor is not NULL, the six monitors.  Expert choice: each expert's
  * top-C selection over the workspace logits replaces the capacity cut

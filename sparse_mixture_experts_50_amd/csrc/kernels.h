@@ -11,8 +11,8 @@
 #define MOE_ROUTER_TOKENS 32
 // Most depth ranges the bf16 router's logits are split into.
 #define MOE_ROUTER_MAX_SPLITS 8
-// Assignments per permute chunk.
-#define MOE_PERMUTE_CHUNK 256
+// Most assignments (T*k) that the single-block permute takes.
+#define MOE_PERMUTE_ONE_BLOCK 256
 
 struct RouterParams {
     const void *x;        // [T][d]
@@ -25,6 +25,9 @@ struct RouterParams {
     float *zh_part;       // [ceil(T/32)][2]: sum lse^2, sum entropy (nats)
     float *scores;        // expert choice: logits [E][T]; null for top-k
     int32_t *slot_of;     // expert choice: [T][E], set to -1 here
+    int32_t *blk;         // top-k: [ceil(T/32)][E] picks of each expert
+                          // among the block's 32 tokens (the dispatch's
+                          // per-chunk counts)
     float *part;          // split bf16 router: [S][T][E] fp32 partial sums
                           // over S consecutive depth ranges of kc each
     int S, kc;            // S = 0: the fused kernel
@@ -43,11 +46,14 @@ struct PermuteParams {
     const int32_t *topk_idx;  // [T*k]
     const float *p_part;      // [n_rtiles][E]
     const float *zh_part;     // [n_rtiles][2]
-    int32_t *blk;             // [n_chunks][E] scratch
+    int32_t *blk;             // [n_chunks][E]: per-chunk expert counts from
+                              // the router, then the chunks' rank bases
     const float *scores;      // expert choice: logits [E][T]; else null
     int32_t *counts, *kept, *offsets, *slot_token, *slot_of;
     float *f, *p, *l_aux;
     float *monitor;           // [6] or null
+    // top-k: chunk c = the assignments of router token tile c,
+    // [32 k c, 32 k (c + 1)); n_chunks = n_rtiles (0 for expert choice)
     int T, E, k, capacity, n_rtiles, n_chunks;
     float alpha;
 };

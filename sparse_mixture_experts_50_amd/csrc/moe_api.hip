@@ -200,11 +200,9 @@ WsLayout layout(const moe_desc *d) {
     WsLayout L;
     const size_t es = elem_bytes(d->dtype);
     L.n_rtiles = (d->T + MOE_ROUTER_TOKENS - 1) / MOE_ROUTER_TOKENS;
-    // expert choice dispatches by per-expert selection, not by chunks
-    L.n_chunks = expert_choice(d)
-                     ? 0
-                     : (int)(((size_t)d->T * d->k + MOE_PERMUTE_CHUNK - 1) /
-                             MOE_PERMUTE_CHUNK);
+    // a dispatch chunk is a router token tile's assignments (expert
+    // choice dispatches by per-expert selection, not by chunks)
+    L.n_chunks = expert_choice(d) ? 0 : L.n_rtiles;
     L.rows = (size_t)routed_rows(d) + (size_t)d->n_shared * d->T;
     size_t off = 0;
     L.p_part = off;
@@ -512,6 +510,7 @@ RouterParams router_params(const moe_desc *desc, const void *x,
     p.zh_part = (float *)at(ws, L.zh_part);
     p.scores = expert_choice(desc) ? (float *)at(ws, L.scores) : nullptr;
     p.slot_of = r->slot_of;
+    p.blk = (int32_t *)at(ws, L.blk);
     const RouterPlan rp = plan(desc);
     p.part = (float *)at(ws, L.rpart);
     p.S = rp.split ? rp.S : 0;

@@ -7,9 +7,10 @@
 // most floor(T/E * cf) tokens, the overflow skips the experts; sec. 2.4:
 // the per-expert bias moves up for an overloaded expert.
 //
-// Three launches (one when T*k fits a single chunk), no float atomics,
-// deterministic:
-//   hist    one block per 256-assignment chunk: LDS-atomic histogram
+// A chunk is the 32 k assignments of one router token tile, whose
+// expert histogram the router block already counted in LDS (with LDS
+// atomics) and wrote to blk.  Two launches (one when T*k fits a single
+// block), no float atomics, deterministic:
 //   scan    one block: per-expert exclusive scan over chunks (rank bases),
 //           counts, kept = min(count, C), offsets, f, p, L_aux
 //   scatter one wave per chunk: within-wave stable ranks by ballot over
@@ -30,25 +31,8 @@
 
 namespace {
 
-constexpr int CH = MOE_PERMUTE_CHUNK;
-
-__global__ __launch_bounds__(256) void permute_hist(PermuteParams p) {
-    __shared__ int h[MOE_MAX_E];
-    for (int e = threadIdx.x; e < p.E; e += blockDim.x) h[e] = 0;
-    __syncthreads();
-    const int n = p.T * p.k;
-    const int a0 = blockIdx.x * CH;
-    const int a1 = min(n, a0 + CH);
-    for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
-        const int e = p.topk_idx[a];
-        // an id outside [0, E) (only possible from non-finite logits) is
-        // never counted and never dispatched
-        if ((unsigned)e < (unsigned)p.E) atomicAdd(&h[e], 1);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < p.E; e += blockDim.x)
-        p.blk[(size_t)blockIdx.x * p.E + e] = h[e];
-}
+// Assignments per chunk: one router token tile's.
+constexpr int CH = MOE_ROUTER_TOKENS;
 
 // One block of 1024 threads, thread = (segment, expert): S = 1024 / E
 // segments split the chunk list and the router-block list, so each thread
@@ -213,8 +197,8 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
     for (int e = lane; e < p.E; e += 64) run[e] = p.blk[(size_t)b * p.E + e];
     __syncthreads();
     const int n = p.T * p.k;
-    const int a0 = b * CH;
-    const int a1 = min(n, a0 + CH);
+    const int a0 = b * CH * p.k;
+    const int a1 = min(n, a0 + CH * p.k);
     const int total = p.offsets[p.E];
     const unsigned long long lt = (1ull << lane) - 1ull;
     // bits of an expert id: the lanes holding the same expert as this one
@@ -254,8 +238,8 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
         if (s >= total) p.slot_token[s] = -1;
 }
 
-// All three steps in one block when every assignment fits one chunk
-// (T*k <= 256, e.g. a decode step): same arithmetic, one launch.
+// Counting, scan and dispatch in one block when T*k <= 256 (e.g. a decode
+// step): the same arithmetic over the same assignments, one launch.
 __global__ __launch_bounds__(256) void permute_small(PermuteParams p) {
     permute_one_block<256>(p);
 }
@@ -432,14 +416,13 @@ __global__ void bias_update_kernel(int E, const int32_t *counts, float target,
 }  // namespace
 
 hipError_t launch_permute(const PermuteParams &p, hipStream_t s) {
-    if (p.n_chunks == 1) {
+    if ((long long)p.T * p.k <= MOE_PERMUTE_ONE_BLOCK) {
         hipLaunchKernelGGL(permute_small, dim3(1), dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(permute_hist, dim3(p.n_chunks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_scatter, dim3(p.n_chunks), dim3(64), 0, s, p);

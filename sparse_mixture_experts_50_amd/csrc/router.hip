@@ -39,10 +39,13 @@ constexpr int RW = 16;            // waves per router block
 // instruction) and the one-lane-per-token reads of the small-E path share
 // banks the same way.
 // Softmax + top-k phase over logits staged in LDS (KS partial planes).
+// hist: LDS counts of each expert's picks among the block's tokens, zeroed
+// by the caller before its last barrier; written out as the block's row of
+// p.blk (top-k only).
 template <int EP, int KS>
 __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP + 1],
                                              const RouterParams &p,
-                                             float (*pp)[EP]) {
+                                             float (*pp)[EP], int *hist) {
     static_assert(RT % RW == 0, "tokens per wave");
     constexpr int PER = EP >= 64 ? EP / 64 : 1;
     const int lane = threadIdx.x & 63;
@@ -152,6 +155,9 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP + 1],
         if (lane < p.k) {
             p.topk_idx[(size_t)t * p.k + lane] = my_e;
             p.topk_w[(size_t)t * p.k + lane] = my_ex / wsum;
+            // an id outside [0, E) (only from non-finite logits) is never
+            // counted and never dispatched
+            if ((unsigned)my_e < (unsigned)p.E) atomicAdd(&hist[my_e], 1);
         }
     }
     // block column sums of the probabilities, fixed order over waves
@@ -177,6 +183,7 @@ __device__ __forceinline__ void route_tokens(const float (*lg)[RT][EP + 1],
 #pragma unroll
         for (int w = 1; w < RW; ++w) s += pp[w][e];
         p.p_part[(size_t)blockIdx.x * p.E + e] = s;
+        if (!p.scores) p.blk[(size_t)blockIdx.x * p.E + e] = hist[e];
     }
     if (p.scores) {
         // the same additions in the same order as v[] above, so the
@@ -415,7 +422,7 @@ __device__ __forceinline__ void route_lanes(const float (*lg)[EP + 1],
                                             const float *addv,
                                             const float *subv,
                                             float (*pr)[EP + 1],
-                                            float (*zh)[2]) {
+                                            float (*zh)[2], int *hist) {
     const int tl = threadIdx.x;          // 0..31
     const int t = blockIdx.x * RT + tl;
     float z = 0.0f, h = 0.0f;
@@ -484,6 +491,7 @@ __device__ __forceinline__ void route_lanes(const float (*lg)[EP + 1],
                 taken |= 1u << be;
                 p.topk_idx[(size_t)t * p.k + j] = be;
                 p.topk_w[(size_t)t * p.k + j] = pr[tl][be] * winv;
+                if (be < p.E) atomicAdd(&hist[be], 1);
             }
         }
     } else {
@@ -529,20 +537,23 @@ __device__ __forceinline__ void route_tile_lanes(const RouterParams &p) {
     __shared__ float pr[RT][EP + 1];
     __shared__ float zh[RT][2];
     __shared__ float addv[EP], subv[EP];
+    __shared__ int hist[EP];
     if (threadIdx.x < EP) {
         const int e = threadIdx.x;
         addv[e] = (e < p.E && p.add) ? p.add[e] : 0.0f;
         subv[e] = (e < p.E && p.sub) ? p.sub[e] : 0.0f;
+        hist[e] = 0;
     }
     sum_partials<EP>(p, lg);
     __syncthreads();
-    if (threadIdx.x < RT) route_lanes<EP>(lg, p, addv, subv, pr, zh);
+    if (threadIdx.x < RT) route_lanes<EP>(lg, p, addv, subv, pr, zh, hist);
     __syncthreads();
     // block sums in token order: probability columns, then lse^2, entropy
     for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
         float s = pr[0][e];
         for (int tl = 1; tl < RT; ++tl) s += pr[tl][e];
         p.p_part[(size_t)blockIdx.x * p.E + e] = s;
+        if (!p.scores) p.blk[(size_t)blockIdx.x * p.E + e] = hist[e];
     }
     if (threadIdx.x >= 64 && threadIdx.x < 66) {
         const int c = threadIdx.x - 64;
@@ -562,9 +573,11 @@ __global__ __launch_bounds__(EP <= 32 ? 256 : RW * 64) void router_route(RouterP
     } else {
         __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
         __shared__ float pp[RW][EP];
+        __shared__ int hist[EP];
+        for (int e = threadIdx.x; e < EP; e += blockDim.x) hist[e] = 0;
         sum_partials<EP>(p, lg[0]);
         __syncthreads();
-        route_tokens<EP, 1>(lg, p, pp);
+        route_tokens<EP, 1>(lg, p, pp, hist);
     }
 }
 
@@ -595,6 +608,8 @@ __global__ __launch_bounds__(RW * 64) void router_fused(RouterParams p) {
     constexpr int TPW = NTE >= RW ? NTE / RW : 1; // tiles per wave
     __shared__ float lg[KS][RT][EP + 1];  // rows of EP + 1 floats (LG_PAD)
     __shared__ float pp[RW][EP];
+    __shared__ int hist[EP];
+    for (int e = threadIdx.x; e < EP; e += blockDim.x) hist[e] = 0;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(RW * 64) void router_fused(RouterParams p) {
         }
     }
     __syncthreads();
-    route_tokens<EP, KS>(lg, p, pp);
+    route_tokens<EP, KS>(lg, p, pp, hist);
 }
 
 // fp32 logits with plain FMA (sequential over d).
@@ -653,6 +668,8 @@ template <int EP>
 __global__ __launch_bounds__(RW * 64) void router_f32(RouterParams p) {
     __shared__ float lg[1][RT][EP + 1];   // rows of EP + 1 floats (LG_PAD)
     __shared__ float pp[RW][EP];
+    __shared__ int hist[EP];
+    for (int e = threadIdx.x; e < EP; e += blockDim.x) hist[e] = 0;
     const int t0 = blockIdx.x * RT;
     const float *x = (const float *)p.x;
     const float *wr = (const float *)p.wr;
@@ -676,7 +693,7 @@ __global__ __launch_bounds__(RW * 64) void router_f32(RouterParams p) {
         lg[0][tl][e] = s;
     }
     __syncthreads();
-    route_tokens<EP, 1>(lg, p, pp);
+    route_tokens<EP, 1>(lg, p, pp, hist);
 }
 
 }  // namespace
@@ -762,7 +779,7 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
 
 bool route_permute_small_ok(const RouterParams &p) {
     return p.S > 0 && p.S <= MOE_ROUTER_MAX_SPLITS && p.E <= 32 &&
-           p.T <= RT && p.T * p.k <= MOE_PERMUTE_CHUNK && !p.scores;
+           p.T <= RT && p.T * p.k <= MOE_PERMUTE_ONE_BLOCK && !p.scores;
 }
 
 hipError_t launch_route_permute_small(const RouterParams &p,
