@@ -54,20 +54,26 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     const int e = tid % p.E, seg = tid / p.E;
     const bool active = seg < S;
 
-    // 1. chunk counts of expert e over this segment's chunks
+    // 1. chunk counts of expert e over this segment's chunks, in batches
+    // of 32, then 8, whose loads are issued before any is added
     const int L = (p.n_chunks + S - 1) / S;
     const int c0 = min(p.n_chunks, seg * L), c1 = min(p.n_chunks, c0 + L);
     int part = 0;
+    auto counts = [&](auto nb, int &b) __attribute__((always_inline)) {
+        constexpr int B = decltype(nb)::value;
+        for (; b + B <= c1; b += B) {
+            int v[B];
+#pragma unroll
+            for (int u = 0; u < B; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+#pragma unroll
+            for (int u = 0; u < B; ++u) part += v[u];
+        }
+    };
     if (active) {
         int b = c0;
-        for (; b + 32 <= c1; b += 32) {
-            int v[32];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) part += v[u];
-        }
-        for (; b < c1; ++b) part += p.blk[(size_t)b * p.E + e];
+        counts(std::integral_constant<int, 32>{}, b);
+        counts(std::integral_constant<int, 8>{}, b);
+        counts(std::integral_constant<int, 1>{}, b);
         seg_i[seg * p.E + e] = part;
     }
     // 2. probability column sums over this segment's router blocks, in
@@ -115,27 +121,27 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         __syncthreads();
     }
     // 4. rank bases: the segment's base plus a running count over its
-    // chunks, 32 counts loaded before any base is written (one memory round
-    // trip per 32 chunks rather than per chunk)
+    // chunks, a batch of counts (32, then 8) loaded before any base is
+    // written (one memory round trip per batch rather than per chunk)
     if (active && p.n_chunks > 0) {
         int run = seg_i[seg * p.E + e] - part;   // earlier segments' counts
-        int b = c0;
-        for (; b + 32 <= c1; b += 32) {
-            int v[32];
+        auto bases = [&](auto nb, int &b) __attribute__((always_inline)) {
+            constexpr int B = decltype(nb)::value;
+            for (; b + B <= c1; b += B) {
+                int v[B];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
+                for (int u = 0; u < B; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                p.blk[(size_t)(b + u) * p.E + e] = run;   // rank base in chunk b+u
-                run += v[u];
+                for (int u = 0; u < B; ++u) {
+                    p.blk[(size_t)(b + u) * p.E + e] = run;   // rank base in chunk b+u
+                    run += v[u];
+                }
             }
-        }
-        for (; b < c1; ++b) {
-            const size_t i = (size_t)b * p.E + e;
-            const int v = p.blk[i];
-            p.blk[i] = run;
-            run += v;
-        }
+        };
+        int b = c0;
+        bases(std::integral_constant<int, 32>{}, b);
+        bases(std::integral_constant<int, 8>{}, b);
+        bases(std::integral_constant<int, 1>{}, b);
     }
     // 5. per expert (threads 0..E-1): counts, kept, f, p
     int cnt = 0, kept = 0;
