@@ -101,6 +101,16 @@ def algorithmic(wl, counts, kept):
                 up_flops=up_flops, up_bytes=up_bytes)
 
 
+def roofline_bound(alg, flops_peak_tflops) -> str:
+    """The roofline bound of the up GEMM: whichever of its algorithmic
+    bytes at the HBM peak and its FLOPs at the matrix peak takes longer
+    (arithmetic intensity below or above the ridge point, 2500 / 8 = 312
+    FLOP per byte for bf16)."""
+    t_hbm = alg["up_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["up_flops"] / (flops_peak_tflops * 1e12)
+    return "hbm" if t_hbm > t_mfma else "mfma"
+
+
 def dense_gemm_tflops(M, N, K, dev) -> float:
     """torch.matmul (hipBLASLt) bf16 rate on one dense M x N x K product."""
     import torch
@@ -304,16 +314,20 @@ def main():
     counts, kept = m["counts"], m["kept"]
     alg = algorithmic(wl, counts, kept)
     tokens_per_s = wl.T * steps / (total_ms / 1e3)
-    if float(np.sum(kept)) / wl.E <= 48:       # rows per routed expert
-        roof = dict(bound="hbm", achieved=alg["up_bytes"] / (up_avg_ms * 1e6),
-                    peak=HBM_PEAK_GBS, unit="GB/s")
+    flops_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" \
+        else MFMA_F32_PEAK_TFLOPS
+    gbs = alg["up_bytes"] / (up_avg_ms * 1e6)
+    tflops = alg["up_flops"] / (up_avg_ms * 1e9)
+    if roofline_bound(alg, flops_peak) == "hbm":
+        roof = dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s")
     else:
-        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" \
-            else MFMA_F32_PEAK_TFLOPS
-        roof = dict(bound="mfma", achieved=alg["up_flops"] /
-                    (up_avg_ms * 1e9), peak=peak, unit="TFLOP/s")
+        roof = dict(bound="mfma", achieved=tflops, peak=flops_peak,
+                    unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    if roof["bound"] == "mfma" and wl.dtype == "bf16":
+    # the same launch against both peaks
+    roof["hbm_frac"] = gbs / HBM_PEAK_GBS
+    roof["mfma_frac"] = tflops / flops_peak
+    if wl.dtype == "bf16" and float(np.sum(kept)) / wl.E > 48:
         # the vendor library's dense bf16 GEMM of the same FLOPs as the up
         # GEMM (rows x d_ff x d), measured here beside the nominal peak
         roof["measured_dense_gemm_tflops"] = dense_gemm_tflops(

@@ -1,6 +1,7 @@
 """Host logic of bench.py on the CPU: the algorithmic FLOP and byte counts
-the roofline fractions divide by, the refusal of more than one GPU, and the
-rule that a traffic profile counts only while the GEMM source is unchanged."""
+the roofline fractions divide by, the roofline bound they are taken
+against, the refusal of more than one GPU, and the rule that a traffic
+profile counts only while the GEMM source is unchanged."""
 import json
 import os
 import subprocess
@@ -66,3 +67,25 @@ def test_traffic_profile_needs_the_current_gemm_source(tmp_path, monkeypatch):
         "traffic_bytes_per_launch: 123\ngemm_source_sha256_16: 0000\n")
     assert bench.recorded_traffic("y") is None
     assert bench.recorded_traffic("missing") is None
+
+
+def test_roofline_bound_by_arithmetic_intensity():
+    """The up GEMM's bound is the peak it would take longer at: the Mixtral
+    prefill GEMM (775 FLOP per byte) is matrix-bound; the DeepSeek-shaped
+    one (8192 x 8 + 8192 rows over 257 experts' weights: 243 FLOP per
+    byte), the Expert-Choice one (181) and the decode one are HBM-bound,
+    all against the 312 FLOP per byte of 2.5 PFLOP/s over 8 TB/s."""
+    W = workloads.WORKLOADS
+    peak = bench.MFMA_BF16_PEAK_TFLOPS
+    cases = {"mixtral_prefill": (np.full(8, 1024), "mfma"),
+             "deepseek_v3": (np.full(256, 256), "hbm"),
+             "mixtral_decode": (np.full(8, 8), "hbm"),
+             "mixtral_prefill_swiglu": (np.full(8, 1024), "mfma")}
+    for name, (kept, want) in cases.items():
+        a = bench.algorithmic(W[name], kept, kept)
+        assert bench.roofline_bound(a, peak) == want, name
+    ec = W["expert_choice_c2"]
+    kept = np.full(ec.E, 256)
+    a = bench.algorithmic(ec, kept, kept)
+    assert 150 < a["up_flops"] / a["up_bytes"] < 312
+    assert bench.roofline_bound(a, peak) == "hbm"
