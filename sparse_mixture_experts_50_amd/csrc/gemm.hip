@@ -2771,6 +2771,8 @@ GemmVariantInfo gemm_variant_info(int variant) {
     case GEMM_BF16_W4X_256x256: return {256, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4X_128x256: return {128, 256, 256, 2 * 512 * 128};
     case GEMM_BF16_W4_256x192: return {256, 192, 256, 2 * 512 * 128};
+    case GEMM_BF16_TALL_320x192: return {320, 192, 256, 2 * 512 * 128};
+    case GEMM_BF16_TALL_288x224: return {288, 224, 256, 2 * 512 * 128};
     case GEMM_BF16_X2_128x256: return {128, 256, 256, 3 * 384 * 64};
     case GEMM_BF16_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_BF16};
     case GEMM_FP8_RING_16x16: return {16, 16, 256, 4 * 16 * MOE_RING_CB_FP8};
@@ -2827,6 +2829,8 @@ hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
         // most 256 rows per expert): weights streamed non-temporally
         return up ? launch_w4<true, 256, false, 192, true>(p, grid, s)
                   : launch_w4<false, 256, false, 192, true>(p, grid, s);
+    case GEMM_BF16_TALL_320x192: return launch_gemm_tall(p, 192, up, grid, s);
+    case GEMM_BF16_TALL_288x224: return launch_gemm_tall(p, 224, up, grid, s);
     case GEMM_BF16_X2_128x256:
         if (up)
             hipLaunchKernelGGL(gemm_bf16_x2<true>, dim3(grid), dim3(256), 0, s, p);

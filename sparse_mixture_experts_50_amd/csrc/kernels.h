@@ -92,7 +92,13 @@ enum GemmVariant {
     GEMM_BF16_W4X_256x256 = 21,    // variant 14 with 32x32x16 MFMAs, mixed tile heights
     GEMM_BF16_W4X_128x256 = 22,    // variant 15 with 32x32x16 MFMAs
     GEMM_BF16_W4_256x192 = 23,     // variant 14 with 192-column tiles (ungated, N % 192 == 0)
+    GEMM_BF16_TALL_320x192 = 24,   // four waves of 160 x 96: one tile per group of <= 320 rows (ungated)
+    GEMM_BF16_TALL_288x224 = 25,   // four waves of 144 x 112: one tile per group of <= 288 rows (ungated)
 };
+
+inline bool tall_variant(int v) {
+    return v == GEMM_BF16_TALL_320x192 || v == GEMM_BF16_TALL_288x224;
+}
 
 // Weight-ring kernels: bytes of each weight row per stage (bf16 / FP8),
 // and the most routed slots whose tokens they stage in LDS.
@@ -138,6 +144,9 @@ hipError_t launch_route_permute_small(const RouterParams &p,
 hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams &p, int variant, bool up, int grid,
                        hipStream_t s);
+// The tall-tile kernel (variants 24 and 25): bn = 192 or 224 columns.
+hipError_t launch_gemm_tall(const GemmParams &p, int bn, bool up, int grid,
+                            hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int dtype, hipStream_t s);
 hipError_t launch_bias_update(int E, const int32_t *counts, float target,
                               float gamma, float *bias, hipStream_t s);

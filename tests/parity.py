@@ -80,6 +80,7 @@ def sample_tokens(T: int, n: int, seed: int = 0, must=()) -> np.ndarray:
 TILE_ROWS = {0: (256,), 1: (128,), 2: (32,), 3: (64,), 5: (256,), 6: (128,),
              8: (256,), 9: (128,), 13: (320, 256), 14: (256, 224, 192, 160, 128), 21: (256, 192, 128),
              22: (128,), 23: (256, 224, 192, 160, 128),
+             24: (320, 288, 256, 192, 128, 64), 25: (288, 256, 192, 128, 64),
              15: (128,), 20: (128,)}
 
 

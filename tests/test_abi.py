@@ -253,13 +253,13 @@ def _desc_of(w):
 # (host side only: no GPU needed).  4: fp32 SIMT; 8 / 13: eight-wave
 # 256- / 320-row tiles; 11 / 12: bf16 / FP8 weight streaming; 14: four-wave
 # 256-row tiles with half-height tails; 15: four-wave 128-row tiles; 23:
-# four-wave 256-row tiles of 192 columns.
+# four-wave 256-row tiles of 192 columns; 24: four-wave 320 x 192 tiles.
 PICKS = {
     "tiny_top2_f32": (4, 4),
     "switch_top1_cap": (2, 15),
     "mixtral_prefill": (14, 14),
     "mixtral_decode": (18, 18),
-    "deepseek_v3": (13, 14),
+    "deepseek_v3": (24, 14),
     "mixtral_decode_fp8": (19, 19),
     "mixtral_prefill_swiglu": (14, 14),
     "mixtral_decode_swiglu": (11, 18),

@@ -71,7 +71,7 @@ def test_small_full_parity(name):
 
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3", "5", "6", "7", "8",
                                      "9", "11", "13", "14", "15", "16", "20",
-                                     "21", "22"])
+                                     "21", "22", "24", "25"])
 def test_every_gemm_variant(variant, monkeypatch):
     """Each bf16 tile variant forced on a shape with groups of 0 to ~100
     rows (several row chunks for the small-tile kernels)."""
@@ -84,7 +84,8 @@ def test_every_gemm_variant(variant, monkeypatch):
     say(f"[variant {variant}] {rep}")
 
 
-@pytest.mark.parametrize("variant", ["13", "14", "15", "20", "21", "22"])
+@pytest.mark.parametrize("variant", ["13", "14", "15", "20", "21", "22",
+                                     "24", "25"])
 def test_large_tile_variants_multi_tile_groups(variant, monkeypatch):
     """The 320- and four-wave 256-row kernels on groups of ~600 rows (three
     row tiles, the last ragged), eight column tiles and 16 stages of K,
@@ -424,3 +425,49 @@ def test_four_wave_even_split_group_sizes(C, kernel, monkeypatch):
     # (expert choice: every expert keeps exactly C rows)
     assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
     say(f"[even split C={C}, kernel {kernel}] {check_expert_choice(w, inp, gpu)}")
+
+
+@pytest.mark.parametrize("kernel", ["24", "25"])
+@pytest.mark.parametrize("C", [1, 64, 65, 128, 129, 193, 256, 257, 288, 289,
+                               320, 321, 577, 641])
+def test_tall_tile_group_sizes(C, kernel, monkeypatch):
+    """The tall-tile kernel (24: 320 x 192 tiles, 25: 288 x 224) on
+    Expert-Choice groups of exactly C rows: a group runs as
+    ceil(C / 320) (or / 288) row tiles of the smallest height in 64, 128,
+    192, 256, 288, 320 that holds its share, so C covers each height, one
+    row either side of a boundary, one-tile groups (non-temporal weights)
+    and two or three tiles (577, 641).  d = 256 and d_ff = 512 make every
+    GEMM's last column tile ragged (512 = 2 x 192 + 128 = 2 x 224 + 64;
+    256 = 192 + 64 = 224 + 32)."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", kernel)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", kernel)
+    w = scaled(W["expert_choice_c2"], T=2 * C, d=256, E=2, k=2, d_ff=512,
+               capacity_factor=1.0)
+    d = moe.make_desc(w.T, w.d, w.E, w.k, w.d_ff, torch.bfloat16,
+                      capacity=C, routing="expert_choice")
+    assert (moe.moe_gemm_variant(d, True), moe.moe_gemm_variant(d, False)) \
+        == (int(kernel), int(kernel))
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
+    say(f"[tall {kernel} C={C}] {check_expert_choice(w, inp, gpu)}")
+
+
+@pytest.mark.parametrize("up,down,act", [("24", "25", "gelu"),
+                                         ("25", "24", "gelu"),
+                                         ("24", "14", "silu")])
+def test_tall_tiles_deepseek_shaped(up, down, act, monkeypatch):
+    """A DeepSeek-shaped layer at reduced size (top-8 of 64 experts, about
+    256 rows each, the Zipf balancing bias, a shared expert of all 2048
+    tokens: seven or eight row tiles sharing each panel, plain loads) with
+    the tall-tile kernels on both GEMMs (and the SiLU epilogue), N = 512
+    and 1024 (ragged last column tiles); every output row against the
+    oracle."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", up)
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", down)
+    w = scaled(W["deepseek_v3"], T=2048, d=1024, E=64, d_ff=512,
+               activation=act)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    rep = check_layer(w, inp, gpu)
+    say(f"[tall deepseek {up}/{down} {act}] {rep}")
