@@ -47,7 +47,7 @@ def parse():
 
 # the grouped-GEMM kernels and the headers they compile
 GEMM_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_50_amd", "csrc", f)
-                for f in ("gemm.hip", "common.h", "kernels.h")]
+                for f in ("gemm.hip", "gemm_tall.hip", "common.h", "kernels.h")]
 
 
 def source_digest() -> str:
