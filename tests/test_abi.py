@@ -256,7 +256,7 @@ def _desc_of(w):
 # four-wave 256-row tiles of 192 columns; 24: four-wave 320 x 192 tiles.
 PICKS = {
     "tiny_top2_f32": (4, 4),
-    "switch_top1_cap": (2, 15),
+    "switch_top1_cap": (2, 24),
     "mixtral_prefill": (14, 14),
     "mixtral_decode": (18, 18),
     "deepseek_v3": (24, 14),
