@@ -406,12 +406,14 @@ int pick_variant(const moe_desc *d, int N, bool up) {
         d->n_shared == 0 && w4_fits(d, up) &&
         (long long)d->E * (N / 192) <= device_cus())
         return GEMM_BF16_W4_256x192;
-    // A down projection (K >= 2048) under a top-k capacity limit of at most
-    // 320 rows: every group is one tall row tile, whose weight panel then
+    // A down projection (K >= 2048) under a top-k capacity limit of 129..320
+    // rows: every group is one tall row tile, whose weight panel then
     // streams with the non-temporal hint (the Switch-shaped down GEMM, 0..160
     // rows per expert: layer 0.187 -> 0.177 ms against 128-row four-wave
-    // tiles; its up GEMM, K = 768, ran 86 us against 70 on 32-row tiles)
-    if (!up && !expert_choice(d) && d->capacity >= 0 && d->capacity <= 320 &&
+    // tiles; its up GEMM, K = 768, ran 86 us against 70 on 32-row tiles).
+    // Under a limit of at most 128 rows the 128-row four-wave tiles below
+    // stay (not measured against this).
+    if (!up && !expert_choice(d) && d->capacity > 128 && d->capacity <= 320 &&
         K >= 2048 && w4_fits(d, up))
         return GEMM_BF16_TALL_320x192;
     if (avg <= 128.0)
