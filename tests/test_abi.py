@@ -277,6 +277,33 @@ def test_gemm_variant_choice(name, monkeypatch):
             moe.moe_gemm_variant(d, False)) == PICKS[name]
 
 
+def test_tall_tile_variants_are_validated(monkeypatch):
+    """The tall-tile kernel (24, 25) takes a ragged last column tile (N not
+    a multiple of 192 or 224), unlike the fixed-width kernels; it is
+    refused for a gated (SwiGLU) up projection, whose waves must hold whole
+    64-column gate/up chunks, and where the four-wave K rule fails."""
+    import dataclasses
+    import workloads
+    ds = workloads.WORKLOADS["deepseek_v3"]
+    d = _desc_of(ds)                         # up N = 2048, down N = 7168
+    for v in ("24", "25"):
+        monkeypatch.setenv("MOE_GEMM_VARIANT_UP", v)
+        monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", v)
+        assert moe.moe_gemm_variant(d, True) == int(v)
+        assert moe.moe_gemm_variant(d, False) == int(v)
+    # the 192-column four-wave form needs N % 192 == 0: refused for up
+    # (2048), back to the pick
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "23")
+    assert moe.moe_gemm_variant(d, True) == 24
+    # gated up projection: refused (the pick is a gate-capable kernel)
+    sw = _desc_of(workloads.WORKLOADS["mixtral_prefill_swiglu"])
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "24")
+    assert moe.moe_gemm_variant(sw, True) == 14
+    # K % 128 != 0: refused
+    odd = _desc_of(dataclasses.replace(ds, d=7168 + 64))
+    assert moe.moe_gemm_variant(odd, True) not in (24, 25)
+
+
 def test_gemm_variant_override_is_validated(monkeypatch):
     import workloads
     d = _desc_of(workloads.WORKLOADS["mixtral_prefill"])
