@@ -23,7 +23,8 @@
 // ceil(R / m) rows.  Column tiles need not divide N: the last one is
 // ragged (N = 2048 with 192-column tiles: 10 full and one of 128 columns);
 // its weight loads past N re-read the last valid 8 rows and its columns
-// past N are not stored.  The epilogue (bias, GELU / SiLU for the up GEMM,
+// past N are not stored.  In the 320 x 192 form of an up projection a group
+// of at most 256 rows (one row tile) takes 256-column tiles instead.  The epilogue (bias, GELU / SiLU for the up GEMM,
 // bf16) stores straight from the accumulators: a lane's 4 consecutive
 // columns of one row as an 8-byte store.
 //
@@ -307,6 +308,21 @@ __device__ __forceinline__ void run_tile(int h, const GemmParams &p,
     }
 }
 
+// A one-tile group of at most 256 rows on 256-column tiles (weights with
+// the non-temporal hint).
+template <bool UP>
+__device__ __forceinline__ void run_wide_tile(int h, const GemmParams &p,
+                                              u32x4 *slot0, u32x4 *slot1,
+                                              int g, int row0, int nrows,
+                                              int n0, bool routed, int wave) {
+    switch (h) {
+    case 64: tall_tile<UP, 32, 256, true>(p, slot0, slot1, g, row0, nrows, n0, routed, wave); break;
+    case 128: tall_tile<UP, 64, 256, true>(p, slot0, slot1, g, row0, nrows, n0, routed, wave); break;
+    case 192: tall_tile<UP, 96, 256, true>(p, slot0, slot1, g, row0, nrows, n0, routed, wave); break;
+    default: tall_tile<UP, 128, 256, true>(p, slot0, slot1, g, row0, nrows, n0, routed, wave); break;
+    }
+}
+
 // Persistent over the tiles: group-major, then column tile, then row tile,
 // so that the row tiles of a weight panel are consecutive.  Logical tile L
 // of round r goes to block (xcd, local) with L = r * grid + xcd * grid/8 +
@@ -320,10 +336,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tall(GemmParams p) {
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
     __shared__ TileTable tt;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // 320 x 192 form of an up projection: a group of at most 256 rows runs
+    // on 256-column tiles (DeepSeek-shaped up GEMM 2.26 -> 2.20 ms: fewer,
+    // fuller tiles).  Not for a down projection: on the Switch-shaped one
+    // (N = 768) three column tiles a group instead of four left a quarter of
+    // the CUs idle (68 -> 83 us).
+    constexpr bool WIDE = BN == 192 && UP;
     const int NTN = (p.N + BN - 1) / BN;
+    const int NTW = (p.N + 255) / 256;
     const int G = p.E + p.n_shared;
+    // tt.mt: every tile of the group (row tiles x its column tiles)
     build_tile_table_by(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
-                        NTN, [](int rows) { return (rows + TRMAX - 1) / TRMAX; });
+                        1, [NTN, NTW](int rows) {
+                            const int m = (rows + TRMAX - 1) / TRMAX;
+                            return m * (WIDE && rows <= 256 ? NTW : NTN);
+                        });
     const int total = __builtin_amdgcn_readfirstlane(tt.base[G]);
     const int nb = gridDim.x, per = nb >> 3;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
@@ -332,16 +359,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tall(GemmParams p) {
         if (L >= total) break;
         const int g = __builtin_amdgcn_readfirstlane(find_group(tt, G, L));
         const int local = L - __builtin_amdgcn_readfirstlane(tt.base[g]);
-        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]);
+        const int grows = __builtin_amdgcn_readfirstlane(tt.rows[g]);
+        const bool wide = WIDE && grows <= 256;
+        const int mt = __builtin_amdgcn_readfirstlane(tt.mt[g]) / (wide ? NTW : NTN);
         const int n_tile = local / mt;
         const int m_tile = local - n_tile * mt;
-        const int grows = __builtin_amdgcn_readfirstlane(tt.rows[g]);
         const int h = height<TRMAX>(grows, mt);
         const int row0 = __builtin_amdgcn_readfirstlane(tt.start[g]) + m_tile * h;
         const int nrows = min(h, grows - m_tile * h);
         if (nrows <= 0) continue;
-        const int n0 = n_tile * BN;
         const bool routed = g < p.E;
+        if (wide) {
+            run_wide_tile<UP>(h, p, slot0, slot1, g, row0, nrows, n_tile * 256,
+                              routed, wave);
+            continue;
+        }
+        const int n0 = n_tile * BN;
         // one row tile: its panel is read by no other tile
         if (mt == 1)
             run_tile<UP, BN, true>(h, p, slot0, slot1, g, row0, nrows, n0, routed, wave);

@@ -471,3 +471,20 @@ def test_tall_tiles_deepseek_shaped(up, down, act, monkeypatch):
     gpu = gpu_forward(w, inp)
     rep = check_layer(w, inp, gpu)
     say(f"[tall deepseek {up}/{down} {act}] {rep}")
+
+
+@pytest.mark.parametrize("C", [100, 256, 300])
+def test_tall_tile_wide_ragged_columns(C, monkeypatch):
+    """The 320 x 192 kernel's up GEMM runs a one-tile group of at most 256
+    rows on 256-column tiles: with d_ff = 640 those are two full column
+    tiles and a ragged one of 128 columns (a 300-row group keeps 192-column
+    tiles: three full and one of 64), every output row against the
+    oracle."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT_UP", "24")
+    monkeypatch.setenv("MOE_GEMM_VARIANT_DOWN", "24")
+    w = scaled(W["expert_choice_c2"], T=2 * C, d=256, E=2, k=2, d_ff=640,
+               capacity_factor=1.0)
+    inp = inputs_on(w, device())
+    gpu = gpu_forward(w, inp)
+    assert int(gpu["kept"].max()) == C and int(gpu["kept"].min()) == C
+    say(f"[tall wide C={C}] {check_expert_choice(w, inp, gpu)}")
