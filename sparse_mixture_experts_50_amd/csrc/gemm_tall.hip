@@ -23,8 +23,8 @@
 // ceil(R / m) rows.  Column tiles need not divide N: the last one is
 // ragged (N = 2048 with 192-column tiles: 10 full and one of 128 columns);
 // its weight loads past N re-read the last valid 8 rows and its columns
-// past N are not stored.  In the 320 x 192 form of an up projection a group
-// of at most 256 rows (one row tile) takes 256-column tiles instead.  The epilogue (bias, GELU / SiLU for the up GEMM,
+// past N are not stored.  In the 320 x 192 form with N >= 2048 a group of at
+// most 256 rows (one row tile) takes 256-column tiles instead.  The epilogue (bias, GELU / SiLU for the up GEMM,
 // bf16) stores straight from the accumulators: a lane's 4 consecutive
 // columns of one row as an 8-byte store.
 //
@@ -336,18 +336,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tall(GemmParams p) {
     __shared__ u32x4 slot0[STAGE], slot1[STAGE];
     __shared__ TileTable tt;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // 320 x 192 form of an up projection: a group of at most 256 rows runs
-    // on 256-column tiles (DeepSeek-shaped up GEMM 2.26 -> 2.20 ms: fewer,
-    // fuller tiles).  Not for a down projection: on the Switch-shaped one
-    // (N = 768) three column tiles a group instead of four left a quarter of
-    // the CUs idle (68 -> 83 us).
-    constexpr bool WIDE = BN == 192 && UP;
+    // 320 x 192 form with N >= 2048: a group of at most 256 rows runs on
+    // 256-column tiles (fewer, fuller tiles: DeepSeek-shaped up GEMM 2.26 ->
+    // 2.20 ms, layer with the tall down GEMM 4.955 -> 4.926 ms).  Not for a
+    // narrow N: on the Switch-shaped down GEMM (N = 768) three column tiles
+    // a group instead of four left a quarter of the CUs idle (68 -> 83 us).
+    const bool WIDE = BN == 192 && p.N >= 2048;
     const int NTN = (p.N + BN - 1) / BN;
     const int NTW = (p.N + 255) / 256;
     const int G = p.E + p.n_shared;
     // tt.mt: every tile of the group (row tiles x its column tiles)
     build_tile_table_by(tt, p.offsets, p.E, p.n_shared, p.shared_base, p.T,
-                        1, [NTN, NTW](int rows) {
+                        1, [NTN, NTW, WIDE](int rows) {
                             const int m = (rows + TRMAX - 1) / TRMAX;
                             return m * (WIDE && rows <= 256 ? NTW : NTN);
                         });

@@ -259,7 +259,7 @@ PICKS = {
     "switch_top1_cap": (2, 24),
     "mixtral_prefill": (14, 14),
     "mixtral_decode": (18, 18),
-    "deepseek_v3": (24, 14),
+    "deepseek_v3": (24, 24),
     "mixtral_decode_fp8": (19, 19),
     "mixtral_prefill_swiglu": (14, 14),
     "mixtral_decode_swiglu": (11, 18),
