@@ -6,7 +6,7 @@
 // training guide", sec. 3.1: the router is an nn.Linear (additive bias).
 //
 // bf16: two kernels.  The logits kernel spreads the logits GEMM over many
-// blocks: each block takes 32 (E <= 64, router_logits) or 256 (E > 64,
+// blocks: each block takes 32 (E <= 64, router_logits) or 128 (E > 64,
 // router_logits_lds, router rows staged in LDS) tokens, all experts and one
 // of S consecutive depth ranges, with MFMA 32x32x16 (fp32 accumulation),
 // and writes fp32 partial sums; a single block per 32 tokens would pull
@@ -311,18 +311,21 @@ __global__ __launch_bounds__(256) void router_logits(RouterParams p) {
 }
 
 // Partial logits over one depth range for E > 64 (EP = 128 or 256).  A
-// block takes 256 tokens, 64 per wave (two 32-token MFMA tiles), and every
-// expert: each wave holds 2 x EP / 32 accumulator tiles of 32x32.  The
-// router rows of each 64-deep step are staged in LDS once per block (two
-// buffers, loaded into registers one step ahead, one barrier per step) and
-// every wave reads its B fragments there; with 64 tokens per wave each
-// fragment feeds two MFMAs.  Against one 32-token tile per wave reading
-// the router rows straight from L2, the router matrix is pulled from L2 a
-// quarter as often per token and half as often per MFMA.  Staged rows are
-// 128 bytes of eight 16-byte chunks, chunk c of row r at c ^ ((r / 2) % 8),
-// so that 32 lanes reading 32 rows at one chunk hit distinct bank groups.
-template <int EP>
-__global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
+// block takes 128 MT tokens, 32 MT per wave (MT 32-token MFMA tiles), and
+// every expert: each wave holds MT x EP / 32 accumulator tiles of 32x32.
+// The router rows of each 64-deep step are staged in LDS once per block
+// (two buffers, loaded into registers one step ahead, one barrier per
+// step) and every wave reads its B fragments there (with MT = 2 each feeds
+// two MFMAs).  Against one 32-token tile per wave reading the router rows
+// straight from L2, the router matrix is pulled from L2 a quarter (MT = 2)
+// or half (MT = 1) as often per token.  MT = 1 is launched: its 128
+// accumulators let two blocks share a CU and hide each other's load waits
+// (DeepSeek-shaped logits 62.5 -> 55.4 us against MT = 2's one block of
+// 256 accumulators per wave).  Staged rows are 128 bytes of eight 16-byte
+// chunks, chunk c of row r at c ^ ((r / 2) % 8), so that 32 lanes reading
+// 32 rows at one chunk hit distinct bank groups.
+template <int EP, int MT>
+__global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void router_logits_lds(RouterParams p) {
     constexpr int ET = EP / 32;                 // 32-expert tiles
     constexpr int CH = EP * 8;                  // 16-byte chunks per step
     constexpr int PT = CH / 256;                // chunks per thread per step
@@ -330,11 +333,11 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = blockIdx.y;
     const int k_lo = s * p.kc, k_hi = min(p.d, k_lo + p.kc);
-    const int t0 = blockIdx.x * 256 + wave * 64;
+    const int t0 = blockIdx.x * (128 * MT) + wave * (32 * MT);
     const int kg = (lane >> 5) * 8;
-    const uint16_t *xr[2];
+    const uint16_t *xr[MT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MT; ++m) {
         const int tok = min(t0 + 32 * m + (lane & 31), p.T - 1);
         xr[m] = (const uint16_t *)p.x + (size_t)tok * p.d + kg;
     }
@@ -347,20 +350,20 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
         wsrc[i] = (const uint16_t *)p.wr + (size_t)e * p.d + 8 * c;
         wdst[i] = r * 8 + (c ^ ((r >> 1) & 7));
     }
-    floatx16 acc[2][ET];
+    floatx16 acc[MT][ET];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int et = 0; et < ET; ++et)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[m][et][v] = 0.0f;
 
-    u32x4 wreg[PT], areg[2][4];
+    u32x4 wreg[PT], areg[MT][4];
     auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < PT; ++i) wreg[i] = *(const u32x4 *)(wsrc[i] + k0);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 areg[m][j] = *(const u32x4 *)(xr[m] + k0 + 16 * j);
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
         for (int i = 0; i < PT; ++i) st[wdst[i]] = wreg[i];
         u32x4 a[2][4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) a[m][j] = areg[m][j];
         __syncthreads();
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
                 const int r = 32 * et + (lane & 31);
                 const u32x4 bv = st[r * 8 + (c ^ ((r >> 1) & 7))];
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
+                for (int m = 0; m < MT; ++m)
                     acc[m][et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         as_bf16x8(a[m][j]), as_bf16x8(bv), acc[m][et], 0, 0, 0);
             }
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds(RouterParams p) {
     // 8*(v/4) + 4*(lane/32) + v%4 of its tile
     float *part = p.part + (size_t)s * p.T * p.E;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
             const int e = 32 * et + (lane & 31);
@@ -710,13 +713,12 @@ RouterPlan router_plan(int T, int d, int E, int cus) {
     const double fbytes = 2.0 * d * (RT + E);
     r.split = !(2 * fblocks >= cus && fbytes <= 400e3);
     const bool small = r.ep <= 64;
-    r.tokens = small ? 32 : 256;
+    r.tokens = small ? 32 : 128;
     const int kw = small ? 4 / (r.ep / 32) : 1;
     const long long blocks = T > 0 ? (T + r.tokens - 1) / r.tokens : 1;
-    // about two blocks per CU (one for E > 64, whose blocks of 256 tokens
-    // hold a wave per SIMD), each wave keeping at least 8 16-deep MFMA
+    // about two blocks per CU, each wave keeping at least 8 16-deep MFMA
     // steps of its range (E > 64: four 64-deep staged steps)
-    const long long want = (long long)cus * (small ? 2 : 1);
+    const long long want = (long long)cus * 2;
     int S = (int)((want + blocks - 1) / blocks);
     const int most = small ? d / (16 * 8 * kw) : d / 256;
     if (S > most) S = most;
@@ -746,7 +748,7 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
         return hipGetLastError();
     }
     if (dtype == 1) {
-        const int tokens = EP <= 64 ? 32 : 256;
+        const int tokens = EP <= 64 ? 32 : 128;
         const dim3 lgrid((p.T + tokens - 1) / tokens, p.S);
         switch (EP) {
         case 32:
@@ -758,11 +760,11 @@ hipError_t launch_router(const RouterParams &p, int dtype, hipStream_t s) {
             hipLaunchKernelGGL(router_route<64>, grid, block, 0, s, p);
             break;
         case 128:
-            hipLaunchKernelGGL(router_logits_lds<128>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((router_logits_lds<128, 1>), lgrid, dim3(256), 0, s, p);
             hipLaunchKernelGGL(router_route<128>, grid, block, 0, s, p);
             break;
         default:
-            hipLaunchKernelGGL(router_logits_lds<256>, lgrid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((router_logits_lds<256, 1>), lgrid, dim3(256), 0, s, p);
             hipLaunchKernelGGL(router_route<256>, grid, block, 0, s, p);
             break;
         }
