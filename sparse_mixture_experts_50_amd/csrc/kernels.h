@@ -46,8 +46,8 @@ struct PermuteParams {
     const int32_t *topk_idx;  // [T*k]
     const float *p_part;      // [n_rtiles][E]
     const float *zh_part;     // [n_rtiles][2]
-    int32_t *blk;             // [n_chunks][E]: per-chunk expert counts from
-                              // the router, then the chunks' rank bases
+    const int32_t *blk;       // [n_chunks][E]: per-chunk expert counts from
+                              // the router
     const float *scores;      // expert choice: logits [E][T]; else null
     int32_t *counts, *kept, *offsets, *slot_token, *slot_of;
     float *f, *p, *l_aux;

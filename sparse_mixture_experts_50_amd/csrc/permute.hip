@@ -9,19 +9,21 @@
 //
 // A chunk is the 32 k assignments of one router token tile, whose
 // expert histogram the router block already counted in LDS (with LDS
-// atomics) and wrote to blk.  Two launches (one when T*k fits a single
-// block), no float atomics, deterministic:
-//   scan    one block: per-expert exclusive scan over chunks (rank bases),
-//           counts, kept = min(count, C), offsets, f, p, L_aux
-//   scatter one wave per chunk: within-wave stable ranks by ballot over
-//           equal experts, slot = offset + rank, overflow -> -1
+// atomics) and wrote to blk.  One launch, no float atomics, deterministic:
+//   dispatch one block per chunk: from the whole histogram its rank bases
+//            (counts of the earlier chunks) and the expert offsets
+//            (exclusive scan of kept = min(count, C)); integer sums, so
+//            every block finds the same offsets.  Then one wave ranks
+//            equal experts by ballot: slot = offset + rank, overflow -> -1
+//   stats    one more block: counts, kept, offsets, f, p, L_aux, monitor
+// (a single block does all of it when T*k fits one block).
 // Assignments are numbered a = t*k + j, so chunk order is token-major and
 // the resulting permutation is stable in (t, j).
 //
 // Expert choice ("AI-Research-SKILLs MoE training guide", sec. 4.2): every
 // token is a candidate of every expert (counts = T, k = E) and expert e
 // keeps its C largest logits instead of its first C tokens.  Two launches:
-//   scan    as above, with counts = T
+//   stats   as above, with counts = T
 //   select  one block per expert: exact radix select of the C-th largest
 //           logit (passes of 11, 11 and 10 bits over order-preserving
 //           keys), then the picks in token order; equal keys go to the
@@ -33,14 +35,17 @@ namespace {
 
 // Assignments per chunk: one router token tile's.
 constexpr int CH = MOE_ROUTER_TOKENS;
+// Most experts per token under top-k routing.
+constexpr int MOE_MAX_TOPK = 64;
 
-// One block of 1024 threads, thread = (segment, expert): S = 1024 / E
+// Blocks of 1024 threads, thread = (segment, expert): S = 1024 / E
 // segments split the chunk list and the router-block list, so each thread
 // walks n/S entries instead of n; partial results meet in LDS and are
 // summed in segment order (deterministic).
 constexpr int SCAN_THREADS = 1024;
 
-__global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
+// Counts, kept, offsets, f, p, L_aux and the monitor, in one block.
+__device__ __forceinline__ void stats_block(const PermuteParams &p) {
     __shared__ int seg_i[SCAN_THREADS];
     __shared__ float seg_f[SCAN_THREADS];
     __shared__ float zh_w[SCAN_THREADS / 64][2];
@@ -54,45 +59,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     const int e = tid % p.E, seg = tid / p.E;
     const bool active = seg < S;
 
-    // 1. chunk counts of expert e over this segment's chunks, in batches
-    // of 32, then 8, whose loads are issued before any is added
+    // 1-2. chunk counts of expert e over this segment's chunks, and its
+    // probability column sum over the segment's router blocks (blocks
+    // seg, seg + S, ... added in that order); both in batches of 16 loads
+    // issued before any is added (past the end a batch re-reads the last
+    // entry and adds zero instead, which is exact: the probabilities are
+    // never -0)
     const int L = (p.n_chunks + S - 1) / S;
     const int c0 = min(p.n_chunks, seg * L), c1 = min(p.n_chunks, c0 + L);
-    int part = 0;
-    auto counts = [&](auto nb, int &b) __attribute__((always_inline)) {
-        constexpr int B = decltype(nb)::value;
-        for (; b + B <= c1; b += B) {
-            int v[B];
-#pragma unroll
-            for (int u = 0; u < B; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
-#pragma unroll
-            for (int u = 0; u < B; ++u) part += v[u];
-        }
-    };
+    const int nr = seg < p.n_rtiles ? (p.n_rtiles - 1 - seg) / S + 1 : 0;
     if (active) {
-        int b = c0;
-        counts(std::integral_constant<int, 32>{}, b);
-        counts(std::integral_constant<int, 8>{}, b);
-        counts(std::integral_constant<int, 1>{}, b);
-        seg_i[seg * p.E + e] = part;
-    }
-    // 2. probability column sums over this segment's router blocks, in
-    // block order; the loads of 32 blocks are issued before any is added
-    // (past the end a batch re-reads the last block and adds zero instead,
-    // which is exact: the sums are of probabilities, never -0)
-    if (active) {
+        const bool has_c = c0 < c1, has_r = nr > 0;
+        const int nb = max((c1 - c0 + 15) / 16, (nr + 15) / 16);
+        int part = 0;
         float ps = 0.0f;
-        for (int b = seg; b < p.n_rtiles; b += 32 * S) {
-            float v[32];
+        for (int it = 0; it < nb; ++it) {
+            int vi[16];
+            float vf[16];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                const int bu = b + u * S;
-                const float x = p.p_part[(size_t)min(bu, p.n_rtiles - 1) * p.E + e];
-                v[u] = bu < p.n_rtiles ? x : 0.0f;
+            for (int u = 0; u < 16; ++u) {
+                const int c = max(min(c0 + it * 16 + u, c1 - 1), 0);
+                vi[u] = has_c ? p.blk[(size_t)c * p.E + e] : 0;
             }
 #pragma unroll
-            for (int u = 0; u < 32; ++u) ps += v[u];
+            for (int u = 0; u < 16; ++u) {
+                const int r = max(min(it * 16 + u, nr - 1), 0);
+                vf[u] = has_r ? p.p_part[(size_t)(seg + r * S) * p.E + e] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                part += c0 + it * 16 + u < c1 ? vi[u] : 0;
+                ps += it * 16 + u < nr ? vf[u] : 0.0f;
+            }
         }
+        seg_i[seg * p.E + e] = part;
         seg_f[seg * p.E + e] = ps;
     }
     // 3. router z / entropy partials: all threads, then waves in order
@@ -110,49 +110,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         }
     }
     __syncthreads();
-    // 4a. inclusive scan of the segment counts over the segments, per
-    // expert: log2(S) steps through LDS instead of a loop over up to S - 1
-    // earlier segments per thread (S = 128 at E = 8)
-    for (int d = 1; d < S; d <<= 1) {
-        int v = 0;
-        if (active && seg >= d) v = seg_i[(seg - d) * p.E + e];
-        __syncthreads();
-        if (active) seg_i[seg * p.E + e] += v;
-        __syncthreads();
-    }
-    // 4. rank bases: the segment's base plus a running count over its
-    // chunks, a batch of counts (32, then 8) loaded before any base is
-    // written (one memory round trip per batch rather than per chunk)
-    if (active && p.n_chunks > 0) {
-        int run = seg_i[seg * p.E + e] - part;   // earlier segments' counts
-        auto bases = [&](auto nb, int &b) __attribute__((always_inline)) {
-            constexpr int B = decltype(nb)::value;
-            for (; b + B <= c1; b += B) {
-                int v[B];
-#pragma unroll
-                for (int u = 0; u < B; ++u) v[u] = p.blk[(size_t)(b + u) * p.E + e];
-#pragma unroll
-                for (int u = 0; u < B; ++u) {
-                    p.blk[(size_t)(b + u) * p.E + e] = run;   // rank base in chunk b+u
-                    run += v[u];
-                }
-            }
-        };
-        int b = c0;
-        bases(std::integral_constant<int, 32>{}, b);
-        bases(std::integral_constant<int, 8>{}, b);
-        bases(std::integral_constant<int, 1>{}, b);
-    }
-    // 5. per expert (threads 0..E-1): counts, kept, f, p
+    // 4. per expert (threads 0..E-1): counts, kept, f, p
     int cnt = 0, kept = 0;
     if (tid < p.E) {
-        if (p.scores) {
-            cnt = p.T;                    // expert choice: every token
-        } else {
-            cnt = seg_i[(S - 1) * p.E + tid];   // inclusive over every segment
-        }
+        int cs = 0;
         float ps = 0.0f;
-        for (int q = 0; q < S; ++q) ps += seg_f[q * p.E + tid];
+        for (int q = 0; q < S; ++q) {
+            cs += seg_i[q * p.E + tid];
+            ps += seg_f[q * p.E + tid];
+        }
+        cnt = p.scores ? p.T : cs;        // expert choice: every token
         kept = (p.capacity >= 0 && cnt > p.capacity) ? p.capacity : cnt;
         p.counts[tid] = cnt;
         p.kept[tid] = kept;
@@ -164,7 +131,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
         kept_s[tid] = kept;
         cnt_s[tid] = cnt;
     }
-    // 6. offsets: exclusive scan of kept over experts (waves 0-3)
+    // 5. offsets: exclusive scan of kept over experts (waves 0-3)
     int incl = kept;
     if (tid < 256) {
 #pragma unroll
@@ -196,28 +163,107 @@ __global__ __launch_bounds__(SCAN_THREADS) void permute_scan(PermuteParams p) {
     }
 }
 
-__global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
+// Expert choice: the statistics only (its picks come from ec_select).
+__global__ __launch_bounds__(SCAN_THREADS) void permute_stats(PermuteParams p) {
+    stats_block(p);
+}
+
+// Chunk b: rank bases (its experts' counts over chunks 0..b-1) and the
+// expert offsets from the whole histogram, then one wave places the
+// chunk's assignments.
+__device__ __forceinline__ void chunk_block(const PermuteParams &p, int b) {
+    __shared__ int tot_s[MOE_MAX_E];
     __shared__ int run[MOE_MAX_E];
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
-    for (int e = lane; e < p.E; e += 64) run[e] = p.blk[(size_t)b * p.E + e];
-    __syncthreads();
+    __shared__ int off_s[MOE_MAX_E + 1];
+    __shared__ int idx_s[CH * MOE_MAX_TOPK];
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int E = p.E;
     const int n = p.T * p.k;
     const int a0 = b * CH * p.k;
     const int a1 = min(n, a0 + CH * p.k);
-    const int total = p.offsets[p.E];
+    // the chunk's expert ids, requested first so that they arrive while
+    // the histogram is read
+    for (int a = a0 + tid; a < a1; a += SCAN_THREADS) idx_s[a - a0] = p.topk_idx[a];
+    for (int i = tid; i < E; i += SCAN_THREADS) {
+        tot_s[i] = 0;
+        run[i] = 0;
+    }
+    __syncthreads();
+    // 1. counts of expert e over this segment's chunks, all of them and
+    // those before b, in batches of 16 loads (a partial batch re-reads the
+    // segment's last chunk and adds zero for it)
+    const int S = SCAN_THREADS / E;                // E <= 256: S >= 4
+    const int e = tid % E, seg = tid / E;
+    if (seg < S) {
+        const int L = (p.n_chunks + S - 1) / S;
+        const int c0 = min(p.n_chunks, seg * L), c1 = min(p.n_chunks, c0 + L);
+        int tot = 0, bef = 0;
+        int c = c0;
+        for (; c + 16 <= c1; c += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)(c + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                tot += v[u];
+                bef += c + u < b ? v[u] : 0;
+            }
+        }
+        for (; c < c1; c += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = p.blk[(size_t)min(c + u, c1 - 1) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int x = c + u < c1 ? v[u] : 0;
+                tot += x;
+                bef += c + u < b ? x : 0;
+            }
+        }
+        if (tot) atomicAdd(&tot_s[e], tot);
+        if (bef) atomicAdd(&run[e], bef);
+    }
+    __syncthreads();
+    // 2. offsets: exclusive scan of kept = min(count, C) over experts
+    int kept = 0, incl = 0;
+    if (tid < 256) {
+        if (tid < E) {
+            const int cnt = tot_s[tid];
+            kept = (p.capacity >= 0 && cnt > p.capacity) ? p.capacity : cnt;
+        }
+        incl = kept;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < E) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        off_s[tid] = before + incl - kept;
+        if (tid == E - 1) off_s[E] = before + incl;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // 3. one wave: stable ranks by ballot over equal experts
+    const int total = off_s[E];
     const unsigned long long lt = (1ull << lane) - 1ull;
     // bits of an expert id: the lanes holding the same expert as this one
     // are those whose ballot agrees with this lane's on every bit
-    const int nbits = p.E > 1 ? 32 - __clz(p.E - 1) : 1;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
     for (int base = a0; base < a1; base += 64) {
         const int a = base + lane;
-        int e = a < a1 ? p.topk_idx[a] : -1;
-        if ((unsigned)e >= (unsigned)p.E) e = -1;
-        const bool ok = e >= 0;
+        int ea = a < a1 ? idx_s[a - a0] : -1;
+        if ((unsigned)ea >= (unsigned)E) ea = -1;
+        const bool ok = ea >= 0;
         unsigned long long same = __ballot(ok);
         for (int bit = 0; bit < nbits; ++bit) {
-            const bool on = (e >> bit) & 1;
+            const bool on = (ea >> bit) & 1;
             const unsigned long long m = __ballot(on);
             same &= on ? m : ~m;
         }
@@ -227,13 +273,13 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
         int rank = 0;
         if (ok) {
             const int before = __popcll(same & lt);
-            rank = run[e] + before;
-            if (before == __popcll(same) - 1) run[e] = rank + 1;
+            rank = run[ea] + before;
+            if (before == __popcll(same) - 1) run[ea] = rank + 1;
         }
         if (a < a1) {
             int slot = -1;
             if (ok && (p.capacity < 0 || rank < p.capacity)) {
-                slot = p.offsets[e] + rank;
+                slot = off_s[ea] + rank;
                 p.slot_token[slot] = a / p.k;
             }
             p.slot_of[a] = slot;
@@ -242,6 +288,17 @@ __global__ __launch_bounds__(64) void permute_scatter(PermuteParams p) {
     // slots past the last kept one hold -1
     for (int s = a0 + lane; s < a1; s += 64)
         if (s >= total) p.slot_token[s] = -1;
+}
+
+// Top-k dispatch: blocks 0..n_chunks-1 place their chunks, block n_chunks
+// writes the statistics.  At most 64 registers a lane, so that two blocks
+// fit a CU and the statistics block, the last, does not wait for a chunk
+// block to end.
+__global__ __launch_bounds__(SCAN_THREADS, 8) void permute_dispatch(PermuteParams p) {
+    if ((int)blockIdx.x == p.n_chunks)
+        stats_block(p);
+    else
+        chunk_block(p, blockIdx.x);
 }
 
 // Counting, scan and dispatch in one block when T*k <= 256 (e.g. a decode
@@ -426,17 +483,13 @@ hipError_t launch_permute(const PermuteParams &p, hipStream_t s) {
         hipLaunchKernelGGL(permute_small, dim3(1), dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(permute_scatter, dim3(p.n_chunks), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(permute_dispatch, dim3(p.n_chunks + 1), dim3(SCAN_THREADS),
+                       0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(SCAN_THREADS), 0, s, p);
+    hipLaunchKernelGGL(permute_stats, dim3(1), dim3(SCAN_THREADS), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(ec_select, dim3(p.E), dim3(EC_THREADS), 0, s, p);

@@ -1,6 +1,6 @@
 // Counting, capacity, stable dispatch and statistics of a whole layer in
 // one block, for T*k <= 256 assignments (one permute chunk) and one router
-// token tile: the single-block form of permute.hip's three kernels (same
+// token tile: the single-block form of permute.hip's dispatch (same
 // arithmetic, same results), shared by the single-launch permute and by the
 // router kernel that also routes and dispatches a decode step.
 #pragma once
