@@ -301,6 +301,32 @@ def test_all_tokens_on_one_expert():
     assert gpu["counts"][5] == 300 and gpu["counts"][2] == 300
 
 
+# The multi-chunk dispatch (T*k above the one-block limit): every chunk's
+# block derives its rank bases and the expert offsets from the router's
+# per-tile histogram, split over 1024 / E segments of its threads.
+DISPATCH = {
+    # 258 assignments: 5 chunks, the last holding one token; E = 48 gives
+    # 21 segments, most of them empty; capacity overflow
+    "just_above_one_block": scaled(W["switch_top1_cap"], T=129, d=256, E=48,
+                                   k=2, d_ff=256, capacity_factor=1.0),
+    # E = 256, k = 8: 4 segments of 4 chunks each, capacity overflow
+    "e256_k8_capacity": scaled(W["deepseek_v3"], T=100, d=256, E=256, k=8,
+                               d_ff=256, capacity_factor=1.0),
+    # E = 3: 341 segments for 32 chunks (one chunk or none each)
+    "e3_many_segments": scaled(W["mixtral_prefill"], T=1000, d=256, E=3,
+                               k=2, d_ff=256),
+}
+
+
+@pytest.mark.parametrize("name", list(DISPATCH))
+def test_multi_chunk_dispatch(name):
+    w = DISPATCH[name]
+    say(f"[dispatch] {name}: {w}")
+    inp, gpu, rep = edge(w, lambda i: None)
+    assert w.T * w.k > 256
+    say(f"[dispatch] {name}: {rep}")
+
+
 def test_empty_experts():
     w = scaled(W["mixtral_prefill"], T=256, d=256, E=16, k=2, d_ff=512)
 
