@@ -22,8 +22,8 @@
 //
 // Expert choice ("AI-Research-SKILLs MoE training guide", sec. 4.2): every
 // token is a candidate of every expert (counts = T, k = E) and expert e
-// keeps its C largest logits instead of its first C tokens.  Two launches:
-//   stats   as above, with counts = T
+// keeps its C largest logits instead of its first C tokens.  One launch:
+//   stats   one block, as above, with counts = T
 //   select  one block per expert: exact radix select of the C-th largest
 //           logit (passes of 11, 11 and 10 bits over order-preserving
 //           keys), then the picks in token order; equal keys go to the
@@ -161,11 +161,6 @@ __device__ __forceinline__ void stats_block(const PermuteParams &p) {
             write_monitor(p, z, h, cnt_s, kept_s);
         }
     }
-}
-
-// Expert choice: the statistics only (its picks come from ec_select).
-__global__ __launch_bounds__(SCAN_THREADS) void permute_stats(PermuteParams p) {
-    stats_block(p);
 }
 
 // Chunk b: rank bases (its experts' counts over chunks 0..b-1) and the
@@ -343,18 +338,17 @@ __device__ __forceinline__ void ec_pick_step(const PermuteParams &p, int e,
     eb += __popcll(em);
 }
 
-// Expert choice, block e: wave w owns the contiguous token segment
+// Expert choice, expert e (block 1 + e): wave w owns the token segment
 // [w*L, (w+1)*L) (L a multiple of 64) and lane l its tokens w*L + 64i + l.
 // Keys of the first EC_KR*1024 tokens are staged in LDS; beyond that
 // (T > 8192) they are re-read.  The router has already set
 // slot_of[t][e] = -1 everywhere, so only the C picks are written here.
-__global__ __launch_bounds__(EC_THREADS) void ec_select(PermuteParams p) {
+__device__ __forceinline__ void ec_select_block(const PermuteParams &p, int e) {
     __shared__ unsigned keys[EC_KR * EC_THREADS];
     __shared__ __attribute__((aligned(16))) int hist[EC_BINS];
     __shared__ int w_gt[EC_WAVES], w_eq[EC_WAVES];
     __shared__ unsigned s_digit;
     __shared__ int s_need;
-    const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, C = p.capacity;
     if (C == 0) return;
@@ -466,6 +460,19 @@ __global__ __launch_bounds__(EC_THREADS) void ec_select(PermuteParams p) {
     }
 }
 
+// Expert choice: block 0 writes the statistics (counts = T, kept = C,
+// offsets e*C: it reads no pick, the picks read none of it), block 1 + e
+// picks expert e's tokens.  The statistics block goes first: where the
+// E + 1 blocks outnumber the CUs (one such block fits a CU), the block
+// left waiting is a pick that starts when the short statistics block ends.
+static_assert(EC_THREADS == SCAN_THREADS, "one block shape");
+__global__ __launch_bounds__(EC_THREADS) void ec_dispatch(PermuteParams p) {
+    if (blockIdx.x == 0)
+        stats_block(p);
+    else
+        ec_select_block(p, (int)blockIdx.x - 1);
+}
+
 __global__ void bias_update_kernel(int E, const int32_t *counts, float target,
                                    float gamma, float *bias) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -489,10 +496,7 @@ hipError_t launch_permute(const PermuteParams &p, hipStream_t s) {
 }
 
 hipError_t launch_expert_choice(const PermuteParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(permute_stats, dim3(1), dim3(SCAN_THREADS), 0, s, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(ec_select, dim3(p.E), dim3(EC_THREADS), 0, s, p);
+    hipLaunchKernelGGL(ec_dispatch, dim3(p.E + 1), dim3(EC_THREADS), 0, s, p);
     return hipGetLastError();
 }
 
